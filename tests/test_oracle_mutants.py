@@ -1,0 +1,172 @@
+"""Plants plausible mistakes into the CPU oracle and checks that the pins catch
+each one.  This is evidence that the pins bind every part of the oracle, not
+only that the oracle agrees with itself.  Runs on the CPU; the mistakes live
+only inside the monkeypatched oracle of this test process."""
+import numpy as np
+import pytest
+
+import oracle.int4 as oi
+import oracle.mla as om
+import pins
+
+_orig = {
+    "rope_rotate": om.rope_rotate, "rope_frequencies": om.rope_frequencies,
+    "token_coords": om.token_coords, "visible": om.visible, "slot_frames": om.slot_frames,
+    "query_frames": om.query_frames, "attention_core": om.attention_core,
+    "materialize_head": om.materialize_head, "output_projection": om.output_projection,
+    "absorb_query": om.absorb_query, "round_bf16": om.round_bf16,
+    "softmax_scale": om.softmax_scale, "query_coords": om.query_coords,
+    "quantize_groups": oi.quantize_groups, "pack_nibbles": oi.pack_nibbles,
+    "unpack_nibbles": oi.unpack_nibbles,
+}
+
+
+def _rope_sign(u, coords, cfg):
+    return _orig["rope_rotate"](u, -np.asarray(coords, np.float64), cfg)
+
+
+def _rope_freq(band, theta):
+    i = np.arange(band // 2, dtype=np.float64)
+    return theta ** (-i / band)
+
+
+def _coords_hw_swap(cfg, frame, tok):
+    c = _orig["token_coords"](cfg, frame, tok)
+    if cfg.rope_dims == 3:
+        c = c[..., [0, 2, 1]]
+    return c
+
+
+def _visible_le(cfg, f_q, f_k):
+    f_q, f_k = np.asarray(f_q), np.asarray(f_k)
+    fpb = cfg.frames_per_block
+    return (f_k >= 0) & (f_k // fpb <= f_q // fpb) & (f_q - f_k <= cfg.window)
+
+
+def _visible_not_causal(cfg, f_q, f_k):
+    f_q, f_k = np.asarray(f_q), np.asarray(f_k)
+    return (f_k >= 0) & (np.abs(f_q - f_k) < cfg.window)
+
+
+def _slot_frames_off(cfg, newest):
+    return _orig["slot_frames"](cfg, newest + 1)
+
+
+def _query_frames_token(cfg, q_first):
+    return q_first + np.arange(cfg.n_q) // max(1, cfg.tokens_per_frame // 2)
+
+
+def _no_lse_max(q, K, V, mask, scale):
+    o, P, lse = _orig["attention_core"](q, K, V, mask, scale)
+    s = np.where(mask, (q @ K.T) * scale, -np.inf)
+    m = np.where(np.isfinite(s.max(axis=1)), s.max(axis=1), 0.0)
+    return o, P, np.where(np.isfinite(lse), lse - m, lse)
+
+
+def _no_mask(q, K, V, mask, scale):
+    return _orig["attention_core"](q, K, V, np.ones_like(mask), scale)
+
+
+def _wrong_value_head(cfg, cache_b, w_uk, w_uv, h):
+    K, _ = _orig["materialize_head"](cfg, cache_b, w_uk, w_uv, h)
+    _, V = _orig["materialize_head"](cfg, cache_b, w_uk, w_uv, (h + 1) % cfg.n_heads)
+    return K, V
+
+
+def _wrong_key_head(cfg, cache_b, w_uk, w_uv, h):
+    _, V = _orig["materialize_head"](cfg, cache_b, w_uk, w_uv, h)
+    K, _ = _orig["materialize_head"](cfg, cache_b, w_uk, w_uv, (h + 1) % cfg.n_heads)
+    return K, V
+
+
+def _wo_untransposed(o_heads, w_o):
+    o = np.asarray(o_heads, np.float64)
+    w = np.asarray(w_o, np.float64)
+    if w.shape[0] == w.shape[1]:
+        return o.reshape(o.shape[:-2] + (-1,)) @ w
+    return _orig["output_projection"](o_heads, w_o)
+
+
+def _absorb_wrong_head(cfg, q_nope, q_rope, w_uk, q_first):
+    return _orig["absorb_query"](cfg, q_nope, q_rope, np.roll(np.asarray(w_uk), 1, axis=0), q_first)
+
+
+def _bf16_truncate(a):
+    a = np.asarray(a, np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))
+    return np.trunc(a / step) * step
+
+
+def _scale_nope_only(cfg):
+    return 1.0 / np.sqrt(cfg.d_nope)
+
+
+def _query_coords_shift(cfg, q_first):
+    return _orig["query_coords"](cfg, q_first + 1)
+
+
+def _int4_half_away(x, group):
+    x = np.asarray(x, np.float32)
+    n = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (n // group, group))
+    s16 = (np.max(np.abs(g), axis=-1) / np.float32(7)).astype(np.float16)
+    s = s16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.sign(g / s) * np.floor(np.abs(g / s) + np.float32(0.5))
+    q = np.where(s == 0, 0, q)
+    return np.clip(q, -8, 7).astype(np.int8).reshape(x.shape), s16
+
+
+def _int4_scale_8(x, group):
+    x = np.asarray(x, np.float32)
+    n = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (n // group, group))
+    s16 = (np.max(np.abs(g), axis=-1) / np.float32(8)).astype(np.float16)
+    s = s16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(g / s)
+    q = np.where(s == 0, 0, q)
+    return np.clip(q, -8, 7).astype(np.int8).reshape(x.shape), s16
+
+
+def _pack_swapped(codes):
+    c = np.asarray(codes).astype(np.int16)
+    return ((c[..., 1::2] & 0xF) | ((c[..., 0::2] & 0xF) << 4)).astype(np.uint8)
+
+
+def _unpack_swapped(packed):
+    out = _orig["unpack_nibbles"](packed)
+    return out.reshape(out.shape[:-1] + (-1, 2))[..., ::-1].reshape(out.shape)
+
+
+MUTANTS = {
+    "rope_rotates_backwards": [(om, "rope_rotate", _rope_sign)],
+    "rope_frequency_exponent": [(om, "rope_frequencies", _rope_freq)],
+    "rope_axes_swapped": [(om, "token_coords", _coords_hw_swap)],
+    "window_off_by_one": [(om, "visible", _visible_le)],
+    "mask_not_causal": [(om, "visible", _visible_not_causal)],
+    "ring_frames_off_by_one": [(om, "slot_frames", _slot_frames_off)],
+    "query_frame_index": [(om, "query_frames", _query_frames_token)],
+    "lse_without_max": [(om, "attention_core", _no_lse_max)],
+    "mask_ignored": [(om, "attention_core", _no_mask)],
+    "value_from_other_head": [(om, "materialize_head", _wrong_value_head)],
+    "key_from_other_head": [(om, "materialize_head", _wrong_key_head)],
+    "output_weight_untransposed": [(om, "output_projection", _wo_untransposed)],
+    "absorb_other_head": [(om, "absorb_query", _absorb_wrong_head)],
+    "bf16_truncates": [(om, "round_bf16", _bf16_truncate)],
+    "softmax_scale_nope_only": [(om, "softmax_scale", _scale_nope_only)],
+    "query_rotated_at_next_frame": [(om, "query_coords", _query_coords_shift)],
+    "int4_ties_away_from_zero": [(oi, "quantize_groups", _int4_half_away)],
+    "int4_scale_amax_over_8": [(oi, "quantize_groups", _int4_scale_8)],
+    "int4_nibbles_swapped": [(oi, "pack_nibbles", _pack_swapped), (oi, "unpack_nibbles", _unpack_swapped)],
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    for mod, attr, fn in MUTANTS[name]:
+        monkeypatch.setattr(mod, attr, fn)
+    res = pins.run_checks(stop_at_first_failure=True)
+    failed = [n for n, (err, tol, _) in res.items() if not err <= tol]
+    assert failed, f"planted mistake {name} passed every pin"
