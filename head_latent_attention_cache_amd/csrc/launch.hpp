@@ -1,0 +1,42 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+#include "common.hpp"
+
+namespace mla {
+
+// C[z] = A[z] . B[z]^T, strides in elements
+struct GemmArgs {
+  int M, N, K, batch;
+  const void* A; long long lda, sA;
+  const void* B; long long ldb, sB;
+  void* C; long long ldc, sC;
+  int out_f32;  // 1: C is float, 0: C has the storage type
+};
+
+struct AttnArgs {
+  Dims d;
+  Geo g;
+  int n_q, n_rows;         // rows per sequence = n_q * H, heads fastest
+  const void* q_abs;
+  const int* q_first;
+  const int* newest;
+  const void* cache;
+  const __half* aux;
+  int batch;
+  void* o_lat;
+  float* lse;
+};
+
+hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st);
+hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
+                               const int* frame, void* cache, void* aux, hipStream_t st);
+hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,
+                         const int* q_first, void* q_abs, hipStream_t st);
+hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* cache, const void* aux,
+                          float* out, hipStream_t st);
+hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t st);
+bool attn_mfma_supported(const Dims& d);
+size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows);
+hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
+
+}  // namespace mla

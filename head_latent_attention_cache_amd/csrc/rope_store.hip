@@ -1,0 +1,202 @@
+// Rotary embedding, cache-row storage (dense or INT4) and the absorbed query's
+// rotary half.
+//
+// Rotary embedding: "Multi-Head Latent Attention" concept page, The RoPE
+// problem, and the decoupled fix (a position-dependent rotation whose query/key
+// product depends on the offset only); VideoMLA review, Key Concepts (3D-RoPE
+// over time, height and width).  Pair i of a band of width b at coordinate p
+// rotates by p * theta^(-2i/b); bands are ordered (t, h, w).
+//
+// INT4 storage: "Multi-Head Latent Attention" topic page, QuantMLA abstract
+// (both cache paths in INT4, dequantised inside attention).  scale =
+// fp16(amax / 7), code = round-half-even(x / scale) clamped to [-8, 7] in IEEE
+// fp32, element 2j in the low nibble.
+#include "launch.hpp"
+
+namespace mla {
+
+// angles of all d_r/2 rotary pairs of one token, computed in fp64
+__device__ void rope_table(const Dims& d, const double* coord, float* cosv, float* sinv) {
+  const int npair = d.d_r / 2;
+  for (int i = threadIdx.x; i < npair; i += blockDim.x) {
+    int axis = 0, ii = i, band = d.band0;
+    if (d.rope_dims == 3) {
+      if (ii >= d.band0 / 2) {
+        ii -= d.band0 / 2;
+        axis = 1;
+        band = d.band1;
+        if (ii >= d.band1 / 2) {
+          ii -= d.band1 / 2;
+          axis = 2;
+          band = d.band2;
+        }
+      }
+    }
+    double freq = pow((double)d.theta, -2.0 * (double)ii / (double)band);
+    double s, c;
+    sincos(coord[axis] * freq, &s, &c);
+    cosv[i] = (float)c;
+    sinv[i] = (float)s;
+  }
+}
+
+// quantise n values (n even) of an LDS row to INT4 codes + one fp16 scale
+__device__ __forceinline__ void quant_int4(const float* v, int n, uint8_t* codes, __half* scale) {
+  float amax = 0.f;
+  for (int j = 0; j < n; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  __half s16 = __float2half_rn(amax / 7.0f);
+  float s = __half2float(s16);
+  *scale = s16;
+  for (int j = 0; j < n; j += 2) {
+    int q0 = 0, q1 = 0;
+    if (s != 0.f) {
+      q0 = (int)fminf(fmaxf(rintf(v[j] / s), -8.f), 7.f);
+      q1 = (int)fminf(fmaxf(rintf(v[j + 1] / s), -8.f), 7.f);
+    }
+    codes[j / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finish the append: rotate the k_rope columns of the projected rows, round to
+// the storage type and store the row at its ring slot.
+// grid (n_tokens, B); y: [B, n_tokens, d_qk] fp32 projection x . w_dkr^T
+// ---------------------------------------------------------------------------
+template <typename T, bool INT4>
+__global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, int n_tokens,
+                                    const int* __restrict__ frame, void* __restrict__ cache,
+                                    __half* __restrict__ aux, int batch) {
+  extern __shared__ float smem[];
+  float* row = smem;                       // d_qk
+  float* cosv = row + d.d_qk;              // d_r / 2
+  float* sinv = cosv + d.d_r / 2;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int f = frame[b] + i / g.P, tok = i % g.P;
+  double coord[3];
+  token_coords(d.rope_dims, g.P, g.grid_w, f, tok, coord);
+  rope_table(d, coord, cosv, sinv);
+  const float* src = y + ((size_t)b * n_tokens + i) * d.d_qk;
+  for (int j = threadIdx.x; j < d.d_c; j += blockDim.x) row[j] = round_to<T>(src[j]);
+  __syncthreads();
+  for (int p = threadIdx.x; p < d.d_r / 2; p += blockDim.x) {
+    float x0 = src[d.d_c + 2 * p], x1 = src[d.d_c + 2 * p + 1];
+    float c = cosv[p], s = sinv[p];
+    row[d.d_c + 2 * p] = round_to<T>(x0 * c - x1 * s);
+    row[d.d_c + 2 * p + 1] = round_to<T>(x0 * s + x1 * c);
+  }
+  __syncthreads();
+  const int slot = ring_slot(g, f, tok);
+  const size_t srow = (size_t)b * g.capacity + slot;
+  if (!INT4) {
+    T* out = (T*)cache + srow * d.d_qk;
+    for (int j = threadIdx.x; j < d.d_qk; j += blockDim.x) Elem<T>::store(out, j, row[j]);
+  } else {
+    uint8_t* codes = (uint8_t*)cache + srow * (d.d_qk / 2);
+    const int ng = d.d_c / 32;
+    __half* cscale = aux + srow * ng;
+    __half* rscale = aux + (size_t)batch * g.capacity * ng + srow;
+    for (int grp = threadIdx.x; grp <= ng; grp += blockDim.x) {
+      if (grp < ng) quant_int4(row + grp * 32, 32, codes + grp * 16, cscale + grp);
+      else quant_int4(row + d.d_c, d.d_r, codes + d.d_c / 2, rscale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rotary half of the absorbed query: q_abs[b,t,h,d_c:] = RoPE(q_rope[b,t,h])
+// grid (n_q, B)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n_q,
+                              const int* __restrict__ q_first, T* __restrict__ q_abs) {
+  extern __shared__ float smem[];
+  float* cosv = smem;
+  float* sinv = smem + d.d_r / 2;
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int f = q_first[b] + t / g.P, tok = t % g.P;
+  double coord[3];
+  token_coords(d.rope_dims, g.P, g.grid_w, f, tok, coord);
+  rope_table(d, coord, cosv, sinv);
+  __syncthreads();
+  const int npair = d.d_r / 2;
+  const size_t tok_index = (size_t)b * n_q + t;
+  for (int e = threadIdx.x; e < d.H * npair; e += blockDim.x) {
+    const int h = e / npair, p = e % npair;
+    const T* src = q_rope + (tok_index * d.H + h) * d.d_r;
+    T* dst = q_abs + (tok_index * d.H + h) * d.d_qk + d.d_c;
+    float x0 = Elem<T>::load(src, 2 * p), x1 = Elem<T>::load(src, 2 * p + 1);
+    float c = cosv[p], s = sinv[p];
+    Elem<T>::store(dst, 2 * p, x0 * c - x1 * s);
+    Elem<T>::store(dst, 2 * p + 1, x0 * s + x1 * c);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cache rows as float (inspection utility)
+// ---------------------------------------------------------------------------
+template <typename T, bool INT4>
+__global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict__ cache,
+                               const __half* __restrict__ aux, float* __restrict__ out) {
+  const size_t total = (size_t)batch * g.capacity * d.d_qk;
+  const int ng = d.d_c / 32;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const size_t srow = e / d.d_qk;
+    const int j = (int)(e % d.d_qk);
+    float v;
+    if (!INT4) {
+      v = Elem<T>::load((const T*)cache, e);
+    } else {
+      const uint8_t byte = ((const uint8_t*)cache)[srow * (d.d_qk / 2) + j / 2];
+      int q = (j & 1) ? (byte >> 4) : (byte & 0xF);
+      q = (q ^ 8) - 8;
+      const float s = j < d.d_c ? __half2float(aux[srow * ng + j / 32])
+                                : __half2float(aux[(size_t)batch * g.capacity * ng + srow]);
+      v = (float)q * s;
+    }
+    out[e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
+                               const int* frame, void* cache, void* aux, hipStream_t st) {
+  dim3 grid(n_tokens, batch);
+  size_t shm = (size_t)(d.d_qk + d.d_r) * sizeof(float);
+  if (d.cache_fmt == MLA_CACHE_INT4)
+    append_store_kernel<bf16_t, true><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch);
+  else if (d.dtype == MLA_BF16)
+    append_store_kernel<bf16_t, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch);
+  else
+    append_store_kernel<float, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,
+                         const int* q_first, void* q_abs, hipStream_t st) {
+  dim3 grid(n_q, batch);
+  size_t shm = (size_t)d.d_r * sizeof(float);
+  if (d.dtype == MLA_BF16)
+    q_rope_kernel<bf16_t><<<grid, 256, shm, st>>>(d, g, (const bf16_t*)q_rope, n_q, q_first, (bf16_t*)q_abs);
+  else
+    q_rope_kernel<float><<<grid, 256, shm, st>>>(d, g, (const float*)q_rope, n_q, q_first, (float*)q_abs);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* cache, const void* aux,
+                          float* out, hipStream_t st) {
+  const size_t total = (size_t)batch * g.capacity * d.d_qk;
+  int blocks = (int)((total + 255) / 256);
+  if (blocks > 65536) blocks = 65536;
+  if (d.cache_fmt == MLA_CACHE_INT4)
+    dequant_kernel<bf16_t, true><<<blocks, 256, 0, st>>>(d, g, batch, cache, (const __half*)aux, out);
+  else if (d.dtype == MLA_BF16)
+    dequant_kernel<bf16_t, false><<<blocks, 256, 0, st>>>(d, g, batch, cache, nullptr, out);
+  else
+    dequant_kernel<float, false><<<blocks, 256, 0, st>>>(d, g, batch, cache, nullptr, out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

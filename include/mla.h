@@ -1,0 +1,210 @@
+/*
+ * mla.h - C-ABI of the MI355X (gfx950) multi-head latent attention library.
+ *
+ * Multi-head latent attention (MLA) caches, per token, one low-rank content
+ * latent c_kv (d_c values) and one decoupled rotary key k_rope (d_r values),
+ * shared by every head.  The key up-projection W^UK is absorbed into the query
+ * and the value up-projection W^UV into the output, so per-head keys and values
+ * are never materialised.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [MLA concept]   "Multi-Head Latent Attention" (praveentn.live concept page):
+ *                   Low-rank joint compression; The RoPE problem, and the
+ *                   decoupled fix; When it breaks.
+ *   [MLA explainer] "Understanding Multi-Head Latent Attention and KV
+ *                   Compression": Low-Rank Joint Compression; On-the-Fly
+ *                   Reconstruction and Matrix Absorption; Decoupling RoPE.
+ *   [VideoMLA review] "VideoMLA: Compressing Video Diffusion Memory by 92.7%
+ *                   with Low-Rank Latent Attention": The Gap; Core Mechanism;
+ *                   Key Concepts.
+ *   [MLA topics]    "Multi-Head Latent Attention" (thelatestinai.com topic
+ *                   page): VideoMLA abstract; QuantMLA abstract.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer, owned by the caller, row-major
+ *   and contiguous with the last dimension fastest, 16-byte aligned.  The
+ *   library never allocates, frees or retains device memory.
+ * - Floating-point tensors use dims->dtype (MLA_F32: float, MLA_BF16:
+ *   bfloat16) for storage; all arithmetic accumulates in fp32.  `lse` is float.
+ * - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every
+ *   call validates its arguments on the host, enqueues kernels on `stream` and
+ *   returns without synchronising.
+ * - Per-sequence frame counters (`frame`, `q_first`, `newest`) are DEVICE
+ *   int32 arrays of length geom->batch, so a captured or repeated launch can
+ *   advance them without a host round trip.
+ * - Errors: an invalid argument returns MLA_ERR_INVALID_ARG (or
+ *   MLA_ERR_UNSUPPORTED for a valid shape with no kernel) before anything is
+ *   launched, leaving every output untouched; a failed launch returns
+ *   MLA_ERR_HIP.  mla_last_error() gives a thread-local message for the last
+ *   non-OK return.  Faults inside kernels surface at the caller's next
+ *   synchronisation.  No C++ exception crosses this interface.
+ * - Sizes of zero (batch, n_tokens, n_q) are valid and launch nothing.
+ *
+ * Cache geometry ([VideoMLA review, The Gap]; [MLA topics, VideoMLA abstract]:
+ * a fixed-size sliding window of recent frames)
+ * ---------------------------------------------------------------------------
+ * A frame is grid_h x grid_w tokens, P = grid_h * grid_w, ordered row-major.
+ * Each sequence owns a ring of `window` frames, capacity = window * P slots;
+ * token `tok` of frame f lives in slot (f mod window) * P + tok.  A language
+ * model is the same geometry with grid 1 x 1 (one token per frame, frame index
+ * = token position) and window = the maximum context.
+ * With `newest` the newest frame written, slot s holds frame
+ *     f_k = newest - ((newest - s / P) mod window),   written iff f_k >= 0,
+ * and a query of frame f_q sees that key iff it is written, is not in a later
+ * block (f_k / frames_per_block <= f_q / frames_per_block: block-causal by
+ * frame when frames_per_block = 1) and f_q - f_k < window.
+ *
+ * Rotary embedding ([MLA concept, The RoPE problem, and the decoupled fix];
+ * [VideoMLA review, Key Concepts]: 3D-RoPE over time, height and width)
+ * ---------------------------------------------------------------------------
+ * rope_dims = 3: the d_r values split into bands of widths band[0..2] for
+ * the coordinates (t, h, w) = (frame, row, column); rope_dims = 1: one band of
+ * width d_r over the position frame * P + tok.  In a band of width b at
+ * coordinate p, pair i = (u[2i], u[2i+1]) rotates by the angle p * theta^(-2i/b).
+ */
+#ifndef MLA_AMD_H
+#define MLA_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,
+  MLA_ERR_UNSUPPORTED = -2,
+  MLA_ERR_WORKSPACE = -3,
+  MLA_ERR_HIP = -4
+} mla_status;
+
+enum { MLA_F32 = 0, MLA_BF16 = 1 };
+enum { MLA_CACHE_DENSE = 0, MLA_CACHE_INT4 = 1 };
+
+/* Model dimensions, identical for every call on one cache. */
+typedef struct {
+  int32_t n_heads;     /* H */
+  int32_t d_model;     /* hidden width */
+  int32_t d_nope;      /* per-head content query/key width */
+  int32_t d_v;         /* per-head value width */
+  int32_t d_c;         /* shared content latent width (multiple of 32 for INT4) */
+  int32_t d_r;         /* shared rotary key width (even) */
+  int32_t rope_dims;   /* 1 or 3 */
+  int32_t band[3];     /* rotary band widths; 3D: (t, h, w), each even, sum d_r; 1D: band[0] = d_r */
+  float rope_theta;    /* frequency base, e.g. 10000 */
+  float softmax_scale; /* <= 0 selects 1/sqrt(d_nope + d_r) */
+  int32_t dtype;       /* MLA_F32 or MLA_BF16 */
+  int32_t cache_fmt;   /* MLA_CACHE_DENSE, or MLA_CACHE_INT4 (requires MLA_BF16) */
+} mla_dims;
+
+/* Cache geometry shared by every sequence of a batch. */
+typedef struct {
+  int32_t batch;            /* B sequences */
+  int32_t grid_h, grid_w;   /* tokens per frame P = grid_h * grid_w */
+  int32_t window;           /* frames per ring; capacity = window * P slots */
+  int32_t frames_per_block; /* block-causal granularity (>= 1) */
+} mla_geom;
+
+/*
+ * Cache storage.
+ *   DENSE: cache = [B, capacity, d_c + d_r] in dims->dtype; cache_aux unused.
+ *   INT4 ([MLA topics, QuantMLA abstract]: both cache paths in INT4, unpacked
+ *   and dequantised inside attention):
+ *     cache     = [B, capacity, (d_c + d_r) / 2] bytes; content codes then
+ *                 rotary codes, element 2j in the low nibble of byte j, 2j+1 in
+ *                 the high nibble, two's complement in [-8, 7];
+ *     cache_aux = fp16 scales: [B, capacity, d_c / 32] per 32-element content
+ *                 group, followed by [B, capacity] per-token rotary scales.
+ *     value = code * scale; scale = fp16(amax / 7), code = round-half-even of
+ *     x / scale clamped to [-8, 7] (IEEE fp32), a zero scale gives zero codes.
+ * Both functions return 0 when the arguments are invalid.
+ */
+size_t mla_cache_bytes(const mla_dims* dims, const mla_geom* geom);
+size_t mla_cache_aux_bytes(const mla_dims* dims, const mla_geom* geom);
+
+/*
+ * mla_cache_append: [MLA concept, Low-rank joint compression] and
+ * [MLA explainer, Low-Rank Joint Compression; Decoupling RoPE].
+ * For every sequence b and token i < n_tokens of x[b], with frame
+ * f = frame[b] + i / P and tok = i % P:
+ *     c      = w_dkr[0 : d_c] . x[b, i]        (content latent)
+ *     k_rope = RoPE(w_dkr[d_c : d_c + d_r] . x[b, i], coordinates of (f, tok))
+ *     cache row at slot (f mod window) * P + tok  <-  [c | k_rope] in the cache format.
+ *   x       [B, n_tokens, d_model]   dims->dtype
+ *   frame   [B] int32 (device)        first frame written per sequence (>= 0)
+ *   w_dkr   [d_c + d_r, d_model]      dims->dtype (output-feature major)
+ *   cache, cache_aux                  see "Cache storage"
+ *   workspace: >= mla_append_workspace_size() bytes of device scratch.
+ * n_tokens must be a multiple of P and n_tokens / P <= window.  The caller
+ * tracks the newest frame (frame[b] + n_tokens / P - 1).
+ */
+size_t mla_append_workspace_size(const mla_dims* dims, const mla_geom* geom, int32_t n_tokens);
+mla_status mla_cache_append(const mla_dims* dims, const mla_geom* geom, void* stream,
+                            const void* x, int32_t n_tokens, const int32_t* frame,
+                            const void* w_dkr, void* cache, void* cache_aux,
+                            void* workspace, size_t workspace_bytes);
+
+/*
+ * mla_absorb_q: [MLA concept, Low-rank joint compression]: since
+ * q . (W^UK c) = ((W^UK)^T q) . c, the key up-projection folds into the query.
+ * For query token t of sequence b (frame q_first[b] + t / P, tok t % P) and head h:
+ *     q_abs[b, t, h, 0 : d_c]        = w_uk[h] . q_nope[b, t, h]
+ *     q_abs[b, t, h, d_c : d_c + d_r] = RoPE(q_rope[b, t, h], coordinates of the token)
+ *   q_nope  [B, n_q, H, d_nope]; q_rope [B, n_q, H, d_r] (unrotated)
+ *   q_first [B] int32 (device)
+ *   w_uk    [H, d_c, d_nope]   w_uk[h] = (W^UK_h)^T, W^UK_h mapping c to the head's content key
+ *   q_abs   [B, n_q, H, d_c + d_r]
+ */
+mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                        const void* q_nope, const void* q_rope, const int32_t* q_first,
+                        const void* w_uk, void* q_abs);
+
+/*
+ * mla_attention: [MLA concept, Low-rank joint compression] ("attend directly in
+ * latent space") and [The RoPE problem, and the decoupled fix] (score = content
+ * term + rotary term); [MLA explainer, Decoupling RoPE] (concatenation).
+ * For every (b, t, h), over the slots s visible to frame q_first[b] + t / P:
+ *     a_s = scale * q_abs[b, t, h] . cache_row[b, s]          (width d_c + d_r)
+ *     o_lat[b, t, h] = sum_s softmax(a)_s * cache_row[b, s, 0 : d_c]
+ *     lse[b, t, h]   = log sum_s exp(a_s)
+ * A row with no visible key gives o_lat = 0 and lse = -inf.
+ *   q_abs   [B, n_q, H, d_c + d_r]; q_first [B], newest [B] int32 (device)
+ *   o_lat   [B, n_q, H, d_c]; lse [B, n_q, H] float, or NULL
+ *   workspace: >= mla_attention_workspace_size() bytes (split-key partials).
+ */
+size_t mla_attention_workspace_size(const mla_dims* dims, const mla_geom* geom, int32_t n_q);
+mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                         const void* q_abs, const int32_t* q_first, const int32_t* newest,
+                         const void* cache, const void* cache_aux,
+                         void* o_lat, float* lse, void* workspace, size_t workspace_bytes);
+
+/*
+ * mla_unabsorb_out: [MLA concept, Low-rank joint compression] ("the same trick
+ * folds W^UV into the output projection"); [MLA explainer, On-the-Fly
+ * Reconstruction and Matrix Absorption].
+ *     o_heads[b, t, h*d_v : (h+1)*d_v] = w_uv[h] . o_lat[b, t, h]
+ *     y[b, t] = w_o . o_heads[b, t]
+ *   o_lat [B, n_q, H, d_c]; w_uv [H, d_v, d_c]; w_o [d_model, H * d_v]
+ *   o_heads [B, n_q, H * d_v] (written, also usable as scratch); y [B, n_q, d_model]
+ */
+mla_status mla_unabsorb_out(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                            const void* o_lat, const void* w_uv, const void* w_o,
+                            void* o_heads, void* y);
+
+/* Inspection utility (not on the hot path): cache rows as float [B, capacity, d_c + d_r]. */
+mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* stream,
+                             const void* cache, const void* cache_aux, float* out);
+
+const char* mla_status_string(int status);
+const char* mla_last_error(void);
+int mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_AMD_H */

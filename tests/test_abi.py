@@ -1,0 +1,148 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+arguments on the host before touching the GPU.  Runs on the CPU: no call
+here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_latent_attention_cache_amd as mla
+from head_latent_attention_cache_amd import _lib
+from mla_inputs import CONFIGS, SMALL_CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"mla_cache_append", "mla_absorb_q", "mla_attention", "mla_unabsorb_out"} <= names
+    assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_status_string(-1) == b"MLA_ERR_INVALID_ARG"
+    assert lib.mla_status_string(-3) == b"MLA_ERR_WORKSPACE"
+
+
+def _dims(cfg, **kw):
+    d = mla.api.dims_from_config(cfg)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _geom(cfg, **kw):
+    g = mla.api.geom_from_config(cfg)
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+def test_cache_sizes(lib, key):
+    cfg = CONFIGS[key]
+    d, g = _dims(cfg), _geom(cfg)
+    nb = lib.mla_cache_bytes(ctypes.byref(d), ctypes.byref(g))
+    na = lib.mla_cache_aux_bytes(ctypes.byref(d), ctypes.byref(g))
+    rows = cfg.batch * cfg.capacity
+    if cfg.cache_fmt == "int4":
+        assert nb == rows * cfg.d_qk // 2
+        assert na == rows * (cfg.d_c // 32 + 1) * 2
+        assert (nb + na) // rows == 322
+    else:
+        assert nb == rows * cfg.d_qk * (2 if cfg.dtype == "bf16" else 4)
+        assert na == 0
+
+
+BAD_DIMS = [
+    ("d_r odd", dict(d_r=15)),
+    ("bands do not sum to d_r", dict(band=(ctypes.c_int32 * 3)(4, 6, 8))),
+    ("rope_dims 2", dict(rope_dims=2)),
+    ("negative heads", dict(n_heads=-1)),
+    ("theta zero", dict(rope_theta=0.0)),
+    ("dtype", dict(dtype=7)),
+    ("int4 with fp32", dict(cache_fmt=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BAD_DIMS, ids=[b[0] for b in BAD_DIMS])
+def test_invalid_dims_rejected_before_launch(lib, name, kw):
+    cfg = CONFIGS[1]
+    d, g = _dims(cfg, **kw), _geom(cfg)
+    fake = ctypes.c_void_p(0x1000)       # never dereferenced: validation fails first
+    st = lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 16, fake, fake, fake, fake, None,
+                           fake, None, None, 0)
+    assert st == _lib.MLA_ERR_INVALID_ARG, (name, st)
+    assert lib.mla_last_error()
+
+
+def test_invalid_geometry_and_pointers(lib):
+    cfg = CONFIGS[3]
+    d = _dims(cfg)
+    fake = ctypes.c_void_p(0x1000)
+    g = _geom(cfg, window=0)
+    assert lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 1, fake, fake, fake, fake, None,
+                             fake, None, None, 0) == _lib.MLA_ERR_INVALID_ARG
+    g = _geom(cfg)
+    # NULL q_abs
+    assert lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 1, None, fake, fake, fake, None,
+                             fake, None, None, 0) == _lib.MLA_ERR_INVALID_ARG
+    assert b"q_abs" in lib.mla_last_error()
+    # misaligned cache pointer
+    assert lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 1, fake, fake, fake,
+                             ctypes.c_void_p(0x1002), None, fake, None, None, 0) == _lib.MLA_ERR_INVALID_ARG
+    assert b"aligned" in lib.mla_last_error()
+    # append: n_tokens not a whole number of frames
+    assert lib.mla_cache_append(ctypes.byref(d), ctypes.byref(g), None, fake, 100, fake, fake, fake,
+                                None, fake, 1 << 30) == _lib.MLA_ERR_INVALID_ARG
+    assert b"multiple of P" in lib.mla_last_error()
+    # append: more frames than the window
+    assert lib.mla_cache_append(ctypes.byref(d), ctypes.byref(g), None, fake, 13 * 1560, fake, fake,
+                                fake, None, fake, 1 << 40) == _lib.MLA_ERR_INVALID_ARG
+    # append: workspace too small
+    assert lib.mla_cache_append(ctypes.byref(d), ctypes.byref(g), None, fake, 1560, fake, fake, fake,
+                                None, fake, 64) == _lib.MLA_ERR_WORKSPACE
+    # INT4 cache needs the scale buffer
+    d5, g5 = _dims(CONFIGS[5]), _geom(CONFIGS[5])
+    assert lib.mla_attention(ctypes.byref(d5), ctypes.byref(g5), None, 1, fake, fake, fake, fake, None,
+                             fake, None, fake, 1 << 40) == _lib.MLA_ERR_INVALID_ARG
+    assert b"cache_aux" in lib.mla_last_error()
+
+
+def test_zero_sizes_are_no_ops(lib):
+    cfg = CONFIGS[3]
+    d = _dims(cfg)
+    g = _geom(cfg, batch=0)
+    assert lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 5, None, None, None, None, None,
+                             None, None, None, 0) == _lib.MLA_OK
+    g = _geom(cfg)
+    assert lib.mla_absorb_q(ctypes.byref(d), ctypes.byref(g), None, 0, None, None, None, None,
+                            None) == _lib.MLA_OK
+    assert lib.mla_cache_append(ctypes.byref(d), ctypes.byref(g), None, None, 0, None, None, None,
+                                None, None, 0) == _lib.MLA_OK
+
+
+def test_unsupported_widths(lib):
+    cfg = SMALL_CONFIGS[3]
+    d = _dims(cfg, d_c=2048)
+    g = _geom(cfg)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 1, fake, fake, fake, fake, None,
+                             fake, None, None, 0) == _lib.MLA_ERR_UNSUPPORTED
