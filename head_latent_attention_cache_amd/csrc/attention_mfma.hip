@@ -1,8 +1,439 @@
-// Latent attention on bf16 MFMA (placeholder until the tiled kernel lands).
+// Latent attention on bf16 MFMA (gfx950): the dense cache path.
+//
+// "Multi-Head Latent Attention" concept page, Low-rank joint compression: with
+// W^UK absorbed into the query, every head attends directly in latent space,
+// so all H heads of all query tokens score the same shared cache rows; and The
+// RoPE problem, and the decoupled fix: the score is one dot product with the
+// concatenated row [c_kv | k_rope].  The value of a key is its content latent.
+// Because every (token, head) row shares the keys, the whole chunk is one dense
+// contraction: rows x keys x (d_c + d_r) for the scores, rows x d_c x keys for
+// the output.
+//
+// Work-group: 4 waves, 128 rows (32 per wave), 32-key tiles.
+//  * Scores are formed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16
+//    (A = 32 keys x 16 dims from LDS, B = 16 dims x 32 rows from registers).
+//    Each lane then owns one query row: the row max and sum are in-lane
+//    reductions plus one exchange between the two 32-lane halves.
+//  * The queries of a wave stay in registers for the whole key loop.
+//  * O^T (d_c x 32 rows) accumulates in 16 blocks of 32 x 32.  The
+//    probabilities feed the MFMA B operand straight from the score
+//    accumulators: their key order is a fixed permutation, and the value
+//    fragments (A operand) are read in the same permuted order with
+//    ds_read_b64_tr_b16 from the very LDS tile that served as the keys.
+//  * Key tiles stream into LDS with global_load_lds_dwordx4 (no register
+//    staging), double-buffered.  Tile layout: [64-dim group][key][8 x 16 B],
+//    16-byte chunks XOR-swizzled per key so that both the 16-byte key reads
+//    (16 consecutive keys, one chunk) and the transposed value reads (4 keys,
+//    2 chunks) hit distinct banks.
+//  * Softmax in the log2 domain against a fixed reference per row: the
+//    maximum of the row's first visible tile.  Probabilities are
+//    exp2(score - reference), so later scores above the reference only grow
+//    them (bf16/fp32 hold 2^64 with full relative precision) and the O
+//    accumulators are never rescaled - no VALU instruction ever reads them,
+//    so they live in the MFMA accumulation registers for the whole loop.  If
+//    a row's maximum exceeds its reference by more than 64 (log2 units), the
+//    work-group discards its accumulators and runs the key loop once more
+//    with the final maxima as references, which cannot overflow.
+//  * Never-written slots are zeroed in LDS (their bytes are whatever the
+//    allocation held, and 0 * NaN would poison the output).
+//  * Optional split of the key range over work-groups with a deterministic
+//    log-sum-exp merge (decode and load balance); the block order is
+//    XCD-aware so that the work-groups sharing a key range share an L2.
 #include "launch.hpp"
 
 namespace mla {
-bool attn_mfma_supported(const Dims&) { return false; }
-size_t attn_mfma_workspace(const Dims&, const Geo&, int, int) { return 0; }
-hipError_t launch_attn_mfma(const AttnArgs&, void*, size_t, hipStream_t) { return hipErrorNotSupported; }
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+
+constexpr int MF_WAVES = 4;
+constexpr int MF_ROWS = 32 * MF_WAVES;   // rows per work-group
+constexpr int MF_BN = 32;                // keys per tile
+
+__device__ __forceinline__ int key_swizzle(int key) {
+  const int j = (key >> 1) & 7;
+  return ((j << 1) & 7) | (j >> 2);
+}
+
+struct MfmaArgs {
+  AttnArgs a;
+  int n_rb;          // row blocks per sequence
+  int nsplit;        // key splits
+  int tiles;         // key tiles per sequence
+  int tps;           // tiles per split
+  float* ws_o;       // [nsplit][B][n_rows][d_c] partial outputs (normalised), if nsplit > 1
+  float* ws_lse;     // [nsplit][B][n_rows]
+};
+
+// frame range [f_min, f_max] held by the slots of a tile (ring positions rp0..rp1)
+__device__ __forceinline__ void tile_frames(int rp0, int rp1, int newest, int nm, int W, int* fmin,
+                                            int* fmax) {
+  const int f0 = ring_frame(rp0, newest, nm, W), f1 = ring_frame(rp1, newest, nm, W);
+  int lo = f0 < f1 ? f0 : f1, hi = f0 > f1 ? f0 : f1;
+  const int wrap = nm + 1;                // first ring position after the newest frame
+  if (wrap > rp0 && wrap <= rp1) {        // the tile crosses from newest back to oldest
+    const int fa = ring_frame(wrap, newest, nm, W), fb = ring_frame(wrap - 1, newest, nm, W);
+    lo = min(lo, min(fa, fb));
+    hi = max(hi, max(fa, fb));
+  }
+  *fmin = lo;
+  *fmax = hi;
+}
+
+template <int DC, int DR>
+__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(MfmaArgs ma) {
+  constexpr int DQK = DC + DR;
+  constexpr int NKS = DQK / 16;              // 16-dim MFMA steps of the score product
+  constexpr int NCG = DQK / 64;              // 64-dim groups per row (128 B)
+  constexpr int NDB = DC / 32;               // 32-dim output blocks
+  constexpr int TILE_BYTES = NCG * MF_BN * 128;
+  constexpr int LOADS = TILE_BYTES / (256 * 16);
+  static_assert(DQK % 64 == 0 && DC % 32 == 0, "widths");
+  static_assert(TILE_BYTES % (256 * 16) == 0, "tile");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const AttnArgs& a = ma.a;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5;                   // half of the wave
+  const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
+
+  // ---- XCD-aware block order: consecutive linear indices land on one XCD ----
+  const int total = gridDim.x;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, per = total >> 3, rem = total & 7;
+  const int lin = xcd * per + min(xcd, rem) + (id >> 3);
+  const int per_b = ma.nsplit * ma.n_rb;
+  const int b = lin / per_b;
+  const int split = (lin / ma.n_rb) % ma.nsplit;
+  const int rb = lin % ma.n_rb;
+
+  const int newest = a.newest[b];
+  int nm = newest % W;
+  if (nm < 0) nm += W;
+  const int qf0 = a.q_first[b];
+  const int n_rows = a.n_rows, H = a.d.H;
+
+  // rows of this lane / wave / work-group
+  const int row = rb * MF_ROWS + wave * 32 + (lane & 31);
+  const bool row_ok = row < n_rows;
+  const int fq = qf0 + (min(row, n_rows - 1) / H) / P;
+  const int wrow0 = min(rb * MF_ROWS + wave * 32, n_rows - 1);
+  const int wrow1 = min(rb * MF_ROWS + wave * 32 + 31, n_rows - 1);
+  const int wfq_min = qf0 + (wrow0 / H) / P, wfq_max = qf0 + (wrow1 / H) / P;
+  const int gfq_min = qf0 + ((rb * MF_ROWS) / H) / P;
+  const int gfq_max = qf0 + (min(rb * MF_ROWS + MF_ROWS - 1, n_rows - 1) / H) / P;
+
+  // ---- queries of this lane's row: B fragments of the 36 score steps ----
+  const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (row_ok ? row : 0)) * DQK;
+  bf16x8_t qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    bf16x8_t v = *(const bf16x8_t*)(qrow + ks * 16 + g * 8);
+    if (!row_ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+    }
+    qf[ks] = v;
+  }
+
+  f32x16_t o[NDB];
+  float m_run = -INFINITY, l_run = 0.f;    // reference maximum and row sum (lane partial)
+  float m_seen = -INFINITY;                // true running maximum of the row
+  const float scale_l2 = a.d.scale * 1.4426950408889634f;
+
+  const int t_begin = split * ma.tps;
+  const int t_end = min(t_begin + ma.tps, ma.tiles);
+  const bf16_t* cache_b = (const bf16_t*)a.cache + (size_t)b * cap * DQK;
+
+  // tile classification (uniform over the work-group)
+  auto skip_tile = [&](int t) -> bool {
+    const int k0 = t * MF_BN;
+    const int k1 = min(k0 + MF_BN, cap) - 1;
+    int fmin, fmax;
+    tile_frames(k0 / P, k1 / P, newest, nm, W, &fmin, &fmax);
+    if (fmax < 0) return true;
+    const int fminw = fmin < 0 ? 0 : fmin;
+    if (floor_div(fminw, fpb) > floor_div(gfq_max, fpb)) return true;
+    if (gfq_min - fmax >= W) return true;
+    return false;
+  };
+  auto next_tile = [&](int t) -> int {
+    while (t < t_end && skip_tile(t)) ++t;
+    return t;
+  };
+  auto issue_loads = [&](int t, int buf) {
+    const int k0 = t * MF_BN;
+    uint8_t* base = smem + buf * TILE_BYTES;
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+      const int blk = q * MF_WAVES + wave;          // 1 KB block of the tile
+      const int cg = blk >> 2;                      // 4 blocks per 64-dim group
+      const int key = ((blk & 3) << 3) + (lane >> 3);
+      const int pos = lane & 7;
+      const int chunk = pos ^ key_swizzle(key);
+      const int slot = min(k0 + key, cap - 1);
+      const bf16_t* src = cache_b + (size_t)slot * DQK + cg * 64 + chunk * 8;
+      __builtin_amdgcn_global_load_lds((const GLB_AS void*)src, (LDS_AS void*)(base + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  l_run = 0.f;
+  m_run = pass == 0 ? -INFINITY : m_seen;
+  bool overflow = false;
+  int t = next_tile(t_begin);
+  int buf = 0;
+  if (t < t_end) issue_loads(t, 0);
+  while (t < t_end) {
+    const int tn = next_tile(t + 1);
+    if (tn < t_end) {
+      issue_loads(tn, buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    uint8_t* tile = smem + buf * TILE_BYTES;
+    const int k0 = t * MF_BN;
+    const int k1 = min(k0 + MF_BN, cap) - 1;
+    int fmin, fmax;
+    tile_frames(k0 / P, k1 / P, newest, nm, W, &fmin, &fmax);
+    if (fmin < 0 || k0 + MF_BN > cap) {
+      // zero never-written (or past-the-end) keys of this tile
+      for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
+        const int key = e / (NCG * 8), rest = e % (NCG * 8);
+        const int s = k0 + key;
+        const bool ok = s < cap && ring_frame(s / P, newest, nm, W) >= 0;
+        if (!ok) {
+          const int cg = rest >> 3, pos = rest & 7;
+          *(uint4*)(tile + (cg * MF_BN + key) * 128 + pos * 16) = make_uint4(0, 0, 0, 0);
+        }
+      }
+      __syncthreads();
+    }
+    const bool full = fmin >= 0 && k0 + MF_BN <= cap &&
+                      floor_div(fmax, fpb) <= floor_div(wfq_min, fpb) && (wfq_max - fmin) < W;
+
+    // ---- S^T = K . Q^T : one 32-key block ----
+    f32x16_t s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    {
+      const int key = lane & 31;
+      const int sw = key_swizzle(key) ^ g;
+      const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(tile + key * 128);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int cg = ks >> 2;
+        const int c = ((ks & 3) << 1);
+        const bf16x8_t kf = *(const LDS_AS bf16x8_t*)(krow + cg * MF_BN * 128 + ((c ^ sw) << 4));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+      }
+    }
+
+    // ---- mask, online softmax (log2 domain, lazy reference maximum) ----
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = s[e] * scale_l2;
+      if (!full) {
+        const int sl = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
+        bool vis = sl < cap;
+        if (vis) vis = key_visible(fq, ring_frame(sl / P, newest, nm, W), W, fpb);
+        if (!vis) v = -INFINITY;
+      }
+      s[e] = v;
+      mloc = fmaxf(mloc, v);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    m_seen = fmaxf(m_seen, mloc);
+    if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
+    else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8_t pf[2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2f(s[j * 8 + e] - m_use);
+        lsum += p;
+        pf[j][e] = (__bf16)p;
+      }
+    }
+    l_run += lsum;
+
+    // ---- O^T += V^T . P^T ----
+    const int gg = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int dim = d * 32 + 16 * (gg & 1) + 4 * (li & 3);   // this lane's 4-dim source chunk
+      const int cg = dim >> 6, c = (dim & 63) >> 3, half = (dim & 7) << 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kbase = j * 16 + 4 * g + (li >> 2);
+        const int key0 = kbase, key1 = kbase + 8;
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4_t*)(LDS_AS uint8_t*)(tile + (cg * MF_BN + key0) * 128 + ((c ^ key_swizzle(key0)) << 4) + half));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4_t*)(LDS_AS uint8_t*)(tile + (cg * MF_BN + key1) * 128 + ((c ^ key_swizzle(key1)) << 4) + half));
+        bf16x8_t vf;
+        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, v0), h1 = __builtin_bit_cast(bf16x4_t, v1);
+        vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
+        vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], o[d], 0, 0, 0);
+      }
+    }
+    __syncthreads();     // every wave is done with this buffer before it is refilled
+    buf ^= 1;
+    t = tn;
+  }
+  if (!__syncthreads_or(overflow)) break;
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+  if (!row_ok) return;
+  if (ma.nsplit == 1) {
+    bf16_t* out = (bf16_t*)a.o_lat + ((size_t)b * n_rows + row) * DC;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dim = d * 32 + 8 * q + 4 * g;
+        u32x2_t pk;
+        pk[0] = (uint32_t)f32_to_bf16(o[d][4 * q] * inv) | ((uint32_t)f32_to_bf16(o[d][4 * q + 1] * inv) << 16);
+        pk[1] = (uint32_t)f32_to_bf16(o[d][4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(o[d][4 * q + 3] * inv) << 16);
+        *(u32x2_t*)(out + dim) = pk;
+      }
+    if (a.lse && g == 0) a.lse[(size_t)b * n_rows + row] = lse;
+  } else {
+    const size_t prow = ((size_t)split * a.batch + b) * n_rows + row;
+    float* out = ma.ws_o + prow * DC;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dim = d * 32 + 8 * q + 4 * g;
+        *(float4*)(out + dim) = make_float4(o[d][4 * q] * inv, o[d][4 * q + 1] * inv,
+                                            o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv);
+      }
+    if (g == 0) ma.ws_lse[prow] = lse;
+  }
+}
+
+// merge of the key splits: o = sum_i w_i o_i / sum_i w_i, w_i = exp(lse_i - max)
+// one wave per row; fixed split order (deterministic)
+template <int DC>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
+  const AttnArgs& a = ma.a;
+  const int lane = threadIdx.x & 63;
+  const size_t rows = (size_t)a.batch * a.n_rows;
+  const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < ma.nsplit; ++sp) mx = fmaxf(mx, ma.ws_lse[(size_t)sp * rows + r]);
+  float acc[DC / 64];
+#pragma unroll
+  for (int u = 0; u < DC / 64; ++u) acc[u] = 0.f;
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    for (int sp = 0; sp < ma.nsplit; ++sp) {
+      const float l = ma.ws_lse[(size_t)sp * rows + r];
+      const float w = expf(l - mx);
+      wsum += w;
+      if (w > 0.f) {
+        const float* src = ma.ws_o + ((size_t)sp * rows + r) * DC;
+#pragma unroll
+        for (int u = 0; u < DC / 64; ++u) acc[u] = fmaf(w, src[lane + 64 * u], acc[u]);
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  bf16_t* out = (bf16_t*)a.o_lat + r * DC;
+#pragma unroll
+  for (int u = 0; u < DC / 64; ++u) out[lane + 64 * u] = f32_to_bf16(acc[u] * inv);
+  if (a.lse && lane == 0) a.lse[r] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+bool attn_mfma_supported(const Dims& d) {
+  return d.dtype == MLA_BF16 && d.cache_fmt == MLA_CACHE_DENSE && d.d_c == 512 && d.d_r == 64;
+}
+
+// number of key splits: balance whole rounds of work-groups over 256 CUs
+// against the cost of writing and merging fp32 partial outputs
+static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
+  int best = 1;
+  double best_cost = 1e30;
+  for (int ns = 1; ns <= 16 && ns <= tiles; ++ns) {
+    const int tps = (tiles + ns - 1) / ns;
+    const long long wgs = (long long)units * ns;
+    const long long rounds = (wgs + 255) / 256;
+    // ~2.5 us per 64-key tile per work-group, +1 tile for the query load/epilogue
+    double cost = (double)rounds * (tps + 1) * 2.5e-6;
+    if (ns > 1) cost += (double)ns * n_rows_total * d_c * 8.0 / 4.0e12;   // partial write + read
+    if (cost < best_cost * 0.98) {
+      best_cost = cost;
+      best = ns;
+    }
+  }
+  return best;
+}
+
+static void plan(const Dims& d, const Geo& g, int batch, int n_rows, int* n_rb, int* tiles, int* ns,
+                 int* tps) {
+  *n_rb = (n_rows + MF_ROWS - 1) / MF_ROWS;
+  *tiles = (g.capacity + MF_BN - 1) / MF_BN;
+  *ns = choose_splits(batch * *n_rb, *tiles, batch * n_rows, d.d_c);
+  *tps = (*tiles + *ns - 1) / *ns;
+  *ns = (*tiles + *tps - 1) / *tps;
+}
+
+size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows) {
+  int n_rb, tiles, ns, tps;
+  plan(d, g, batch, n_rows, &n_rb, &tiles, &ns, &tps);
+  if (ns <= 1) return 0;
+  return (size_t)ns * batch * n_rows * (d.d_c + 1) * sizeof(float);
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
+  MfmaArgs ma;
+  ma.a = a;
+  plan(a.d, a.g, a.batch, a.n_rows, &ma.n_rb, &ma.tiles, &ma.nsplit, &ma.tps);
+  ma.ws_o = nullptr;
+  ma.ws_lse = nullptr;
+  if (ma.nsplit > 1) {
+    if (ws_bytes < attn_mfma_workspace(a.d, a.g, a.batch, a.n_rows)) return hipErrorInvalidValue;
+    ma.ws_o = (float*)ws;
+    ma.ws_lse = ma.ws_o + (size_t)ma.nsplit * a.batch * a.n_rows * a.d.d_c;
+  }
+  constexpr int DC = 512, DR = 64;
+  const size_t shm = 2 * (size_t)((DC + DR) / 64) * MF_BN * 128;
+  auto kern = attn_mfma_kernel<DC, DR>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  const int blocks = a.batch * ma.nsplit * ma.n_rb;
+  kern<<<blocks, 256, shm, st>>>(ma);
+  e = hipGetLastError();
+  if (e != hipSuccess || ma.nsplit == 1) return e;
+  const size_t rows = (size_t)a.batch * a.n_rows;
+  attn_merge_kernel<DC><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(ma);
+  return hipGetLastError();
+}
+
 }  // namespace mla
