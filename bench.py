@@ -1,0 +1,301 @@
+#!/usr/bin/env python
+"""Throughput of one MLA step on one MI355X, printed as one JSON line.
+
+A step is one pass of the whole path over one batch of seeded synthetic
+input, through the C-ABI: mla_cache_append (the newest frame or token),
+mla_absorb_q, mla_attention, mla_unabsorb_out.  Inputs are resident in HBM
+before timing starts.  Default workload: LLM decode (batch 32, 128 heads,
+4096 cached tokens per sequence, d_c 512, d_r 64, bf16).  ``--config 3``
+times the video-chunk workload (1560 query tokens over a 12-frame window).
+
+The "roofline" object covers the attention kernel: algorithmic bytes (decode)
+or FLOPs (chunk) per launch divided by its mean launch time, measured with
+HIP events on the stream the library launches on.  "cpu_baseline" is the
+float64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA attention query-tokens/s + TFLOP/s (% MFMA peak); decode cache GB/s (% HBM)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20         # Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: LLM decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "head_latent_attention_cache_amd", "csrc")
+    for n in sorted(os.listdir(d)):
+        if n.startswith("attention") or n in ("common.hpp", "launch.hpp"):
+            h.update(open(os.path.join(d, n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the MLA path here runs on a single MI355X and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import head_latent_attention_cache_amd as mla
+    from head_latent_attention_cache_amd import api
+    from mla_inputs import CONFIGS, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mla.load()                      # raises if the HIP library is not built
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    cfg = CONFIGS[args.config]
+    B, H, P = cfg.batch, cfg.n_heads, cfg.tokens_per_frame
+    dims, geom = api.dims_from_config(cfg), api.geom_from_config(cfg)
+    dt = api.torch_dtype(dims)
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t0 = time.time()
+    inp = make_workload(cfg, seed=0)
+    print(f"[bench] inputs for {cfg.name} drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    w_dkr, w_uk, w_uv, w_o = (dev_t(inp[k]) for k in ("w_dkr", "w_uk", "w_uv", "w_o"))
+    q_nope, q_rope = dev_t(inp["q_nope"]), dev_t(inp["q_rope"])
+
+    # frames appended by the step and the cache state before it
+    step_frames = 1 if cfg.cache_given else cfg.n_frames - cfg.q_first
+    first_step_frame = cfg.n_frames - step_frames
+    cache_bytes, aux_bytes = api.cache_nbytes(dims, geom)
+    hbm_bound = cfg.cache_given
+    n_sets = max(1, math.ceil(3.5 * MALL_BYTES / (cache_bytes + aux_bytes))) if hbm_bound else 1
+    n_sets = min(n_sets, 16)
+    ws_app = torch.empty(max(16, B * step_frames * P * cfg.d_qk * 4, B * P * cfg.d_qk * 4),
+                         dtype=torch.uint8, device=dev)
+    caches = []
+    if cfg.cache_given:
+        cc, cr = dev_t(inp["cache_c"]), dev_t(inp["cache_r"])
+        L = cc.shape[1]
+        x_step = dev_t(inp["x_new"]).reshape(B, P, cfg.d_model)
+        for _ in range(n_sets):
+            c, a = api.new_cache(dims, geom)
+            c[:, :L, :cfg.d_c] = cc
+            c[:, :L, cfg.d_c:] = cr
+            caches.append((c, a))
+        del cc, cr
+    else:
+        x = dev_t(inp["x"])
+        x_step = x[:, first_step_frame:].reshape(B, step_frames * P, cfg.d_model).contiguous()
+        for _ in range(n_sets):
+            c, a = api.new_cache(dims, geom)
+            for f in range(first_step_frame):
+                api.cache_append(dims, geom, x[:, f].contiguous(),
+                                 torch.full((B,), f, dtype=torch.int32, device=dev), w_dkr, c, a,
+                                 workspace=ws_app)
+            caches.append((c, a))
+        del x
+    frame_t = torch.full((B,), first_step_frame, dtype=torch.int32, device=dev)
+    q_first = torch.full((B,), cfg.q_first, dtype=torch.int32, device=dev)
+    newest = torch.full((B,), cfg.newest, dtype=torch.int32, device=dev)
+    q_abs = [torch.empty((B, cfg.n_q, H, cfg.d_qk), dtype=dt, device=dev) for _ in range(n_sets)]
+    o_lat = [torch.empty((B, cfg.n_q, H, cfg.d_c), dtype=dt, device=dev) for _ in range(n_sets)]
+    lse = torch.empty((B, cfg.n_q, H), dtype=torch.float32, device=dev)
+    o_heads = torch.empty((B, cfg.n_q, H * cfg.d_v), dtype=dt, device=dev)
+    y = torch.empty((B, cfg.n_q, cfg.d_model), dtype=dt, device=dev)
+    ws_attn_n = api.attention_workspace_bytes(dims, geom, cfg.n_q)
+    ws_attn = torch.empty(max(16, ws_attn_n), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] setup done ({n_sets} cache set(s) of {cache_bytes / 1e6:.1f} MB)", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = {k: [] for k in ("append", "absorb", "attention", "unabsorb")}
+
+    def step(i, record):
+        c, a = caches[i % n_sets]
+        qa, ol = q_abs[i % n_sets], o_lat[i % n_sets]
+        marks = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append(e)
+        mark()
+        api.cache_append(dims, geom, x_step, frame_t, w_dkr, c, a, workspace=ws_app)
+        mark()
+        api.absorb_q(dims, geom, q_nope, q_rope, q_first, w_uk, qa)
+        mark()
+        api.attention(dims, geom, qa, q_first, newest, c, a, ol, lse, workspace=ws_attn)
+        mark()
+        api.unabsorb_out(dims, geom, ol, w_uv, w_o, o_heads, y)
+        mark()
+        if record:
+            for k, (e0, e1) in zip(ev, zip(marks[:-1], marks[1:])):
+                ev[k].append((e0, e1))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    call_ms = {k: float(np.mean([e0.elapsed_time(e1) for e0, e1 in v])) for k, v in ev.items()}
+
+    # ---- algorithmic work of the attention call ----
+    qf = np.arange(cfg.n_q) // P + cfg.q_first
+    mask_keys = 0
+    for f in qf:   # visible keys per query token (rows of all heads see the same keys)
+        lo = max(cfg.newest - cfg.window + 1, 0)
+        vis = 0
+        for fk in range(lo, cfg.newest + 1):
+            if fk // cfg.frames_per_block <= f // cfg.frames_per_block and f - fk < cfg.window:
+                vis += P
+        mask_keys += vis
+    pairs = B * H * mask_keys
+    flops = 2.0 * pairs * (cfg.d_qk + cfg.d_c)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    # every visible cache row is read once per sequence (all heads share it)
+    rows_visible = min(cfg.capacity, (cfg.newest + 1) * P)
+    cache_row_bytes = (cache_bytes + aux_bytes) / (B * cfg.capacity)
+    cache_read = B * rows_visible * cache_row_bytes
+    io_bytes = B * cfg.n_q * H * (cfg.d_qk * esz + cfg.d_c * esz + 4)
+    attn_ms = call_ms["attention"]
+    attn_s = attn_ms / 1e3
+    tflops = flops / attn_s / 1e12
+    cache_gbs = cache_read / attn_s / 1e9
+    total_gbs = (cache_read + io_bytes) / attn_s / 1e9
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(total_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(total_gbs / PEAK_HBM_GBS, 4)}
+        alg_per_launch = {"bytes": cache_read + io_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+        alg_per_launch = {"flops": flops}
+    roof["traffic"] = None
+    roof["kernel"] = "mla_attention"
+    roof["launch_ms"] = round(attn_ms, 5)
+    src = source_hash()
+    tfile = os.path.join(ROOT, "profiles", f"attention_traffic_{cfg.name}.json")
+    if os.path.exists(tfile):
+        tr = json.load(open(tfile))
+        if tr.get("source_hash") == src:
+            roof["traffic"] = tr.get("hbm_bytes_per_launch")
+    queries = B * cfg.n_q
+    value = queries / (ms_per_step / 1e3)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "heads": H, "query_tokens_per_step": queries,
+                   "keys_per_sequence": rows_visible, "d_c": cfg.d_c, "d_r": cfg.d_r,
+                   "d_model": cfg.d_model, "window_frames": cfg.window, "tokens_per_frame": P,
+                   "cache_sets_rotated": n_sets},
+        "attention": {"ms": round(attn_ms, 5), "tflops": round(tflops, 2),
+                      "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                      "cache_gbs": round(cache_gbs, 1), "cache_hbm_frac": round(cache_gbs / PEAK_HBM_GBS, 4),
+                      "query_tokens_per_s": round(queries / attn_s, 1),
+                      "algorithmic_per_launch": alg_per_launch, "source_hash": src},
+        "breakdown_ms": {k: round(v, 5) for k, v in call_ms.items()},
+        "roofline": roof,
+    }
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+        del src_t, dst_t
+
+    # ---- CPU oracle on a bounded sample ----
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    """Time the float64 oracle on whole sequences (decode) or a strided subset
+    of query tokens (chunk workloads) on this host's cores."""
+    import numpy as np
+    import oracle.mla as om
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    if cfg.cache_given:
+        # whole sequences: build the cache (given rows + the appended token),
+        # absorb, attend, project
+        done, t_used = 0, 0.0
+        while done < cfg.batch and (done == 0 or t_used < budget_s * 0.7):
+            b = done
+            sub_cfg = cfg.replace(batch=1)
+            sub = {k: (v[b:b + 1] if k in ("q_nope", "q_rope", "cache_c", "cache_r", "x_new") else v)
+                   for k, v in inp.items()}
+            t0 = time.time()
+            om.run(sub_cfg, sub)
+            t_used += time.time() - t0
+            done += 1
+        return {"value": round(done / t_used, 4), "unit": "query-tokens/s", "cores": cores,
+                "kind": "oracle", "sample": f"{done} of {cfg.batch} sequences (1 query token each, all "
+                                            f"{cfg.n_heads} heads, full {cfg.n_frames}-token cache), "
+                                            f"{t_used:.1f} s"}
+    # chunk workloads: cache build excluded (resident input); attend a strided
+    # subset of query tokens with all heads, then extrapolate per token
+    st = om.build_cache(cfg, inp)
+    n = 1
+    while True:
+        toks = [(0, int(t)) for t in np.linspace(0, cfg.n_q - 1, n).astype(int)]
+        t0 = time.time()
+        om.run(cfg, inp, tokens=toks, st=st)
+        dt_ = time.time() - t0
+        if dt_ > budget_s * 0.3 or n >= cfg.n_q:
+            break
+        n = min(cfg.n_q, max(n + 1, int(n * budget_s * 0.6 / max(dt_, 1e-3))))
+    return {"value": round(len(toks) / dt_, 4), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(toks)} of {cfg.n_q} query tokens of sample 0 (all {cfg.n_heads} heads, "
+                      f"full key window; cache build excluded), {dt_:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -87,7 +87,8 @@ __device__ __forceinline__ void tile_frames(int rp0, int rp1, int newest, int nm
 }
 
 template <int DC, int DR>
-__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(MfmaArgs ma) {
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_mfma_kernel(MfmaArgs ma) {
   constexpr int DQK = DC + DR;
   constexpr int NKS = DQK / 16;              // 16-dim MFMA steps of the score product
   constexpr int NCG = DQK / 64;              // 64-dim groups per row (128 B)
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(MfmaArgs ma) {
     const bool full = fmin >= 0 && k0 + MF_BN <= cap &&
                       floor_div(fmax, fpb) <= floor_div(wfq_min, fpb) && (wfq_max - fmin) < W;
 
-    // ---- S^T = K . Q^T : one 32-key block ----
+    // ---- S^T = K . Q^T : one 32-key block, LDS reads KPF steps ahead ----
     f32x16_t s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -232,14 +233,43 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(MfmaArgs ma) {
       const int key = lane & 31;
       const int sw = key_swizzle(key) ^ g;
       const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(tile + key * 128);
+      auto kaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
+        return (const LDS_AS bf16x8_t*)(krow + (ks >> 2) * MF_BN * 128 + ((((ks & 3) << 1) ^ sw) << 4));
+      };
+      constexpr int KPF = 6;
+      bf16x8_t kb[KPF];
+#pragma unroll
+      for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
+      // scheduling barriers keep every read KPF MFMAs ahead of its use
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const int cg = ks >> 2;
-        const int c = ((ks & 3) << 1);
-        const bf16x8_t kf = *(const LDS_AS bf16x8_t*)(krow + cg * MF_BN * 128 + ((c ^ sw) << 4));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+        const bf16x8_t cur = kb[ks % KPF];
+        if (ks + KPF < NKS) kb[ks % KPF] = *kaddr(ks + KPF);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+
+    // ---- value fragments: address helpers and the first reads, issued before
+    // the softmax so that its VALU work covers their latency ----
+    const int gg = lane >> 4, li = lane & 15;
+    auto vaddr = [&](int d, int j, int second) -> const LDS_AS i16x4_t* {
+      const int dim = d * 32 + 16 * (gg & 1) + 4 * (li & 3);   // this lane's 4-dim source chunk
+      const int cg = dim >> 6, c = (dim & 63) >> 3, half = (dim & 7) << 1;
+      const int key = j * 16 + 4 * g + (li >> 2) + 8 * second;
+      return (const LDS_AS i16x4_t*)(LDS_AS uint8_t*)(tile + (cg * MF_BN + key) * 128 +
+                                                       ((c ^ key_swizzle(key)) << 4) + half);
+    };
+    constexpr int NPV = NDB * 2;           // output MFMAs per tile: (d, j) pairs
+    constexpr int VPF = 4;
+    i16x4_t vb0[VPF], vb1[VPF];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) {
+      vb0[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr(i >> 1, i & 1, 0));
+      vb1[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr(i >> 1, i & 1, 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask, online softmax (log2 domain, lazy reference maximum) ----
     float mloc = -INFINITY;
@@ -273,26 +303,21 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(MfmaArgs ma) {
     }
     l_run += lsum;
 
-    // ---- O^T += V^T . P^T ----
-    const int gg = lane >> 4, li = lane & 15;
+    // ---- O^T += V^T . P^T, transposed LDS reads VPF MFMAs ahead ----
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const int dim = d * 32 + 16 * (gg & 1) + 4 * (li & 3);   // this lane's 4-dim source chunk
-      const int cg = dim >> 6, c = (dim & 63) >> 3, half = (dim & 7) << 1;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int kbase = j * 16 + 4 * g + (li >> 2);
-        const int key0 = kbase, key1 = kbase + 8;
-        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)(LDS_AS uint8_t*)(tile + (cg * MF_BN + key0) * 128 + ((c ^ key_swizzle(key0)) << 4) + half));
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)(LDS_AS uint8_t*)(tile + (cg * MF_BN + key1) * 128 + ((c ^ key_swizzle(key1)) << 4) + half));
-        bf16x8_t vf;
-        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, v0), h1 = __builtin_bit_cast(bf16x4_t, v1);
-        vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
-        vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], o[d], 0, 0, 0);
+    for (int i = 0; i < NPV; ++i) {
+      const int d = i >> 1, j = i & 1;
+      const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, vb0[i % VPF]);
+      const bf16x4_t h1 = __builtin_bit_cast(bf16x4_t, vb1[i % VPF]);
+      if (i + VPF < NPV) {
+        vb0[i % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr((i + VPF) >> 1, (i + VPF) & 1, 0));
+        vb1[i % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr((i + VPF) >> 1, (i + VPF) & 1, 1));
       }
+      bf16x8_t vf;
+      vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
+      vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
+      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], o[d], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();     // every wave is done with this buffer before it is refilled
     buf ^= 1;

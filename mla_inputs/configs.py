@@ -38,7 +38,8 @@ class MLAConfig:
     q_frames: int        # number of consecutive query frames
     dtype: str           # "f32" or "bf16": storage/I-O type, fp32 accumulate
     cache_fmt: str = "dense"   # "dense" or "int4"
-    cache_given: bool = False  # decode: cache rows are drawn directly, no append
+    cache_given: bool = False  # decode: earlier positions' rows are given; only the
+                               # newest frame is appended
 
     # ---- derived -------------------------------------------------------
     @property

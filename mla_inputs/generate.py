@@ -21,15 +21,18 @@ w_uv       [H, d_v, d_c]            per head, the value          1/sqrt(d_c)
                                     up-projection
 w_o        [d_model, H * d_v]       output projection            1/sqrt(H*d_v)
 x          [B, n_frames, P, d_model] hidden states, frame-major  1
-cache_c    [B, n_frames * P, d_c]   given content latents        1
-cache_r    [B, n_frames * P, d_r]   given (already rotated)      1
+cache_c    [B, (n_frames-1) * P, d_c] given content latents      1
+cache_r    [B, (n_frames-1) * P, d_r] given (already rotated)    1
                                     rotary keys
+x_new      [B, 1, P, d_model]       hidden state of the newest   1
+                                    frame, appended by the step
 q_nope     [B, n_q, H, d_nope]      content queries              1
 q_rope     [B, n_q, H, d_r]         rotary queries (unrotated)   1
 =========  =======================  ===========================  =============
 
-``x`` is only drawn for workloads that build their cache by appending frames;
-``cache_c``/``cache_r`` only for workloads whose cache is given (decode).
+``x`` is only drawn for workloads that build their cache by appending frames.
+Decode workloads are given the cache of every earlier position
+(``cache_c``/``cache_r``) and append only the newest token from ``x_new``.
 """
 from __future__ import annotations
 
@@ -39,7 +42,7 @@ from .configs import MLAConfig
 
 _PART_IDS = {
     "w_dkr": 1, "w_uk": 2, "w_uv": 3, "w_o": 4, "x": 5,
-    "cache_c": 6, "cache_r": 7, "q_nope": 8, "q_rope": 9,
+    "cache_c": 6, "cache_r": 7, "q_nope": 8, "q_rope": 9, "x_new": 10,
 }
 
 
@@ -64,12 +67,13 @@ def part_shapes(cfg: MLAConfig) -> dict:
         "q_nope": ((B, cfg.n_q, H, cfg.d_nope), 1.0),
         "q_rope": ((B, cfg.n_q, H, cfg.d_r), 1.0),
     }
+    shapes["w_dkr"] = ((cfg.d_c + cfg.d_r, cfg.d_model), 1.0 / np.sqrt(cfg.d_model))
     if cfg.cache_given:
-        L = cfg.n_frames * P
+        L = (cfg.n_frames - 1) * P
         shapes["cache_c"] = ((B, L, cfg.d_c), 1.0)
         shapes["cache_r"] = ((B, L, cfg.d_r), 1.0)
+        shapes["x_new"] = ((B, 1, P, cfg.d_model), 1.0)
     else:
-        shapes["w_dkr"] = ((cfg.d_c + cfg.d_r, cfg.d_model), 1.0 / np.sqrt(cfg.d_model))
         shapes["x"] = ((B, cfg.n_frames, P, cfg.d_model), 1.0)
     return shapes
 

@@ -174,11 +174,13 @@ def append_frame(st, cfg, x_frame, w_dkr, frame: int):
 
 
 def given_cache(st, cfg, cache_c, cache_r):
-    """Decode workload: positions 0..L-1 hold given (already rotated) rows."""
+    """Decode workload: frames 0..L/P-1 hold given (already rotated) rows."""
     L = cache_c.shape[1]
+    P = cfg.tokens_per_frame
     rows = np.concatenate([as_f64(cache_c), as_f64(cache_r)], axis=-1)
-    store_rows(st, cfg, slot_index(cfg, np.arange(L), 0), rows)
-    st["newest"] = L - 1
+    i = np.arange(L)
+    store_rows(st, cfg, slot_index(cfg, i // P, i % P), rows)
+    st["newest"] = max(st["newest"], L // P - 1)
 
 
 # ---------------------------------------------------------------------------
@@ -293,6 +295,7 @@ def build_cache(cfg, inp) -> dict:
     st = new_cache(cfg)
     if cfg.cache_given:
         given_cache(st, cfg, inp["cache_c"], inp["cache_r"])
+        append_frame(st, cfg, as_f64(inp["x_new"])[:, 0], as_f64(inp["w_dkr"]), cfg.n_frames - 1)
     else:
         x = as_f64(inp["x"])
         w = as_f64(inp["w_dkr"])

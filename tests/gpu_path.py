@@ -50,14 +50,17 @@ def run_gpu(cfg, inp, fill=None, keep_device=False):
     B, H, P = cfg.batch, cfg.n_heads, cfg.tokens_per_frame
     dt = api.torch_dtype(dims)
     cache, aux = api.new_cache(dims, geom, fill=fill)
+    w_dkr = to_device(inp["w_dkr"])
+    ws = torch.empty(max(16, B * P * cfg.d_qk * 4), dtype=torch.uint8, device="cuda")
     if cfg.cache_given:
+        # earlier positions are given rows (dense cache); the newest frame is appended
         L = inp["cache_c"].shape[1]
         cache[:, :L, :cfg.d_c] = to_device(inp["cache_c"])
         cache[:, :L, cfg.d_c:] = to_device(inp["cache_r"])
+        api.cache_append(dims, geom, to_device(inp["x_new"]).reshape(B, P, cfg.d_model),
+                         int_tensor([cfg.n_frames - 1] * B), w_dkr, cache, aux, workspace=ws)
     else:
-        w_dkr = to_device(inp["w_dkr"])
         x = to_device(inp["x"])                        # [B, F, P, D]
-        ws = torch.empty(max(16, B * P * cfg.d_qk * 4), dtype=torch.uint8, device="cuda")
         for f in range(cfg.n_frames):
             api.cache_append(dims, geom, x[:, f].contiguous(), int_tensor([f] * B), w_dkr, cache, aux,
                              workspace=ws)

@@ -117,10 +117,10 @@ def brute_force(cfg, inp):
         for f in range(cfg.n_frames):
             rows = []
             for tok in range(P):
-                if cfg.cache_given:
+                if cfg.cache_given and f < cfg.n_frames - 1:
                     row = g["cache_c"][b][f * P + tok] + g["cache_r"][b][f * P + tok]
                 else:
-                    xv = g["x"][b][f][tok]
+                    xv = g["x_new"][b][0][tok] if cfg.cache_given else g["x"][b][f][tok]
                     yv = [sum(g["w_dkr"][n][k] * xv[k] for k in range(cfg.d_model))
                           for n in range(dc + dr)]
                     row = yv[:dc] + _bf_rotate(yv[dc:], _bf_coords(cfg, f, tok), cfg.bands, cfg.theta)

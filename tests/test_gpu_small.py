@@ -226,14 +226,20 @@ def test_ragged_batch_lengths(gpu_lib):
     lens = [300, 77, 1][:cfg.batch]
     newest = gp.int_tensor([n - 1 for n in lens])
     q_first = gp.int_tensor([n - 1 for n in lens])
-    q_abs_ref = []
+    refs = []
     for b, n in enumerate(lens):
         c = cfg.replace(batch=1, n_frames=n, q_first=n - 1)
-        sub = {k: v[b:b + 1] for k, v in inp.items() if k in ("q_nope", "q_rope", "cache_c", "cache_r")}
-        sub["cache_c"] = sub["cache_c"][:, :n]
-        sub["cache_r"] = sub["cache_r"][:, :n]
+        sub = {k: inp[k][b:b + 1] for k in ("q_nope", "q_rope")}
         sub.update({k: inp[k] for k in ("w_uk", "w_uv", "w_o")})
-        q_abs_ref.append(om.run(c, sub))
+        # the GPU cache holds given rows at positions 0..298 and the appended
+        # newest token at 299; a sequence of length n sees positions 0..n-1
+        st = om.new_cache(c)
+        L = inp["cache_c"].shape[1]
+        m = min(n, L)
+        om.given_cache(st, c, inp["cache_c"][b:b + 1, :m], inp["cache_r"][b:b + 1, :m])
+        if n > L:
+            om.append_frame(st, c, om.as_f64(inp["x_new"][b:b + 1, 0]), om.as_f64(inp["w_dkr"]), L)
+        refs.append(om.run(c, sub, st=st))
     q_abs = torch.empty_like(dev["q_abs"])
     api.absorb_q(dev["dims"], dev["geom"], gp.to_device(inp["q_nope"]), gp.to_device(inp["q_rope"]),
                  q_first, gp.to_device(inp["w_uk"]), q_abs)
@@ -241,7 +247,7 @@ def test_ragged_batch_lengths(gpu_lib):
     lse = torch.empty_like(dev["lse"])
     api.attention(dev["dims"], dev["geom"], q_abs, q_first, newest, dev["cache"], dev["aux"], o_lat, lse)
     torch.cuda.synchronize()
-    for b, r in enumerate(q_abs_ref):
+    for b, r in enumerate(refs):
         gp.compare(f"q_abs[{b}]", gp.to_host(q_abs)[b:b + 1], r["q_abs"], "bf16")
         gp.compare(f"o_lat[{b}]", gp.to_host(o_lat)[b], r["o_lat"].reshape(cfg.n_q, cfg.n_heads, cfg.d_c), "bf16")
         gp.compare(f"lse[{b}]", gp.to_host(lse)[b], r["lse"].reshape(cfg.n_q, cfg.n_heads), "bf16")
