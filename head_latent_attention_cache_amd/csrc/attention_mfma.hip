@@ -14,14 +14,17 @@
 //    (A = 32 keys x 16 dims from LDS, B = 16 dims x 32 rows from registers).
 //    Each lane then owns one query row: the row max and sum are in-lane
 //    reductions plus one exchange between the two 32-lane halves.
-//  * The queries of a wave stay in registers for the whole key loop.
+//  * The queries of a wave stay in registers for the whole key loop (the
+//    content part; the rotary part sits in LDS, 4 KB per wave).
 //  * O^T (d_c x 32 rows) accumulates in 16 blocks of 32 x 32.  The
 //    probabilities feed the MFMA B operand straight from the score
 //    accumulators: their key order is a fixed permutation, and the value
 //    fragments (A operand) are read in the same permuted order with
 //    ds_read_b64_tr_b16 from the very LDS tile that served as the keys.
 //  * Key tiles stream into LDS with global_load_lds_dwordx4 (no register
-//    staging), double-buffered.  Tile layout: [64-dim group][key][8 x 16 B],
+//    staging) into three buffers, two tiles ahead, with one barrier per tile.
+//    Every tile of the work-group's key range is classified once up front
+//    (skipped / fully visible / masked / masked with never-written keys).  Tile layout: [64-dim group][key][8 x 16 B],
 //    16-byte chunks XOR-swizzled per key so that both the 16-byte key reads
 //    (16 consecutive keys, one chunk) and the transposed value reads (4 keys,
 //    2 chunks) hit distinct banks.
@@ -56,6 +59,26 @@ constexpr int MF_WAVES = 4;
 constexpr int MF_ROWS = 32 * MF_WAVES;   // rows per work-group
 constexpr int MF_BN = 32;                // keys per tile
 
+// work-group barrier without the memory fence of __syncthreads(): the fence
+// would wait for every outstanding global->LDS load (vmcnt(0)), including the
+// tiles prefetched ahead.  Callers wait explicitly for what they need
+// (vmcnt for the tile being consumed, lgkmcnt for their own LDS writes).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4).  Issued through asm so that the compiler does not
+// track it: it has no result register, and the kernel orders it explicitly
+// with s_waitcnt vmcnt before the barrier that publishes the tile (the
+// compiler's own tracking would add vmcnt(0) waits in front of later
+// transposed LDS reads, draining the prefetch pipeline).
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_base) : "memory");
+}
+
 __device__ __forceinline__ int key_swizzle(int key) {
   const int j = (key >> 1) & 7;
   return ((j << 1) & 7) | (j >> 2);
@@ -86,6 +109,12 @@ __device__ __forceinline__ void tile_frames(int rp0, int rp1, int newest, int nm
   *fmax = hi;
 }
 
+constexpr int MF_NBUF = 3;               // LDS tile buffers (loads run two tiles ahead)
+constexpr int MF_MAX_TPS = 4096;         // tiles per split (size of the class table)
+
+// tile classes
+enum : uint8_t { TILE_SKIP = 0, TILE_FULL = 1, TILE_MASKED = 2, TILE_MASKED_ZERO = 3 };
+
 template <int DC, int DR>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(MfmaArgs ma) {
@@ -98,7 +127,11 @@ void attn_mfma_kernel(MfmaArgs ma) {
   static_assert(DQK % 64 == 0 && DC % 32 == 0, "widths");
   static_assert(TILE_BYTES % (256 * 16) == 0, "tile");
 
+  constexpr int NKS_REG = DC / 16;           // score steps whose query fragments live in VGPRs
+  constexpr int NKS_LDS = NKS - NKS_REG;     // rotary steps: query fragments kept in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* qlds = smem + MF_NBUF * TILE_BYTES;             // [wave][NKS_LDS][64 lanes][16 B]
+  uint8_t* cls = qlds + MF_WAVES * NKS_LDS * 64 * 16;
   const AttnArgs& a = ma.a;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5;                   // half of the wave
@@ -120,19 +153,40 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int qf0 = a.q_first[b];
   const int n_rows = a.n_rows, H = a.d.H;
 
-  // rows of this lane / wave / work-group
+  // rows of this lane / work-group
   const int row = rb * MF_ROWS + wave * 32 + (lane & 31);
   const bool row_ok = row < n_rows;
   const int fq = qf0 + (min(row, n_rows - 1) / H) / P;
-  const int wrow0 = min(rb * MF_ROWS + wave * 32, n_rows - 1);
-  const int wrow1 = min(rb * MF_ROWS + wave * 32 + 31, n_rows - 1);
-  const int wfq_min = qf0 + (wrow0 / H) / P, wfq_max = qf0 + (wrow1 / H) / P;
   const int gfq_min = qf0 + ((rb * MF_ROWS) / H) / P;
   const int gfq_max = qf0 + (min(rb * MF_ROWS + MF_ROWS - 1, n_rows - 1) / H) / P;
 
-  // ---- queries of this lane's row: B fragments of the 36 score steps ----
+  const int t_begin = split * ma.tps;
+  const int ntl = min(t_begin + ma.tps, ma.tiles) - t_begin;   // tiles of this split
+
+  // ---- classify every tile of the split once ----
+  for (int i = tid; i < ntl; i += 256) {
+    const int k0 = (t_begin + i) * MF_BN;
+    const int k1 = min(k0 + MF_BN, cap) - 1;
+    int fmin, fmax;
+    tile_frames(k0 / P, k1 / P, newest, nm, W, &fmin, &fmax);
+    uint8_t c;
+    const int fminw = fmin < 0 ? 0 : fmin;
+    if (fmax < 0 || floor_div(fminw, fpb) > floor_div(gfq_max, fpb) || gfq_min - fmax >= W) {
+      c = TILE_SKIP;
+    } else if (fmin < 0 || k0 + MF_BN > cap) {
+      c = TILE_MASKED_ZERO;
+    } else if (floor_div(fmax, fpb) <= floor_div(gfq_min, fpb) && gfq_max - fmin < W) {
+      c = TILE_FULL;
+    } else {
+      c = TILE_MASKED;
+    }
+    cls[i] = c;
+  }
+
+  // ---- queries of this lane's row: B fragments of the score steps ----
   const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (row_ok ? row : 0)) * DQK;
-  bf16x8_t qf[NKS];
+  bf16x8_t qf[NKS_REG];
+  LDS_AS uint8_t* qw = (LDS_AS uint8_t*)(qlds + wave * NKS_LDS * 64 * 16);
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     bf16x8_t v = *(const bf16x8_t*)(qrow + ks * 16 + g * 8);
@@ -140,47 +194,35 @@ void attn_mfma_kernel(MfmaArgs ma) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
     }
-    qf[ks] = v;
+    if (ks < NKS_REG) qf[ks] = v;
+    else *(LDS_AS bf16x8_t*)(qw + ((ks - NKS_REG) * 64 + lane) * 16) = v;
   }
+  __syncthreads();
 
   f32x16_t o[NDB];
   float m_run = -INFINITY, l_run = 0.f;    // reference maximum and row sum (lane partial)
   float m_seen = -INFINITY;                // true running maximum of the row
-  const float scale_l2 = a.d.scale * 1.4426950408889634f;
-
-  const int t_begin = split * ma.tps;
-  const int t_end = min(t_begin + ma.tps, ma.tiles);
+  const float c_l2 = a.d.scale * 1.4426950408889634f;
   const bf16_t* cache_b = (const bf16_t*)a.cache + (size_t)b * cap * DQK;
 
-  // tile classification (uniform over the work-group)
-  auto skip_tile = [&](int t) -> bool {
-    const int k0 = t * MF_BN;
-    const int k1 = min(k0 + MF_BN, cap) - 1;
-    int fmin, fmax;
-    tile_frames(k0 / P, k1 / P, newest, nm, W, &fmin, &fmax);
-    if (fmax < 0) return true;
-    const int fminw = fmin < 0 ? 0 : fmin;
-    if (floor_div(fminw, fpb) > floor_div(gfq_max, fpb)) return true;
-    if (gfq_min - fmax >= W) return true;
-    return false;
+  auto next_tile = [&](int i) -> int {
+    while (i < ntl && cls[i] == TILE_SKIP) ++i;
+    return i;
   };
-  auto next_tile = [&](int t) -> int {
-    while (t < t_end && skip_tile(t)) ++t;
-    return t;
-  };
-  auto issue_loads = [&](int t, int buf) {
-    const int k0 = t * MF_BN;
+  auto issue_loads = [&](int i, int buf) {
+    const int k0 = (t_begin + i) * MF_BN;
+    const bool tail = k0 + MF_BN > cap;
+    const bf16_t* tb = cache_b + (size_t)k0 * DQK;
     uint8_t* base = smem + buf * TILE_BYTES;
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
       const int blk = q * MF_WAVES + wave;          // 1 KB block of the tile
       const int cg = blk >> 2;                      // 4 blocks per 64-dim group
-      const int key = ((blk & 3) << 3) + (lane >> 3);
-      const int pos = lane & 7;
-      const int chunk = pos ^ key_swizzle(key);
-      const int slot = min(k0 + key, cap - 1);
-      const bf16_t* src = cache_b + (size_t)slot * DQK + cg * 64 + chunk * 8;
-      __builtin_amdgcn_global_load_lds((const GLB_AS void*)src, (LDS_AS void*)(base + blk * 1024), 16, 0, 0);
+      int key = ((blk & 3) << 3) + (lane >> 3);
+      const int chunk = (lane & 7) ^ key_swizzle(key);
+      if (tail) key = min(key, cap - 1 - k0);
+      const bf16_t* src = tb + key * DQK + cg * 64 + chunk * 8;
+      dma16(src, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(base + blk * 1024));
     }
   };
 
@@ -192,24 +234,25 @@ void attn_mfma_kernel(MfmaArgs ma) {
   l_run = 0.f;
   m_run = pass == 0 ? -INFINITY : m_seen;
   bool overflow = false;
-  int t = next_tile(t_begin);
-  int buf = 0;
-  if (t < t_end) issue_loads(t, 0);
-  while (t < t_end) {
-    const int tn = next_tile(t + 1);
-    if (tn < t_end) {
-      issue_loads(tn, buf ^ 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    uint8_t* tile = smem + buf * TILE_BYTES;
-    const int k0 = t * MF_BN;
-    const int k1 = min(k0 + MF_BN, cap) - 1;
-    int fmin, fmax;
-    tile_frames(k0 / P, k1 / P, newest, nm, W, &fmin, &fmax);
-    if (fmin < 0 || k0 + MF_BN > cap) {
+
+  int cur = next_tile(0);
+  int nxt = cur < ntl ? next_tile(cur + 1) : ntl;
+  int bcur = 0;
+  if (cur < ntl) issue_loads(cur, 0);
+  if (nxt < ntl) issue_loads(nxt, 1);
+  while (cur < ntl) {
+    const int nn = nxt < ntl ? next_tile(nxt + 1) : ntl;
+    if (nxt < ntl) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // one barrier per tile: the current tile is visible to every wave, and
+    // every wave has finished the previous tile, whose buffer is refilled next
+    lds_barrier();
+    // prefetch the tile after next into the buffer freed at this barrier
+    if (nn < ntl) issue_loads(nn, bcur == 0 ? 2 : bcur - 1);
+    uint8_t* tile = smem + bcur * TILE_BYTES;
+    const int k0 = (t_begin + cur) * MF_BN;
+    const int cl = cls[cur];
+    if (cl == TILE_MASKED_ZERO) {
       // zero never-written (or past-the-end) keys of this tile
       for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
         const int key = e / (NCG * 8), rest = e % (NCG * 8);
@@ -220,10 +263,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
           *(uint4*)(tile + (cg * MF_BN + key) * 128 + pos * 16) = make_uint4(0, 0, 0, 0);
         }
       }
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();
     }
-    const bool full = fmin >= 0 && k0 + MF_BN <= cap &&
-                      floor_div(fmax, fpb) <= floor_div(wfq_min, fpb) && (wfq_max - fmin) < W;
 
     // ---- S^T = K . Q^T : one 32-key block, LDS reads KPF steps ahead ----
     f32x16_t s;
@@ -236,22 +278,27 @@ void attn_mfma_kernel(MfmaArgs ma) {
       auto kaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
         return (const LDS_AS bf16x8_t*)(krow + (ks >> 2) * MF_BN * 128 + ((((ks & 3) << 1) ^ sw) << 4));
       };
-      constexpr int KPF = 6;
-      bf16x8_t kb[KPF];
+      auto qaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
+        return (const LDS_AS bf16x8_t*)(qw + ((ks - NKS_REG) * 64 + lane) * 16);
+      };
+      constexpr int KPF = 4;
+      bf16x8_t kb[KPF], qb[NKS_LDS];
 #pragma unroll
       for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
       // scheduling barriers keep every read KPF MFMAs ahead of its use
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8_t cur = kb[ks % KPF];
+        const bf16x8_t cur_k = kb[ks % KPF];
         if (ks + KPF < NKS) kb[ks % KPF] = *kaddr(ks + KPF);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s, 0, 0, 0);
+        if (ks + KPF >= NKS_REG && ks + KPF < NKS) qb[ks + KPF - NKS_REG] = *qaddr(ks + KPF);
+        const bf16x8_t cur_q = ks < NKS_REG ? qf[ks < NKS_REG ? ks : 0] : qb[ks < NKS_REG ? 0 : ks - NKS_REG];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, cur_q, s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // ---- value fragments: address helpers and the first reads, issued before
+    // ---- value fragments: address helper and the first reads, issued before
     // the softmax so that its VALU work covers their latency ----
     const int gg = lane >> 4, li = lane & 15;
     auto vaddr = [&](int d, int j, int second) -> const LDS_AS i16x4_t* {
@@ -271,32 +318,31 @@ void attn_mfma_kernel(MfmaArgs ma) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- mask, online softmax (log2 domain, lazy reference maximum) ----
-    float mloc = -INFINITY;
+    // ---- mask, softmax against the row's reference maximum (log2 domain) ----
+    if (cl != TILE_FULL) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = s[e] * scale_l2;
-      if (!full) {
+      for (int e = 0; e < 16; ++e) {
         const int sl = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
         bool vis = sl < cap;
         if (vis) vis = key_visible(fq, ring_frame(sl / P, newest, nm, W), W, fpb);
-        if (!vis) v = -INFINITY;
+        if (!vis) s[e] = -INFINITY;
       }
-      s[e] = v;
-      mloc = fmaxf(mloc, v);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    float mloc = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, s[e]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * c_l2;
     m_seen = fmaxf(m_seen, mloc);
     if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
     else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
     bf16x8_t pf[2];
     float lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(s[j * 8 + e] - m_use);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j * 8 + e], c_l2, neg_m));
         lsum += p;
         pf[j][e] = (__bf16)p;
       }
@@ -319,10 +365,11 @@ void attn_mfma_kernel(MfmaArgs ma) {
       o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], o[d], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();     // every wave is done with this buffer before it is refilled
-    buf ^= 1;
-    t = tn;
+    cur = nxt;
+    nxt = nn;
+    bcur = bcur == 2 ? 0 : bcur + 1;
   }
+  __syncthreads();
   if (!__syncthreads_or(overflow)) break;
   }
 
@@ -405,7 +452,7 @@ bool attn_mfma_supported(const Dims& d) {
 static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
   int best = 1;
   double best_cost = 1e30;
-  for (int ns = 1; ns <= 16 && ns <= tiles; ++ns) {
+  for (int ns = 1; ns <= 64 && ns <= tiles; ++ns) {
     const int tps = (tiles + ns - 1) / ns;
     const long long wgs = (long long)units * ns;
     const long long rounds = (wgs + 255) / 256;
@@ -425,6 +472,8 @@ static void plan(const Dims& d, const Geo& g, int batch, int n_rows, int* n_rb, 
   *n_rb = (n_rows + MF_ROWS - 1) / MF_ROWS;
   *tiles = (g.capacity + MF_BN - 1) / MF_BN;
   *ns = choose_splits(batch * *n_rb, *tiles, batch * n_rows, d.d_c);
+  const int min_ns = (*tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // the class table holds MF_MAX_TPS tiles
+  if (*ns < min_ns) *ns = min_ns;
   *tps = (*tiles + *ns - 1) / *ns;
   *ns = (*tiles + *tps - 1) / *tps;
 }
@@ -448,7 +497,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStr
     ma.ws_lse = ma.ws_o + (size_t)ma.nsplit * a.batch * a.n_rows * a.d.d_c;
   }
   constexpr int DC = 512, DR = 64;
-  const size_t shm = 2 * (size_t)((DC + DR) / 64) * MF_BN * 128;
+  const size_t shm = MF_NBUF * (size_t)((DC + DR) / 64) * MF_BN * 128 +
+                     (size_t)MF_WAVES * (DR / 16) * 64 * 16 + MF_MAX_TPS;
   auto kern = attn_mfma_kernel<DC, DR>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
