@@ -14,8 +14,8 @@
 //    (A = 32 keys x 16 dims from LDS, B = 16 dims x 32 rows from registers).
 //    Each lane then owns one query row: the row max and sum are in-lane
 //    reductions plus one exchange between the two 32-lane halves.
-//  * The queries of a wave stay in registers for the whole key loop (the
-//    content part; the rotary part sits in LDS, 4 KB per wave).
+//  * The queries of a wave stay in registers for the whole key loop, except
+//    the last 8 of the 16-dim steps, which sit in LDS (8 KB per wave).
 //  * O^T (d_c x 32 rows) accumulates in 16 blocks of 32 x 32.  The
 //    probabilities feed the MFMA B operand straight from the score
 //    accumulators: their key order is a fixed permutation, and the value
@@ -42,6 +42,9 @@
 //  * Optional split of the key range over work-groups with a deterministic
 //    log-sum-exp merge (decode and load balance); the block order is
 //    XCD-aware so that the work-groups sharing a key range share an L2.
+#include <cstdlib>
+#include <cstring>
+
 #include "launch.hpp"
 
 namespace mla {
@@ -78,6 +81,10 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_base) : "memory");
 }
+// same, with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
 
 __device__ __forceinline__ int key_swizzle(int key) {
   const int j = (key >> 1) & 7;
@@ -110,7 +117,8 @@ __device__ __forceinline__ void tile_frames(int rp0, int rp1, int newest, int nm
 }
 
 constexpr int MF_NBUF = 3;               // LDS tile buffers (loads run two tiles ahead)
-constexpr int MF_MAX_TPS = 4096;         // tiles per split (size of the class table)
+constexpr int MF_MAX_TPS = 2048;         // tiles per split (size of the class table)
+constexpr int MF_QLDS_STEPS = 8;         // query 16-dim steps kept in LDS (per wave 8 KB)
 
 // tile classes
 enum : uint8_t { TILE_SKIP = 0, TILE_FULL = 1, TILE_MASKED = 2, TILE_MASKED_ZERO = 3 };
@@ -121,17 +129,20 @@ void attn_mfma_kernel(MfmaArgs ma) {
   constexpr int DQK = DC + DR;
   constexpr int NKS = DQK / 16;              // 16-dim MFMA steps of the score product
   constexpr int NCG = DQK / 64;              // 64-dim groups per row (128 B)
-  constexpr int NDB = DC / 32;               // 32-dim output blocks
   constexpr int TILE_BYTES = NCG * MF_BN * 128;
   constexpr int LOADS = TILE_BYTES / (256 * 16);
-  static_assert(DQK % 64 == 0 && DC % 32 == 0, "widths");
+  constexpr int NKS_LDS = MF_QLDS_STEPS;      // score steps whose query fragments sit in LDS
+  constexpr int NKS_REG = NKS - NKS_LDS;     // the others stay in VGPRs
+  constexpr int WDIMS = DC / MF_WAVES;       // output dims owned by one wave
+  constexpr int NDB = WDIMS / 32;            // its 32-dim output blocks
+  static_assert(DQK % 64 == 0 && WDIMS % 32 == 0, "widths");
   static_assert(TILE_BYTES % (256 * 16) == 0, "tile");
 
-  constexpr int NKS_REG = DC / 16;           // score steps whose query fragments live in VGPRs
-  constexpr int NKS_LDS = NKS - NKS_REG;     // rotary steps: query fragments kept in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* qlds = smem + MF_NBUF * TILE_BYTES;             // [wave][NKS_LDS][64 lanes][16 B]
-  uint8_t* cls = qlds + MF_WAVES * NKS_LDS * 64 * 16;
+  uint8_t* qlds = smem + MF_NBUF * TILE_BYTES;              // [wave][NKS_LDS][64][16 B]
+  uint8_t* plds = qlds + MF_WAVES * NKS_LDS * 1024;         // [2][wave][2 steps][64][16 B]
+  float* lrow = (float*)(plds + 2 * MF_WAVES * 2 * 1024);   // [128] row sums
+  uint8_t* cls = (uint8_t*)(lrow + MF_ROWS);
   const AttnArgs& a = ma.a;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5;                   // half of the wave
@@ -153,7 +164,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int qf0 = a.q_first[b];
   const int n_rows = a.n_rows, H = a.d.H;
 
-  // rows of this lane / work-group
+  // rows scored by this lane / work-group
   const int row = rb * MF_ROWS + wave * 32 + (lane & 31);
   const bool row_ok = row < n_rows;
   const int fq = qf0 + (min(row, n_rows - 1) / H) / P;
@@ -186,7 +197,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // ---- queries of this lane's row: B fragments of the score steps ----
   const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (row_ok ? row : 0)) * DQK;
   bf16x8_t qf[NKS_REG];
-  LDS_AS uint8_t* qw = (LDS_AS uint8_t*)(qlds + wave * NKS_LDS * 64 * 16);
+  LDS_AS uint8_t* qw = (LDS_AS uint8_t*)(qlds + wave * NKS_LDS * 1024);
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     bf16x8_t v = *(const bf16x8_t*)(qrow + ks * 16 + g * 8);
@@ -199,36 +210,74 @@ void attn_mfma_kernel(MfmaArgs ma) {
   }
   __syncthreads();
 
-  f32x16_t o[NDB];
+  // O^T blocks: [output-dim block of this wave][row block of the work-group]
+  f32x16_t o[NDB * MF_WAVES];
   float m_run = -INFINITY, l_run = 0.f;    // reference maximum and row sum (lane partial)
   float m_seen = -INFINITY;                // true running maximum of the row
   const float c_l2 = a.d.scale * 1.4426950408889634f;
   const bf16_t* cache_b = (const bf16_t*)a.cache + (size_t)b * cap * DQK;
+  const int gg = lane >> 4, li = lane & 15;
 
   auto next_tile = [&](int i) -> int {
     while (i < ntl && cls[i] == TILE_SKIP) ++i;
     return i;
   };
+  // lane part of the DMA source offset: load q of wave w fills 1 KB block
+  // (q * 4 + w) = 64-dim group q, keys 8w .. 8w+7, 8 swizzled chunks per key
+  const int dma_key = (wave << 3) + (lane >> 3);
+  const uint32_t dma_off = (uint32_t)(dma_key * DQK * 2 + (((lane & 7) ^ key_swizzle(dma_key)) << 4));
   auto issue_loads = [&](int i, int buf) {
     const int k0 = (t_begin + i) * MF_BN;
-    const bool tail = k0 + MF_BN > cap;
-    const bf16_t* tb = cache_b + (size_t)k0 * DQK;
-    uint8_t* base = smem + buf * TILE_BYTES;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * TILE_BYTES) + wave * 1024;
+    if (k0 + MF_BN <= cap) {
+      const uint8_t* tb = (const uint8_t*)(cache_b + (size_t)k0 * DQK);
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) {
-      const int blk = q * MF_WAVES + wave;          // 1 KB block of the tile
-      const int cg = blk >> 2;                      // 4 blocks per 64-dim group
-      int key = ((blk & 3) << 3) + (lane >> 3);
-      const int chunk = (lane & 7) ^ key_swizzle(key);
-      if (tail) key = min(key, cap - 1 - k0);
-      const bf16_t* src = tb + key * DQK + cg * 64 + chunk * 8;
-      dma16(src, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(base + blk * 1024));
+      for (int q = 0; q < LOADS; ++q)
+        dma16_sv(tb + q * 128, dma_off, lds0 + q * 4096);
+    } else {
+      // past-the-end keys of the last tile read the last slot (zeroed later)
+      const bf16_t* tb = cache_b + (size_t)k0 * DQK;
+      const int key = min(dma_key, cap - 1 - k0);
+      const int chunk = (lane & 7) ^ key_swizzle(dma_key);
+#pragma unroll
+      for (int q = 0; q < LOADS; ++q)
+        dma16(tb + key * DQK + q * 64 + chunk * 8, lds0 + q * 4096);
+    }
+  };
+  // O^T[wave's dims][all rows] += V^T . P^T for the tile in `vbuf` whose
+  // probabilities sit in P buffer `pb`
+  auto output_product = [&](int vbuf, int pb) {
+    uint8_t* vt = smem + vbuf * TILE_BYTES;
+    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pb * MF_WAVES * 2 * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8_t pfr[MF_WAVES];
+#pragma unroll
+      for (int r = 0; r < MF_WAVES; ++r)
+        pfr[r] = *(const LDS_AS bf16x8_t*)(pbase + ((r * 2 + j) * 64 + lane) * 16);
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const int dim = wave * WDIMS + d * 32 + 16 * (gg & 1) + 4 * (li & 3);
+        const int cg = dim >> 6, c = (dim & 63) >> 3, half = (dim & 7) << 1;
+        const int key0 = j * 16 + 4 * g + (li >> 2), key1 = key0 + 8;
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(LDS_AS uint8_t*)(
+            vt + (cg * MF_BN + key0) * 128 + ((c ^ key_swizzle(key0)) << 4) + half));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(LDS_AS uint8_t*)(
+            vt + (cg * MF_BN + key1) * 128 + ((c ^ key_swizzle(key1)) << 4) + half));
+        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, v0), h1 = __builtin_bit_cast(bf16x4_t, v1);
+        bf16x8_t vf;
+        vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
+        vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
+#pragma unroll
+        for (int r = 0; r < MF_WAVES; ++r)
+          o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[r], o[d * MF_WAVES + r], 0, 0, 0);
+      }
     }
   };
 
   for (int pass = 0;; ++pass) {
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
+  for (int d = 0; d < NDB * MF_WAVES; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
   l_run = 0.f;
@@ -236,19 +285,17 @@ void attn_mfma_kernel(MfmaArgs ma) {
   bool overflow = false;
 
   int cur = next_tile(0);
-  int nxt = cur < ntl ? next_tile(cur + 1) : ntl;
-  int bcur = 0;
+  int bcur = 0, bprev = -1, pb = 0;
   if (cur < ntl) issue_loads(cur, 0);
-  if (nxt < ntl) issue_loads(nxt, 1);
   while (cur < ntl) {
-    const int nn = nxt < ntl ? next_tile(nxt + 1) : ntl;
-    if (nxt < ntl) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // one barrier per tile: the current tile is visible to every wave, and
-    // every wave has finished the previous tile, whose buffer is refilled next
+    const int nxt = next_tile(cur + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // one barrier per tile: this tile is in LDS, the previous tile's
+    // probabilities are published, and the buffer two tiles back is free
     lds_barrier();
-    // prefetch the tile after next into the buffer freed at this barrier
-    if (nn < ntl) issue_loads(nn, bcur == 0 ? 2 : bcur - 1);
+    // buffer of the next tile: the one holding neither this tile nor the previous one
+    const int bnext = bprev < 0 ? (bcur + 1) % MF_NBUF : 3 - bcur - bprev;
+    if (nxt < ntl) issue_loads(nxt, bnext);
     uint8_t* tile = smem + bcur * TILE_BYTES;
     const int k0 = (t_begin + cur) * MF_BN;
     const int cl = cls[cur];
@@ -267,6 +314,10 @@ void attn_mfma_kernel(MfmaArgs ma) {
       lds_barrier();
     }
 
+    // ---- output product of the previous tile: its probabilities were
+    // published before this tile's barrier ----
+    if (bprev >= 0) output_product(bprev, pb ^ 1);
+
     // ---- S^T = K . Q^T : one 32-key block, LDS reads KPF steps ahead ----
     f32x16_t s;
 #pragma unroll
@@ -282,7 +333,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
         return (const LDS_AS bf16x8_t*)(qw + ((ks - NKS_REG) * 64 + lane) * 16);
       };
       constexpr int KPF = 4;
-      bf16x8_t kb[KPF], qb[NKS_LDS];
+      bf16x8_t kb[KPF], qb[KPF];
 #pragma unroll
       for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
       // scheduling barriers keep every read KPF MFMAs ahead of its use
@@ -290,33 +341,16 @@ void attn_mfma_kernel(MfmaArgs ma) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8_t cur_k = kb[ks % KPF];
-        if (ks + KPF < NKS) kb[ks % KPF] = *kaddr(ks + KPF);
-        if (ks + KPF >= NKS_REG && ks + KPF < NKS) qb[ks + KPF - NKS_REG] = *qaddr(ks + KPF);
-        const bf16x8_t cur_q = ks < NKS_REG ? qf[ks < NKS_REG ? ks : 0] : qb[ks < NKS_REG ? 0 : ks - NKS_REG];
+        const bf16x8_t cur_q = ks < NKS_REG ? qf[ks < NKS_REG ? ks : 0] : qb[ks % KPF];
+        if (ks + KPF < NKS) {
+          kb[ks % KPF] = *kaddr(ks + KPF);
+          if (ks + KPF >= NKS_REG) qb[ks % KPF] = *qaddr(ks + KPF);
+        }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, cur_q, s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // ---- value fragments: address helper and the first reads, issued before
-    // the softmax so that its VALU work covers their latency ----
-    const int gg = lane >> 4, li = lane & 15;
-    auto vaddr = [&](int d, int j, int second) -> const LDS_AS i16x4_t* {
-      const int dim = d * 32 + 16 * (gg & 1) + 4 * (li & 3);   // this lane's 4-dim source chunk
-      const int cg = dim >> 6, c = (dim & 63) >> 3, half = (dim & 7) << 1;
-      const int key = j * 16 + 4 * g + (li >> 2) + 8 * second;
-      return (const LDS_AS i16x4_t*)(LDS_AS uint8_t*)(tile + (cg * MF_BN + key) * 128 +
-                                                       ((c ^ key_swizzle(key)) << 4) + half);
-    };
-    constexpr int NPV = NDB * 2;           // output MFMAs per tile: (d, j) pairs
-    constexpr int VPF = 4;
-    i16x4_t vb0[VPF], vb1[VPF];
-#pragma unroll
-    for (int i = 0; i < VPF; ++i) {
-      vb0[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr(i >> 1, i & 1, 0));
-      vb1[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr(i >> 1, i & 1, 1));
-    }
-    __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask, softmax against the row's reference maximum (log2 domain) ----
     if (cl != TILE_FULL) {
@@ -336,73 +370,78 @@ void attn_mfma_kernel(MfmaArgs ma) {
     if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
     else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    bf16x8_t pf[2];
     float lsum = 0.f;
+    LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + (pb * MF_WAVES + wave) * 2 * 1024);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      bf16x8_t pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[j * 8 + e], c_l2, neg_m));
         lsum += p;
-        pf[j][e] = (__bf16)p;
+        pf[e] = (__bf16)p;
       }
+      // publish in the B-fragment layout of the output product
+      *(LDS_AS bf16x8_t*)(pw + (j * 64 + lane) * 16) = pf;
     }
     l_run += lsum;
-
-    // ---- O^T += V^T . P^T, transposed LDS reads VPF MFMAs ahead ----
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int d = i >> 1, j = i & 1;
-      const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, vb0[i % VPF]);
-      const bf16x4_t h1 = __builtin_bit_cast(bf16x4_t, vb1[i % VPF]);
-      if (i + VPF < NPV) {
-        vb0[i % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr((i + VPF) >> 1, (i + VPF) & 1, 0));
-        vb1[i % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)vaddr((i + VPF) >> 1, (i + VPF) & 1, 1));
-      }
-      bf16x8_t vf;
-      vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
-      vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
-      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], o[d], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bprev = bcur;
+    bcur = bnext;
+    pb ^= 1;
     cur = nxt;
-    nxt = nn;
-    bcur = bcur == 2 ? 0 : bcur + 1;
+  }
+  if (bprev >= 0) {
+    lds_barrier();
+    output_product(bprev, pb ^ 1);
   }
   __syncthreads();
   if (!__syncthreads_or(overflow)) break;
   }
 
-  // ---- epilogue ----
+  // ---- epilogue: row sums to every wave, then O / l ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-  if (!row_ok) return;
-  if (ma.nsplit == 1) {
-    bf16_t* out = (bf16_t*)a.o_lat + ((size_t)b * n_rows + row) * DC;
+  if (g == 0) lrow[wave * 32 + lane] = l_tot;
+  __syncthreads();
+  if (row_ok && g == 0) {
+    if (ma.nsplit == 1) {
+      if (a.lse) a.lse[(size_t)b * n_rows + row] = lse;
+    } else {
+      ma.ws_lse[((size_t)split * a.batch + b) * n_rows + row] = lse;
+    }
+  }
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
+  for (int r = 0; r < MF_WAVES; ++r) {
+    const int orow = rb * MF_ROWS + r * 32 + (lane & 31);
+    if (orow >= n_rows) continue;
+    const float lt = lrow[r * 32 + (lane & 31)];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (ma.nsplit == 1) {
+      bf16_t* out = (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int dim = d * 32 + 8 * q + 4 * g;
-        u32x2_t pk;
-        pk[0] = (uint32_t)f32_to_bf16(o[d][4 * q] * inv) | ((uint32_t)f32_to_bf16(o[d][4 * q + 1] * inv) << 16);
-        pk[1] = (uint32_t)f32_to_bf16(o[d][4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(o[d][4 * q + 3] * inv) << 16);
-        *(u32x2_t*)(out + dim) = pk;
-      }
-    if (a.lse && g == 0) a.lse[(size_t)b * n_rows + row] = lse;
-  } else {
-    const size_t prow = ((size_t)split * a.batch + b) * n_rows + row;
-    float* out = ma.ws_o + prow * DC;
+      for (int d = 0; d < NDB; ++d)
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
+        for (int q = 0; q < 4; ++q) {
+          const int dim = d * 32 + 8 * q + 4 * g;
+          const f32x16_t& ob = o[d * MF_WAVES + r];
+          u32x2_t pk;
+          pk[0] = (uint32_t)f32_to_bf16(ob[4 * q] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 1] * inv) << 16);
+          pk[1] = (uint32_t)f32_to_bf16(ob[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 3] * inv) << 16);
+          *(u32x2_t*)(out + dim) = pk;
+        }
+    } else {
+      float* out = ma.ws_o + (((size_t)split * a.batch + b) * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int dim = d * 32 + 8 * q + 4 * g;
-        *(float4*)(out + dim) = make_float4(o[d][4 * q] * inv, o[d][4 * q + 1] * inv,
-                                            o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv);
-      }
-    if (g == 0) ma.ws_lse[prow] = lse;
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int dim = d * 32 + 8 * q + 4 * g;
+          const f32x16_t& ob = o[d * MF_WAVES + r];
+          *(float4*)(out + dim) = make_float4(ob[4 * q] * inv, ob[4 * q + 1] * inv, ob[4 * q + 2] * inv,
+                                              ob[4 * q + 3] * inv);
+        }
+    }
   }
 }
 
@@ -443,8 +482,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// MLA_ATTN_KERNEL=generic routes every shape to the generic kernel (testing)
 bool attn_mfma_supported(const Dims& d) {
-  return d.dtype == MLA_BF16 && d.cache_fmt == MLA_CACHE_DENSE && d.d_c == 512 && d.d_r == 64;
+  static const bool generic = [] {
+    const char* e = getenv("MLA_ATTN_KERNEL");
+    return e && strcmp(e, "generic") == 0;
+  }();
+  return !generic && d.dtype == MLA_BF16 && d.cache_fmt == MLA_CACHE_DENSE && d.d_c == 512 && d.d_r == 64;
 }
 
 // number of key splits: balance whole rounds of work-groups over 256 CUs
@@ -467,11 +511,21 @@ static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
   return best;
 }
 
+// MLA_ATTN_SPLITS=<n> fixes the number of key splits (testing: results must
+// not depend on it beyond rounding)
+static int forced_splits() {
+  static int v = [] {
+    const char* e = getenv("MLA_ATTN_SPLITS");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 static void plan(const Dims& d, const Geo& g, int batch, int n_rows, int* n_rb, int* tiles, int* ns,
                  int* tps) {
   *n_rb = (n_rows + MF_ROWS - 1) / MF_ROWS;
   *tiles = (g.capacity + MF_BN - 1) / MF_BN;
-  *ns = choose_splits(batch * *n_rb, *tiles, batch * n_rows, d.d_c);
+  *ns = forced_splits() > 0 ? min(forced_splits(), *tiles) : choose_splits(batch * *n_rb, *tiles, batch * n_rows, d.d_c);
   const int min_ns = (*tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // the class table holds MF_MAX_TPS tiles
   if (*ns < min_ns) *ns = min_ns;
   *tps = (*tiles + *ns - 1) / *ns;
@@ -498,7 +552,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStr
   }
   constexpr int DC = 512, DR = 64;
   const size_t shm = MF_NBUF * (size_t)((DC + DR) / 64) * MF_BN * 128 +
-                     (size_t)MF_WAVES * (DR / 16) * 64 * 16 + MF_MAX_TPS;
+                     (size_t)MF_WAVES * MF_QLDS_STEPS * 1024 + 2 * MF_WAVES * 2 * 1024 +
+                     MF_ROWS * sizeof(float) + MF_MAX_TPS;
   auto kern = attn_mfma_kernel<DC, DR>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;

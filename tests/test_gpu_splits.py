@@ -1,0 +1,52 @@
+"""Key-split invariance and a generic-kernel cross-check of the MFMA attention
+kernel (each case runs in a subprocess with the override in its environment)."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+CHILD = r'''
+import sys, numpy as np
+sys.path.insert(0, {root!r}); sys.path.insert(0, {here!r})
+import gpu_path as gp
+import oracle.mla as om
+from mla_inputs import SMALL_CONFIGS, make_workload
+cfg = SMALL_CONFIGS[{key}]
+inp = make_workload(cfg, seed=11)
+got = gp.run_gpu(cfg, inp, fill=0xFF if cfg.cache_given else None)
+ref = om.run(cfg, inp)
+B, n_q, H = cfg.batch, cfg.n_q, cfg.n_heads
+gp.compare("o_lat", got["o_lat"], ref["o_lat"].reshape(B, n_q, H, cfg.d_c), cfg.dtype)
+gp.compare("lse", got["lse"], ref["lse"].reshape(B, n_q, H), cfg.dtype)
+np.save({out!r}, got["o_lat"])
+print("child ok", flush=True)
+'''
+
+
+def _run(key, env_extra, out, tmp_path):
+    env = dict(os.environ)
+    env.update(env_extra)
+    code = CHILD.format(root=os.path.dirname(HERE), here=HERE, key=key, out=str(tmp_path / out))
+    print(f"[case] workload {key} env {env_extra}", flush=True)
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    return np.load(tmp_path / (out + ".npy"))
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_split_count_invariance(gpu_lib, key, tmp_path):
+    outs = [_run(key, {"MLA_ATTN_SPLITS": str(ns)}, f"s{ns}", tmp_path) for ns in (1, 2, 3)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 2e-2
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_mfma_matches_generic_kernel(gpu_lib, key, tmp_path):
+    a = _run(key, {}, "mfma", tmp_path)
+    g = _run(key, {"MLA_ATTN_KERNEL": "generic"}, "generic", tmp_path)
+    assert np.max(np.abs(a - g)) <= 2e-2 + 1e-2 * np.max(np.abs(g))
