@@ -100,8 +100,8 @@ def main():
     hbm_bound = cfg.cache_given
     n_sets = max(1, math.ceil(3.5 * MALL_BYTES / (cache_bytes + aux_bytes))) if hbm_bound else 1
     n_sets = min(n_sets, 16)
-    ws_app = torch.empty(max(16, B * step_frames * P * cfg.d_qk * 4, B * P * cfg.d_qk * 4),
-                         dtype=torch.uint8, device=dev)
+    ws_app = torch.empty(max(16, api.append_workspace_bytes(dims, geom, step_frames * P),
+                             api.append_workspace_bytes(dims, geom, P)), dtype=torch.uint8, device=dev)
     caches = []
     if cfg.cache_given:
         cc, cr = dev_t(inp["cache_c"]), dev_t(inp["cache_r"])

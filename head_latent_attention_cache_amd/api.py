@@ -140,6 +140,10 @@ def cache_append(dims, geom, x, frame, w_dkr, cache, cache_aux=None, workspace=N
                                workspace.numel() * workspace.element_size()))
 
 
+def append_workspace_bytes(dims, geom, n_tokens):
+    return int(load().mla_append_workspace_size(_rd(dims), _rd(geom), n_tokens))
+
+
 def absorb_q(dims, geom, q_nope, q_rope, q_first, w_uk, q_abs):
     """q_nope [B, n_q, H, d_nope]; q_rope [B, n_q, H, d_r] -> q_abs [B, n_q, H, d_c + d_r]."""
     lib = load()

@@ -171,11 +171,18 @@ size_t mla_cache_aux_bytes(const mla_dims* dims, const mla_geom* geom) {
   return rows * (d.d_c / 32 + 1) * sizeof(__half);
 }
 
+// fp32 projection rows of the appended tokens, one copy per K split
+static size_t append_ws_bytes(const Dims& d, int batch, int n_tokens) {
+  const int M = batch * n_tokens;
+  const int ks = gemm_skinny_ksplit(d.dtype, M, d.d_qk, d.d_model, 1);
+  return (size_t)ks * M * d.d_qk * sizeof(float);
+}
+
 size_t mla_append_workspace_size(const mla_dims* dims, const mla_geom* geom, int32_t n_tokens) {
   Dims d;
   Geo g;
   if (check_dims(dims, &d) != MLA_OK || check_geom(geom, d, &g) != MLA_OK || n_tokens < 0) return 0;
-  return (size_t)geom->batch * n_tokens * d.d_qk * sizeof(float);
+  return append_ws_bytes(d, geom->batch, n_tokens);
 }
 
 mla_status mla_cache_append(const mla_dims* dims, const mla_geom* geom, void* stream, const void* x,
@@ -198,7 +205,7 @@ mla_status mla_cache_append(const mla_dims* dims, const mla_geom* geom, void* st
   NEED_PTR(cache);
   NEED_PTR(workspace);
   if (d.cache_fmt == MLA_CACHE_INT4) NEED_PTR(cache_aux);
-  const size_t need = (size_t)B * n_tokens * d.d_qk * sizeof(float);
+  const size_t need = append_ws_bytes(d, B, n_tokens);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "append workspace needs %zu bytes, got %zu", need, workspace_bytes);
   hipStream_t st = (hipStream_t)stream;
@@ -211,9 +218,11 @@ mla_status mla_cache_append(const mla_dims* dims, const mla_geom* geom, void* st
   ga.B = w_dkr; ga.ldb = d.d_model; ga.sB = 0;
   ga.C = workspace; ga.ldc = d.d_qk; ga.sC = 0;
   ga.out_f32 = 1;
+  ga.ksplit = gemm_skinny_ksplit(d.dtype, ga.M, ga.N, ga.K, 1);
+  ga.sSplit = (long long)ga.M * d.d_qk;
   hipError_t e = launch_gemm_nt(d.dtype, ga, st);
   if (e != hipSuccess) return hip_status(e, st, "append projection");
-  e = launch_append_store(d, g, B, (const float*)workspace, n_tokens, frame, cache, cache_aux, st);
+  e = launch_append_store(d, g, B, (const float*)workspace, n_tokens, frame, cache, cache_aux, ga.ksplit, st);
   return hip_status(e, st, "append store");
 }
 

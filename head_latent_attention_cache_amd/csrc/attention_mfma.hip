@@ -25,9 +25,8 @@
 //    staging) into three buffers, two tiles ahead, with one barrier per tile.
 //    Every tile of the work-group's key range is classified once up front
 //    (skipped / fully visible / masked / masked with never-written keys).  Tile layout: [64-dim group][key][8 x 16 B],
-//    16-byte chunks XOR-swizzled per key so that both the 16-byte key reads
-//    (16 consecutive keys, one chunk) and the transposed value reads (4 keys,
-//    2 chunks) hit distinct banks.
+//    16-byte chunks XOR-swizzled by (key & 7), so that the 16-byte key reads
+//    (consecutive keys, one chunk) hit distinct banks.
 //  * Softmax in the log2 domain against a fixed reference per row: the
 //    maximum of the row's first visible tile.  Probabilities are
 //    exp2(score - reference), so later scores above the reference only grow
@@ -86,10 +85,10 @@ __device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint3
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
-__device__ __forceinline__ int key_swizzle(int key) {
-  const int j = (key >> 1) & 7;
-  return ((j << 1) & 7) | (j >> 2);
-}
+// 16-byte chunk swizzle of a key row.  gfx950 LDS serves 16-byte reads with a
+// 128-byte bank period, so the 8 keys read by each 8-lane group must hit 8
+// different chunk positions: position = chunk ^ (key & 7).
+__device__ __forceinline__ int key_swizzle(int key) { return key & 7; }
 
 struct MfmaArgs {
   AttnArgs a;
@@ -144,7 +143,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
   float* lrow = (float*)(plds + 2 * MF_WAVES * 2 * 1024);   // [128] row sums
   uint8_t* cls = (uint8_t*)(lrow + MF_ROWS);
   const AttnArgs& a = ma.a;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int g = lane >> 5;                   // half of the wave
   const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
 
@@ -244,35 +244,50 @@ void attn_mfma_kernel(MfmaArgs ma) {
         dma16(tb + key * DQK + q * 64 + chunk * 8, lds0 + q * 4096);
     }
   };
+  // per-lane parts of the transposed value-read addresses.  For value dim
+  // block d (0..3) and key step j (0..1) the read of keys key0 (key1 = key0 + 8)
+  // lands at: group (2 * wave + d / 2), key j * 16 + kq, 16-byte chunk
+  // ((d & 1) * 4 + cpart) ^ swizzle(key), byte half; the swizzle of key0 and
+  // key1 does not depend on j.
+  const int kq = 4 * g + (li >> 2);
+  const int cpart = 2 * (gg & 1) + ((li >> 1) & 1);
+  const int vhalf = (li & 1) * 8;
+  const int vsw0 = key_swizzle(kq), vsw1 = key_swizzle(kq + 8);
   // O^T[wave's dims][all rows] += V^T . P^T for the tile in `vbuf` whose
-  // probabilities sit in P buffer `pb`
+  // probabilities sit in P buffer `pb`; every LDS read is issued up front
   auto output_product = [&](int vbuf, int pb) {
-    uint8_t* vt = smem + vbuf * TILE_BYTES;
-    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pb * MF_WAVES * 2 * 1024);
+    const LDS_AS uint8_t* vt = (const LDS_AS uint8_t*)(smem + vbuf * TILE_BYTES) + (2 * wave) * MF_BN * 128;
+    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pb * MF_WAVES * 2 * 1024) + lane * 16;
+    bf16x8_t pfr[2][MF_WAVES];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8_t pfr[MF_WAVES];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < MF_WAVES; ++r)
-        pfr[r] = *(const LDS_AS bf16x8_t*)(pbase + ((r * 2 + j) * 64 + lane) * 16);
+        pfr[j][r] = *(const LDS_AS bf16x8_t*)(pbase + (r * 2 + j) * 1024);
+    i16x4_t v0[2][NDB], v1[2][NDB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        const int dim = wave * WDIMS + d * 32 + 16 * (gg & 1) + 4 * (li & 3);
-        const int cg = dim >> 6, c = (dim & 63) >> 3, half = (dim & 7) << 1;
-        const int key0 = j * 16 + 4 * g + (li >> 2), key1 = key0 + 8;
-        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(LDS_AS uint8_t*)(
-            vt + (cg * MF_BN + key0) * 128 + ((c ^ key_swizzle(key0)) << 4) + half));
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(LDS_AS uint8_t*)(
-            vt + (cg * MF_BN + key1) * 128 + ((c ^ key_swizzle(key1)) << 4) + half));
-        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, v0), h1 = __builtin_bit_cast(bf16x4_t, v1);
+        const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
+        v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4_t*)(gbase + ((((d & 1) * 4 + cpart) ^ vsw0) << 4)));
+        v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, v0[j][d]), h1 = __builtin_bit_cast(bf16x4_t, v1[j][d]);
         bf16x8_t vf;
         vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
         vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
 #pragma unroll
         for (int r = 0; r < MF_WAVES; ++r)
-          o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[r], o[d * MF_WAVES + r], 0, 0, 0);
+          o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[j][r], o[d * MF_WAVES + r], 0, 0, 0);
       }
-    }
   };
 
   for (int pass = 0;; ++pass) {

@@ -186,6 +186,119 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs a) {
       }
 }
 
+// ---------------------------------------------------------------------------
+// skinny bf16 kernel for M <= 32 (decode-time products, weight-bandwidth bound)
+//   work-group: all M rows x 64 output columns; the 4 waves split the
+//   work-group's K range into quarters and each streams its weight slice
+//   straight into MFMA B fragments (16 contiguous bytes per lane from a
+//   K-contiguous weight row), two 64-wide K stages in flight per wave.  The
+//   four partial 32 x 64 tiles are summed in LDS at the end (fixed order).
+//   Optional split of the K range over work-groups (blockIdx.y) writes float
+//   partials at C + split * sSplit for the caller to sum.
+// ---------------------------------------------------------------------------
+constexpr int SK_BN = 64, SK_BK = 64;
+
+__global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
+  __shared__ float red[4][2][64][17];
+  const int z = blockIdx.z;
+  const bf16_t* A = (const bf16_t*)a.A + (size_t)z * a.sA;
+  const bf16_t* B = (const bf16_t*)a.B + (size_t)z * a.sB;
+  const int n0 = blockIdx.x * SK_BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;
+  // K range of this work-group, then of this wave (multiples of SK_BK)
+  const int kchunks = (a.K + SK_BK - 1) / SK_BK;
+  const int wg_chunks = (kchunks + a.ksplit - 1) / a.ksplit;
+  const int c_begin = blockIdx.y * wg_chunks;
+  const int c_end = min(c_begin + wg_chunks, kchunks);
+  const int w_chunks = (max(c_end - c_begin, 0) + 3) / 4;
+  const int wc0 = c_begin + wave * w_chunks;
+  const int wc1 = min(wc0 + w_chunks, c_end);
+
+  const int m = lane & 31;
+  const bool m_ok = m < a.M;
+  const bf16_t* arow = A + (size_t)(m_ok ? m : 0) * a.lda;
+  const bf16_t* brow0 = B + (size_t)min(n0 + m, a.N - 1) * a.ldb;
+  const bf16_t* brow1 = B + (size_t)min(n0 + 32 + m, a.N - 1) * a.ldb;
+  const bool n0_ok = n0 + m < a.N, n1_ok = n0 + 32 + m < a.N;
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  auto ld = [&](const bf16_t* row, int k, bool ok) -> bf16x8_t {
+    u32x4v v = {0u, 0u, 0u, 0u};
+    if (ok && k < a.K) v = *(const u32x4v*)(row + k);
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  // one K stage = 4 MFMA steps of 16: A fragment + two B fragments each
+  struct Stage { bf16x8_t fa[4], fb0[4], fb1[4]; };
+  auto load_stage = [&](Stage& st, int c) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k = c * SK_BK + ks * 16 + g * 8;
+      st.fa[ks] = ld(arow, k, m_ok);
+      st.fb0[ks] = ld(brow0, k, n0_ok);
+      st.fb1[ks] = ld(brow1, k, n1_ok);
+    }
+  };
+  Stage s0, s1;
+  if (wc0 < wc1) load_stage(s0, wc0);
+  if (wc0 + 1 < wc1) load_stage(s1, wc0 + 1);
+  for (int c = wc0; c < wc1; c += 2) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0.fa[ks], s0.fb0[ks], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0.fa[ks], s0.fb1[ks], acc[1], 0, 0, 0);
+    }
+    if (c + 2 < wc1) load_stage(s0, c + 2);
+    if (c + 1 < wc1) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1.fa[ks], s1.fb0[ks], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1.fa[ks], s1.fb1[ks], acc[1], 0, 0, 0);
+      }
+      if (c + 3 < wc1) load_stage(s1, c + 3);
+    }
+  }
+  // sum the four wave partials (fixed order) and store
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[wave][j][lane][e] = acc[j][e];
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int l = t & 63, j = (t >> 6) & 1, eh = (t >> 7) * 8;
+#pragma unroll
+  for (int e = eh; e < eh + 8; ++e) {
+    const float v = red[0][j][l][e] + red[1][j][l][e] + red[2][j][l][e] + red[3][j][l][e];
+    const int mm = 8 * (e / 4) + 4 * (l / 32) + (e % 4);
+    const int nn = n0 + j * 32 + (l & 31);
+    if (mm < a.M && nn < a.N) {
+      if (a.ksplit > 1)
+        ((float*)a.C)[(size_t)blockIdx.y * a.sSplit + (size_t)z * a.sC + (size_t)mm * a.ldc + nn] = v;
+      else if (a.out_f32)
+        ((float*)a.C)[(size_t)z * a.sC + (size_t)mm * a.ldc + nn] = v;
+      else
+        ((bf16_t*)a.C)[(size_t)z * a.sC + (size_t)mm * a.ldc + nn] = f32_to_bf16(v);
+    }
+  }
+}
+
+int gemm_skinny_ksplit(int dtype, int M, int N, int K, int batch) {
+  if (dtype != MLA_BF16 || M > 32 || M <= 0) return 1;
+  const int wgs = ((N + SK_BN - 1) / SK_BN) * batch;
+  const int kchunks = (K + SK_BK - 1) / SK_BK;
+  int ks = 1;
+  // aim at >= 256 work-groups, keeping >= 4 K stages per wave
+  while (wgs * ks < 256 && (kchunks / (ks * 2)) >= 16) ks *= 2;
+  return ks;
+}
+
 hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0 || a.batch == 0) return hipSuccess;
   if (dtype == MLA_F32) {
@@ -194,7 +307,12 @@ hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st) {
     else gemm_nt_f32_kernel<float><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
-  // bf16: small-M products (decode) use 64-row tiles, wide ones 128 x 128
+  if (a.M <= 32) {
+    dim3 grid((a.N + SK_BN - 1) / SK_BN, a.ksplit, a.batch);
+    gemm_skinny_bf16_kernel<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  // bf16: small-M products use 64-row tiles, wide ones 128 x 128
   if (a.M <= 64) {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, a.batch);
     gemm_nt_bf16_kernel<64, 64><<<grid, 256, 0, st>>>(a);

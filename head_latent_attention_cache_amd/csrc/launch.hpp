@@ -11,7 +11,14 @@ struct GemmArgs {
   const void* B; long long ldb, sB;
   void* C; long long ldc, sC;
   int out_f32;  // 1: C is float, 0: C has the storage type
+  // split of the K range over work-groups (skinny products only): partial
+  // products go to C + s * sSplit (float) and the caller sums them
+  int ksplit = 1;
+  long long sSplit = 0;
 };
+
+// K splits the skinny product would use for an M x N x K problem (1 if not skinny)
+int gemm_skinny_ksplit(int dtype, int M, int N, int K, int batch);
 
 struct AttnArgs {
   Dims d;
@@ -29,7 +36,7 @@ struct AttnArgs {
 
 hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st);
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
-                               const int* frame, void* cache, void* aux, hipStream_t st);
+                               const int* frame, void* cache, void* aux, int nsplit, hipStream_t st);
 hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,
                          const int* q_first, void* q_abs, hipStream_t st);
 hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* cache, const void* aux,

@@ -32,11 +32,15 @@ __device__ void rope_table(const Dims& d, const double* coord, float* cosv, floa
         }
       }
     }
-    double freq = pow((double)d.theta, -2.0 * (double)ii / (double)band);
-    double s, c;
-    sincos(coord[axis] * freq, &s, &c);
-    cosv[i] = (float)c;
-    sinv[i] = (float)s;
+    // angle in fp64, reduced to [-pi, pi] in fp64, then an fp32 sine/cosine
+    const double freq = exp2(-2.0 * (double)ii / (double)band * log2((double)d.theta));
+    const double ang = coord[axis] * freq;
+    const double two_pi = 6.283185307179586476925286766559;
+    const float r = (float)(ang - two_pi * rint(ang / two_pi));
+    float s, c;
+    sincosf(r, &s, &c);
+    cosv[i] = c;
+    sinv[i] = s;
   }
 }
 
@@ -65,7 +69,7 @@ __device__ __forceinline__ void quant_int4(const float* v, int n, uint8_t* codes
 template <typename T, bool INT4>
 __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, int n_tokens,
                                     const int* __restrict__ frame, void* __restrict__ cache,
-                                    __half* __restrict__ aux, int batch) {
+                                    __half* __restrict__ aux, int batch, int nsplit) {
   extern __shared__ float smem[];
   float* row = smem;                       // d_qk
   float* cosv = row + d.d_qk;              // d_r / 2
@@ -75,11 +79,18 @@ __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, 
   double coord[3];
   token_coords(d.rope_dims, g.P, g.grid_w, f, tok, coord);
   rope_table(d, coord, cosv, sinv);
+  // projection of this token: the sum of the K-split partials (fixed order)
   const float* src = y + ((size_t)b * n_tokens + i) * d.d_qk;
-  for (int j = threadIdx.x; j < d.d_c; j += blockDim.x) row[j] = round_to<T>(src[j]);
+  const size_t split_stride = (size_t)batch * n_tokens * d.d_qk;
+  auto proj = [&](int j) {
+    float v = src[j];
+    for (int sp = 1; sp < nsplit; ++sp) v += src[sp * split_stride + j];
+    return v;
+  };
+  for (int j = threadIdx.x; j < d.d_c; j += blockDim.x) row[j] = round_to<T>(proj(j));
   __syncthreads();
   for (int p = threadIdx.x; p < d.d_r / 2; p += blockDim.x) {
-    float x0 = src[d.d_c + 2 * p], x1 = src[d.d_c + 2 * p + 1];
+    float x0 = proj(d.d_c + 2 * p), x1 = proj(d.d_c + 2 * p + 1);
     float c = cosv[p], s = sinv[p];
     row[d.d_c + 2 * p] = round_to<T>(x0 * c - x1 * s);
     row[d.d_c + 2 * p + 1] = round_to<T>(x0 * s + x1 * c);
@@ -120,8 +131,9 @@ __global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n
   __syncthreads();
   const int npair = d.d_r / 2;
   const size_t tok_index = (size_t)b * n_q + t;
-  for (int e = threadIdx.x; e < d.H * npair; e += blockDim.x) {
-    const int h = e / npair, p = e % npair;
+  const int h0 = blockIdx.z * 16, h1 = min(d.H, h0 + 16);
+  for (int e = threadIdx.x; e < (h1 - h0) * npair; e += blockDim.x) {
+    const int h = h0 + e / npair, p = e % npair;
     const T* src = q_rope + (tok_index * d.H + h) * d.d_r;
     T* dst = q_abs + (tok_index * d.H + h) * d.d_qk + d.d_c;
     float x0 = Elem<T>::load(src, 2 * p), x1 = Elem<T>::load(src, 2 * p + 1);
@@ -162,21 +174,21 @@ __global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict_
 // host launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
-                               const int* frame, void* cache, void* aux, hipStream_t st) {
+                               const int* frame, void* cache, void* aux, int nsplit, hipStream_t st) {
   dim3 grid(n_tokens, batch);
   size_t shm = (size_t)(d.d_qk + d.d_r) * sizeof(float);
   if (d.cache_fmt == MLA_CACHE_INT4)
-    append_store_kernel<bf16_t, true><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch);
+    append_store_kernel<bf16_t, true><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch, nsplit);
   else if (d.dtype == MLA_BF16)
-    append_store_kernel<bf16_t, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch);
+    append_store_kernel<bf16_t, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
   else
-    append_store_kernel<float, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch);
+    append_store_kernel<float, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
   return hipGetLastError();
 }
 
 hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,
                          const int* q_first, void* q_abs, hipStream_t st) {
-  dim3 grid(n_q, batch);
+  dim3 grid(n_q, batch, (d.H + 15) / 16);
   size_t shm = (size_t)d.d_r * sizeof(float);
   if (d.dtype == MLA_BF16)
     q_rope_kernel<bf16_t><<<grid, 256, shm, st>>>(d, g, (const bf16_t*)q_rope, n_q, q_first, (bf16_t*)q_abs);

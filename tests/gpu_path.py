@@ -51,7 +51,7 @@ def run_gpu(cfg, inp, fill=None, keep_device=False):
     dt = api.torch_dtype(dims)
     cache, aux = api.new_cache(dims, geom, fill=fill)
     w_dkr = to_device(inp["w_dkr"])
-    ws = torch.empty(max(16, B * P * cfg.d_qk * 4), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(16, api.append_workspace_bytes(dims, geom, P)), dtype=torch.uint8, device="cuda")
     if cfg.cache_given:
         # earlier positions are given rows (dense cache); the newest frame is appended
         L = inp["cache_c"].shape[1]
