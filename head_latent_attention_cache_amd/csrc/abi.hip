@@ -262,7 +262,7 @@ size_t mla_attention_workspace_size(const mla_dims* dims, const mla_geom* geom, 
   Dims d;
   Geo g;
   if (check_dims(dims, &d) != MLA_OK || check_geom(geom, d, &g) != MLA_OK || n_q < 0) return 0;
-  if (!attn_mfma_supported(d)) return 0;
+  if (!attn_mfma_supported(d, g)) return 0;
   return attn_mfma_workspace(d, g, geom->batch, n_q * d.H);
 }
 
@@ -299,7 +299,7 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
   a.o_lat = o_lat;
   a.lse = lse;
   hipStream_t st = (hipStream_t)stream;
-  if (attn_mfma_supported(d)) {
+  if (attn_mfma_supported(d, g)) {
     const size_t need = attn_mfma_workspace(d, g, B, a.n_rows);
     if (need && (workspace_bytes < need || !workspace))
       return fail(MLA_ERR_WORKSPACE, "attention workspace needs %zu bytes, got %zu", need, workspace_bytes);

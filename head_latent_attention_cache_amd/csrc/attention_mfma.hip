@@ -122,10 +122,23 @@ constexpr int MF_QLDS_STEPS = 8;         // query 16-dim steps kept in LDS (per 
 // tile classes
 enum : uint8_t { TILE_SKIP = 0, TILE_FULL = 1, TILE_MASKED = 2, TILE_MASKED_ZERO = 3 };
 
+// LDS bytes of one packed INT4 tile (staging): codes [key][DQK / 2 B], then
+// the content scales [key][DC / 32] fp16, then the rotary scales [key] fp16
 template <int DC, int DR>
+constexpr int q4_stage_bytes() { return MF_BN * (DC + DR) / 2 + MF_BN * (DC / 32) * 2 + MF_BN * 2; }
+
+template <int DC, int DR, bool Q4>
+constexpr size_t attn_mfma_lds_bytes() {
+  return (size_t)(Q4 ? 2 : MF_NBUF) * ((DC + DR) / 64) * MF_BN * 128 +
+         (Q4 ? 2 * (size_t)q4_stage_bytes<DC, DR>() : 0) + (size_t)MF_WAVES * MF_QLDS_STEPS * 1024 +
+         2 * MF_WAVES * 2 * 1024 + MF_ROWS * sizeof(float) + MF_MAX_TPS;
+}
+
+template <int DC, int DR, bool Q4>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(MfmaArgs ma) {
   constexpr int DQK = DC + DR;
+  constexpr int NTB = Q4 ? 2 : MF_NBUF;      // bf16 tile buffers
   constexpr int NKS = DQK / 16;              // 16-dim MFMA steps of the score product
   constexpr int NCG = DQK / 64;              // 64-dim groups per row (128 B)
   constexpr int TILE_BYTES = NCG * MF_BN * 128;
@@ -137,8 +150,11 @@ void attn_mfma_kernel(MfmaArgs ma) {
   static_assert(DQK % 64 == 0 && WDIMS % 32 == 0, "widths");
   static_assert(TILE_BYTES % (256 * 16) == 0, "tile");
 
+  constexpr int STG_BYTES = Q4 ? q4_stage_bytes<DC, DR>() : 0;
+  static_assert(STG_BYTES % 16 == 0, "staging");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* qlds = smem + MF_NBUF * TILE_BYTES;              // [wave][NKS_LDS][64][16 B]
+  uint8_t* stg = smem + NTB * TILE_BYTES;                   // INT4: [2] packed tiles
+  uint8_t* qlds = stg + 2 * STG_BYTES;                      // [wave][NKS_LDS][64][16 B]
   uint8_t* plds = qlds + MF_WAVES * NKS_LDS * 1024;         // [2][wave][2 steps][64][16 B]
   float* lrow = (float*)(plds + 2 * MF_WAVES * 2 * 1024);   // [128] row sums
   uint8_t* cls = (uint8_t*)(lrow + MF_ROWS);
@@ -290,50 +306,11 @@ void attn_mfma_kernel(MfmaArgs ma) {
       }
   };
 
-  for (int pass = 0;; ++pass) {
-#pragma unroll
-  for (int d = 0; d < NDB * MF_WAVES; ++d)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  l_run = 0.f;
-  m_run = pass == 0 ? -INFINITY : m_seen;
+  // ---- scores of one tile, S^T = K . Q^T (one 32-key block, LDS reads KPF
+  // steps ahead), mask, probabilities against the row's reference maximum
+  // (log2 domain), published to P buffer `pbuf` ----
   bool overflow = false;
-
-  int cur = next_tile(0);
-  int bcur = 0, bprev = -1, pb = 0;
-  if (cur < ntl) issue_loads(cur, 0);
-  while (cur < ntl) {
-    const int nxt = next_tile(cur + 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // one barrier per tile: this tile is in LDS, the previous tile's
-    // probabilities are published, and the buffer two tiles back is free
-    lds_barrier();
-    // buffer of the next tile: the one holding neither this tile nor the previous one
-    const int bnext = bprev < 0 ? (bcur + 1) % MF_NBUF : 3 - bcur - bprev;
-    if (nxt < ntl) issue_loads(nxt, bnext);
-    uint8_t* tile = smem + bcur * TILE_BYTES;
-    const int k0 = (t_begin + cur) * MF_BN;
-    const int cl = cls[cur];
-    if (cl == TILE_MASKED_ZERO) {
-      // zero never-written (or past-the-end) keys of this tile
-      for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
-        const int key = e / (NCG * 8), rest = e % (NCG * 8);
-        const int s = k0 + key;
-        const bool ok = s < cap && ring_frame(s / P, newest, nm, W) >= 0;
-        if (!ok) {
-          const int cg = rest >> 3, pos = rest & 7;
-          *(uint4*)(tile + (cg * MF_BN + key) * 128 + pos * 16) = make_uint4(0, 0, 0, 0);
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      lds_barrier();
-    }
-
-    // ---- output product of the previous tile: its probabilities were
-    // published before this tile's barrier ----
-    if (bprev >= 0) output_product(bprev, pb ^ 1);
-
-    // ---- S^T = K . Q^T : one 32-key block, LDS reads KPF steps ahead ----
+  auto scores_softmax = [&](const uint8_t* tile, int k0, int cl, int pbuf) {
     f32x16_t s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -365,9 +342,6 @@ void attn_mfma_kernel(MfmaArgs ma) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-
-    // ---- mask, softmax against the row's reference maximum (log2 domain) ----
     if (cl != TILE_FULL) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -386,7 +360,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
     float lsum = 0.f;
-    LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + (pb * MF_WAVES + wave) * 2 * 1024);
+    LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + (pbuf * MF_WAVES + wave) * 2 * 1024);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       bf16x8_t pf;
@@ -401,14 +375,156 @@ void attn_mfma_kernel(MfmaArgs ma) {
     }
     l_run += lsum;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    bprev = bcur;
-    bcur = bnext;
-    pb ^= 1;
-    cur = nxt;
-  }
-  if (bprev >= 0) {
+  };
+
+  // ---- packed INT4 tiles: the packed bytes and scales of a tile are copied
+  // into a staging buffer (global_load_lds), then dequantised into the bf16
+  // tile layout.  Requires capacity % 8 == 0 (16-byte aligned scale rows).
+  constexpr int Q4_CODE_CH = MF_BN * DQK / 32;          // 16-byte chunks of codes
+  constexpr int Q4_CS_CH = MF_BN * DC / 256;            // of content scales
+  constexpr int Q4_RS_CH = MF_BN * 2 / 16;              // of rotary scales
+  constexpr int Q4_CH = Q4_CODE_CH + Q4_CS_CH + Q4_RS_CH;
+  constexpr int Q4_CODE_BYTES = MF_BN * DQK / 2, Q4_CS_BYTES = MF_BN * DC / 16;
+  const uint8_t* q4_codes = (const uint8_t*)a.cache + (size_t)b * cap * (DQK / 2);
+  const uint8_t* q4_cs = (const uint8_t*)a.aux + (size_t)b * cap * (DC / 16);
+  const uint8_t* q4_rs = (const uint8_t*)a.aux + (size_t)a.batch * cap * (DC / 16) + (size_t)b * cap * 2;
+  auto stage_dma = [&](int t, int sidx) {
+    const int k0 = (t_begin + t) * MF_BN;
+    const uint32_t lds_stage = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
+#pragma unroll
+    for (int r = 0; r < (Q4_CH + 255) / 256; ++r) {
+      if (r * 256 + wave * 64 >= Q4_CH) break;   // wave-uniform
+      const int j = r * 256 + wave * 64 + lane;
+      const uint8_t* src;
+      if (j < Q4_CODE_CH) {
+        const int key = j / (DQK / 32), off = j % (DQK / 32);
+        src = q4_codes + (size_t)min(k0 + key, cap - 1) * (DQK / 2) + off * 16;
+      } else if (j < Q4_CODE_CH + Q4_CS_CH) {
+        const int jj = j - Q4_CODE_CH, key = jj / (DC / 256);
+        src = q4_cs + (size_t)min(k0 + key, cap - 1) * (DC / 16) + (jj % (DC / 256)) * 16;
+      } else {
+        // 8 keys per chunk; past-the-end chunks re-read the last 8 keys
+        const int jj = min(j - Q4_CODE_CH - Q4_CS_CH, Q4_RS_CH - 1);
+        src = q4_rs + (size_t)min(k0 + 8 * jj, cap - 8) * 2;
+      }
+      if (j < Q4_CH) dma16(src, lds_stage + (r * 256 + wave * 64) * 16);
+    }
+  };
+  auto dequant = [&](int t, int sidx, int tbuf) {
+    const int k0 = (t_begin + t) * MF_BN;
+    const bool zero_check = cls[t] == TILE_MASKED_ZERO;
+    const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
+    LDS_AS uint8_t* tp = (LDS_AS uint8_t*)(smem + tbuf * TILE_BYTES);
+    constexpr int CPK = DQK / 8;   // 16-byte bf16 chunks per key
+#pragma unroll 3
+    for (int i = 0; i < MF_BN * CPK / 256; ++i) {
+      const int L = i * 256 + tid;
+      const int key = L / CPK, c = L % CPK;
+      const uint32_t codes = *(const LDS_AS uint32_t*)(sp + key * (DQK / 2) + c * 4);
+      const uint16_t sbits = c < DC / 8
+          ? *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + key * (DC / 16) + (c >> 2) * 2)
+          : *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + Q4_CS_BYTES + key * 2);
+      const float sc = __half2float(__ushort_as_half(sbits));
+      bool ok = true;
+      if (zero_check) {
+        const int sl = k0 + key;
+        ok = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0;
+      }
+      bf16x8_t v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // element e = nibble e of the little-endian word (low nibble first), sign-extended
+        const int q = ((int)(codes << (28 - 4 * e))) >> 28;
+        v[e] = __builtin_bit_cast(__bf16, ok ? f32_to_bf16((float)q * sc) : (bf16_t)0);
+      }
+      *(LDS_AS bf16x8_t*)(tp + ((c >> 3) * MF_BN + key) * 128 + (((c & 7) ^ key_swizzle(key)) << 4)) = v;
+    }
+  };
+
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+  for (int d = 0; d < NDB * MF_WAVES; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  l_run = 0.f;
+  m_run = pass == 0 ? -INFINITY : m_seen;
+  overflow = false;
+
+  if constexpr (!Q4) {
+    int cur = next_tile(0);
+    int bcur = 0, bprev = -1, pb = 0;
+    if (cur < ntl) issue_loads(cur, 0);
+    while (cur < ntl) {
+      const int nxt = next_tile(cur + 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // one barrier per tile: this tile is in LDS, the previous tile's
+      // probabilities are published, and the buffer two tiles back is free
+      lds_barrier();
+      // buffer of the next tile: the one holding neither this tile nor the previous one
+      const int bnext = bprev < 0 ? (bcur + 1) % MF_NBUF : 3 - bcur - bprev;
+      if (nxt < ntl) issue_loads(nxt, bnext);
+      uint8_t* tile = smem + bcur * TILE_BYTES;
+      const int k0 = (t_begin + cur) * MF_BN;
+      const int cl = cls[cur];
+      if (cl == TILE_MASKED_ZERO) {
+        // zero never-written (or past-the-end) keys of this tile
+        for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
+          const int key = e / (NCG * 8), rest = e % (NCG * 8);
+          const int s = k0 + key;
+          const bool ok = s < cap && ring_frame(s / P, newest, nm, W) >= 0;
+          if (!ok) {
+            const int cg = rest >> 3, pos = rest & 7;
+            *(uint4*)(tile + (cg * MF_BN + key) * 128 + pos * 16) = make_uint4(0, 0, 0, 0);
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+      }
+      // output product of the previous tile: its probabilities were published
+      // before this tile's barrier
+      if (bprev >= 0) output_product(bprev, pb ^ 1);
+      scores_softmax(tile, k0, cl, pb);
+      bprev = bcur;
+      bcur = bnext;
+      pb ^= 1;
+      cur = nxt;
+    }
+    if (bprev >= 0) {
+      lds_barrier();
+      output_product(bprev, pb ^ 1);
+    }
+  } else {
+    // tile sequence number `it` uses bf16 buffer it & 1 and staging it & 1
+    int cur = next_tile(0), it = 0, pb = 0;
+    if (cur < ntl) {
+      stage_dma(cur, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      dequant(cur, 0, 0);
+    }
+    int nxt = next_tile(cur + 1);
+    if (nxt < ntl) stage_dma(nxt, 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     lds_barrier();
-    output_product(bprev, pb ^ 1);
+    while (cur < ntl) {
+      const int bc = it & 1;
+      const int nn = nxt < ntl ? next_tile(nxt + 1) : ntl;
+      if (it > 0) output_product(bc ^ 1, pb ^ 1);
+      scores_softmax(smem + bc * TILE_BYTES, (t_begin + cur) * MF_BN, cls[cur], pb);
+      // the previous tile's buffer is free, the next tile's packed bytes
+      // have landed, this tile's probabilities are published
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      if (nxt < ntl) dequant(nxt, (it + 1) & 1, bc ^ 1);
+      if (nn < ntl) stage_dma(nn, it & 1);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();
+      ++it;
+      pb ^= 1;
+      cur = nxt;
+      nxt = nn;
+    }
+    if (it > 0) output_product((it - 1) & 1, pb ^ 1);
   }
   __syncthreads();
   if (!__syncthreads_or(overflow)) break;
@@ -498,12 +614,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
 // host side
 // ---------------------------------------------------------------------------
 // MLA_ATTN_KERNEL=generic routes every shape to the generic kernel (testing)
-bool attn_mfma_supported(const Dims& d) {
+// Shapes with an MFMA kernel: bf16, d_c = 512, d_r = 64; the packed INT4
+// cache also needs capacity % 8 == 0 (16-byte aligned scale rows).
+bool attn_mfma_supported(const Dims& d, const Geo& g) {
   static const bool generic = [] {
     const char* e = getenv("MLA_ATTN_KERNEL");
     return e && strcmp(e, "generic") == 0;
   }();
-  return !generic && d.dtype == MLA_BF16 && d.cache_fmt == MLA_CACHE_DENSE && d.d_c == 512 && d.d_r == 64;
+  if (generic || d.dtype != MLA_BF16 || d.d_c != 512 || d.d_r != 64) return false;
+  return d.cache_fmt == MLA_CACHE_DENSE || (d.cache_fmt == MLA_CACHE_INT4 && g.capacity % 8 == 0);
 }
 
 // number of key splits: balance whole rounds of work-groups over 256 CUs
@@ -566,10 +685,9 @@ hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStr
     ma.ws_lse = ma.ws_o + (size_t)ma.nsplit * a.batch * a.n_rows * a.d.d_c;
   }
   constexpr int DC = 512, DR = 64;
-  const size_t shm = MF_NBUF * (size_t)((DC + DR) / 64) * MF_BN * 128 +
-                     (size_t)MF_WAVES * MF_QLDS_STEPS * 1024 + 2 * MF_WAVES * 2 * 1024 +
-                     MF_ROWS * sizeof(float) + MF_MAX_TPS;
-  auto kern = attn_mfma_kernel<DC, DR>;
+  const bool q4 = a.d.cache_fmt == MLA_CACHE_INT4;
+  const size_t shm = q4 ? attn_mfma_lds_bytes<DC, DR, true>() : attn_mfma_lds_bytes<DC, DR, false>();
+  auto kern = q4 ? attn_mfma_kernel<DC, DR, true> : attn_mfma_kernel<DC, DR, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   const int blocks = a.batch * ma.nsplit * ma.n_rb;

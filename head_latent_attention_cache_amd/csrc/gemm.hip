@@ -188,96 +188,150 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // skinny bf16 kernel for M <= 32 (decode-time products, weight-bandwidth bound)
-//   work-group: all M rows x 64 output columns; the 4 waves split the
-//   work-group's K range into quarters and each streams its weight slice
-//   straight into MFMA B fragments (16 contiguous bytes per lane from a
-//   K-contiguous weight row), two 64-wide K stages in flight per wave.  The
-//   four partial 32 x 64 tiles are summed in LDS at the end (fixed order).
+//   work-group: all M rows x BN output columns.  The weight block of a K
+//   stage (BN weight rows x SEG elements) is read with fully coalesced 16-byte
+//   loads (each wave instruction covers 1 KB of consecutive row bytes),
+//   staged through registers into LDS, and read back as MFMA B fragments; the
+//   SEG / 16 MFMA steps of a stage are split over the 4 waves, each step
+//   serving BN / 32 column blocks with one activation fragment.  The
+//   activation (A) is re-read once per work-group, so wider tiles cut that
+//   traffic.  SK_NST stages are in flight per wave; every load is
+//   unconditional (addresses clamped into the operand, values zeroed by
+//   mask), so the compiler's load counting keeps the later stages in flight
+//   while one is consumed.  The activation fragments come straight from
+//   global memory (cache-resident).  The four wave partials are summed in
+//   LDS at the end (fixed order).
 //   Optional split of the K range over work-groups (blockIdx.y) writes float
 //   partials at C + split * sSplit for the caller to sum.
 // ---------------------------------------------------------------------------
-constexpr int SK_BN = 64, SK_BK = 64;
-
+constexpr int SK_BN = 64, SK_SEG = 256;
+template <int SK_NST, int BN, int SEG>
 __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
-  __shared__ float red[4][2][64][17];
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  constexpr int CPR = SEG / 8;                 // 16-byte chunks per weight row and stage
+  constexpr int WLOADS = BN * CPR / 256;       // 16-byte weight loads per lane and stage
+  constexpr int NB = BN / 32;                  // 32-column MFMA blocks
+  constexpr int TSTEPS = SEG / 64;             // 16-wide MFMA steps per wave and stage
+  static_assert(BN % 32 == 0 && SEG % 64 == 0 && (BN * CPR) % 256 == 0, "skinny tile");
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][BN * SEG * 2];
   const int z = blockIdx.z;
   const bf16_t* A = (const bf16_t*)a.A + (size_t)z * a.sA;
   const bf16_t* B = (const bf16_t*)a.B + (size_t)z * a.sB;
-  const int n0 = blockIdx.x * SK_BN;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5;
-  // K range of this work-group, then of this wave (multiples of SK_BK)
-  const int kchunks = (a.K + SK_BK - 1) / SK_BK;
-  const int wg_chunks = (kchunks + a.ksplit - 1) / a.ksplit;
-  const int c_begin = blockIdx.y * wg_chunks;
-  const int c_end = min(c_begin + wg_chunks, kchunks);
-  const int w_chunks = (max(c_end - c_begin, 0) + 3) / 4;
-  const int wc0 = c_begin + wave * w_chunks;
-  const int wc1 = min(wc0 + w_chunks, c_end);
+  const int n0 = blockIdx.x * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  // K stages of this work-group
+  const int kst = (a.K + SEG - 1) / SEG;
+  const int wg_st = (kst + a.ksplit - 1) / a.ksplit;
+  const int s_begin = blockIdx.y * wg_st;
+  const int s_end = min(s_begin + wg_st, kst);
+  const int k_last = a.K - 8;   // K % 8 == 0: a clamped 8-element load stays inside the row
 
-  const int m = lane & 31;
-  const bool m_ok = m < a.M;
-  const bf16_t* arow = A + (size_t)(m_ok ? m : 0) * a.lda;
-  const bf16_t* brow0 = B + (size_t)min(n0 + m, a.N - 1) * a.ldb;
-  const bf16_t* brow1 = B + (size_t)min(n0 + 32 + m, a.N - 1) * a.ldb;
-  const bool n0_ok = n0 + m < a.N, n1_ok = n0 + 32 + m < a.N;
-
-  f32x16_t acc[2];
+  // weight loads: load q of this lane takes linear chunk (q * 4 + wave) * 64 + lane
+  // of the stage block (row-major [BN][CPR]), so each wave instruction reads
+  // 1 KB of consecutive row bytes; LDS keeps a row's chunk c at position
+  // c ^ (row & 7) (conflict-free fragment reads)
+  const bf16_t* wrow[WLOADS];
+  int wcol[WLOADS], wlds[WLOADS];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int q = 0; q < WLOADS; ++q) {
+    const int L = (q * 4 + wave) * 64 + lane;
+    const int r = L / CPR, c = L % CPR;
+    wrow[q] = B + (size_t)min(n0 + r, a.N - 1) * a.ldb;
+    wcol[q] = c * 8;
+    wlds[q] = r * (SEG * 2) + ((c ^ (r & 7)) << 4);
+  }
+  // fragments: lane (l32, g) of MFMA step t of this wave reads chunk
+  // c = 2 * (TSTEPS * wave + t) + g of weight row 32 * j + l32 (B, block j)
+  // and of activation row l32 (A)
+  const bool m_ok = l32 < a.M;
+  const bf16_t* arow = A + (size_t)(m_ok ? l32 : 0) * a.lda;
+
+  struct Stage { u32x4v w[WLOADS], x[TSTEPS]; int s; };
+  auto load_stage = [&](Stage& st, int sidx) {
+    st.s = min(sidx, s_end);
+    const int sc = min(sidx, s_end - 1);
+#pragma unroll
+    for (int q = 0; q < WLOADS; ++q)
+      st.w[q] = *(const u32x4v*)(wrow[q] + min(sc * SEG + wcol[q], k_last));
+#pragma unroll
+    for (int t = 0; t < TSTEPS; ++t)
+      st.x[t] = *(const u32x4v*)(arow + min(sc * SEG + (2 * (TSTEPS * wave + t) + g) * 8, k_last));
+  };
+  f32x16_t acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
-
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  auto ld = [&](const bf16_t* row, int k, bool ok) -> bf16x8_t {
-    u32x4v v = {0u, 0u, 0u, 0u};
-    if (ok && k < a.K) v = *(const u32x4v*)(row + k);
-    return __builtin_bit_cast(bf16x8_t, v);
-  };
-  // one K stage = 4 MFMA steps of 16: A fragment + two B fragments each
-  struct Stage { bf16x8_t fa[4], fb0[4], fb1[4]; };
-  auto load_stage = [&](Stage& st, int c) {
+  int buf = 0;
+  auto use_stage = [&](const Stage& st) {
+    if (st.s >= s_end) return;   // empty stage (wave-uniform)
+    lds_u8* wb = (lds_u8*)wbuf[buf];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int k = c * SK_BK + ks * 16 + g * 8;
-      st.fa[ks] = ld(arow, k, m_ok);
-      st.fb0[ks] = ld(brow0, k, n0_ok);
-      st.fb1[ks] = ld(brow1, k, n1_ok);
-    }
-  };
-  Stage s0, s1;
-  if (wc0 < wc1) load_stage(s0, wc0);
-  if (wc0 + 1 < wc1) load_stage(s1, wc0 + 1);
-  for (int c = wc0; c < wc1; c += 2) {
+    for (int q = 0; q < WLOADS; ++q) *(__attribute__((address_space(3))) u32x4v*)(wb + wlds[q]) = st.w[q];
+    // barrier without __syncthreads()'s fence, which would also wait for the
+    // global loads of the later stages: only this stage's LDS writes must land
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0.fa[ks], s0.fb0[ks], acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0.fa[ks], s0.fb1[ks], acc[1], 0, 0, 0);
-    }
-    if (c + 2 < wc1) load_stage(s0, c + 2);
-    if (c + 1 < wc1) {
+    for (int t = 0; t < TSTEPS; ++t) {
+      const int c = 2 * (TSTEPS * wave + t) + g;
+      const int k = st.s * SEG + c * 8;
+      // zeroing by mask (a select would be folded into the load's address)
+      const uint32_t ma = (k < a.K && m_ok) ? ~0u : 0u;
+      const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, st.x[t] & ma);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1.fa[ks], s1.fb0[ks], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1.fa[ks], s1.fb1[ks], acc[1], 0, 0, 0);
+      for (int j = 0; j < NB; ++j) {
+        const int r = 32 * j + l32;
+        const u32x4v wv = *(const __attribute__((address_space(3))) u32x4v*)(wb + r * (SEG * 2) + ((c ^ (r & 7)) << 4));
+        const uint32_t mb = (k < a.K && n0 + r < a.N) ? ~0u : 0u;
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8_t, wv & mb), acc[j], 0, 0, 0);
       }
-      if (c + 3 < wc1) load_stage(s1, c + 3);
+    }
+    buf ^= 1;
+  };
+  if (s_begin < s_end) {
+    // every load is issued inside the loop (the first pass consumes empty
+    // stages), so the outstanding-load count at the loop head is the same on
+    // entry and on the back edge
+    Stage st[SK_NST];
+    const u32x4v zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < SK_NST; ++i) {
+      st[i].s = s_end;
+#pragma unroll
+      for (int q = 0; q < WLOADS; ++q) st[i].w[q] = zero;
+#pragma unroll
+      for (int t = 0; t < TSTEPS; ++t) st[i].x[t] = zero;
+    }
+    for (int c = s_begin - SK_NST; c < s_end; c += SK_NST) {
+#pragma unroll
+      for (int i = 0; i < SK_NST; ++i) {
+        use_stage(st[i]);
+        load_stage(st[i], c + i + SK_NST);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   // sum the four wave partials (fixed order) and store
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[wave][j][lane][e] = acc[j][e];
   __syncthreads();
-  const int t = threadIdx.x;
-  const int l = t & 63, j = (t >> 6) & 1, eh = (t >> 7) * 8;
+  float* red = (float*)wbuf;   // [4 waves][NB][64 lanes][17]
+  static_assert(4 * NB * 64 * 17 * 4 <= 2 * BN * SEG * 2, "reduction buffer");
 #pragma unroll
-  for (int e = eh; e < eh + 8; ++e) {
-    const float v = red[0][j][l][e] + red[1][j][l][e] + red[2][j][l][e] + red[3][j][l][e];
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[((wave * NB + j) * 64 + lane) * 17 + e] = acc[j][e];
+  __syncthreads();
+  for (int o = tid; o < NB * 64 * 16; o += 256) {
+    const int e = o & 15, l = (o >> 4) & 63, j = o >> 10;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += red[((w * NB + j) * 64 + l) * 17 + e];
     const int mm = 8 * (e / 4) + 4 * (l / 32) + (e % 4);
-    const int nn = n0 + j * 32 + (l & 31);
+    const int nn = n0 + 32 * j + (l & 31);
     if (mm < a.M && nn < a.N) {
       if (a.ksplit > 1)
         ((float*)a.C)[(size_t)blockIdx.y * a.sSplit + (size_t)z * a.sC + (size_t)mm * a.ldc + nn] = v;
@@ -292,10 +346,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
 int gemm_skinny_ksplit(int dtype, int M, int N, int K, int batch) {
   if (dtype != MLA_BF16 || M > 32 || M <= 0) return 1;
   const int wgs = ((N + SK_BN - 1) / SK_BN) * batch;
-  const int kchunks = (K + SK_BK - 1) / SK_BK;
+  const int kst = (K + SK_SEG - 1) / SK_SEG;
   int ks = 1;
-  // aim at >= 256 work-groups, keeping >= 4 K stages per wave
-  while (wgs * ks < 256 && (kchunks / (ks * 2)) >= 16) ks *= 2;
+  // aim at >= 512 work-groups, keeping >= 4 K stages per work-group
+  while (wgs * ks < 512 && kst / (ks * 2) >= 4) ks *= 2;
   return ks;
 }
 
@@ -309,7 +363,12 @@ hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st) {
   }
   if (a.M <= 32) {
     dim3 grid((a.N + SK_BN - 1) / SK_BN, a.ksplit, a.batch);
-    gemm_skinny_bf16_kernel<<<grid, 256, 0, st>>>(a);
+    // two K stages in flight (measured best for the 64-column tile: deeper
+    // pipelines cost occupancy), one when the work-group has a single stage
+    const int kst = (a.K + SK_SEG - 1) / SK_SEG;
+    const int wg_st = (kst + a.ksplit - 1) / a.ksplit;
+    if (wg_st >= 2) gemm_skinny_bf16_kernel<2, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
+    else gemm_skinny_bf16_kernel<1, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
   // bf16: small-M products use 64-row tiles, wide ones 128 x 128

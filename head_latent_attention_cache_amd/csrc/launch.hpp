@@ -42,7 +42,7 @@ hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_r
 hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* cache, const void* aux,
                           float* out, hipStream_t st);
 hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t st);
-bool attn_mfma_supported(const Dims& d);
+bool attn_mfma_supported(const Dims& d, const Geo& g);
 size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows);
 hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
 

@@ -82,9 +82,17 @@ __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, 
   // projection of this token: the sum of the K-split partials (fixed order)
   const float* src = y + ((size_t)b * n_tokens + i) * d.d_qk;
   const size_t split_stride = (size_t)batch * n_tokens * d.d_qk;
+  // (loads of 8 partials are issued together, then summed in split order)
   auto proj = [&](int j) {
-    float v = src[j];
-    for (int sp = 1; sp < nsplit; ++sp) v += src[sp * split_stride + j];
+    float v = 0.f;
+    for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = sp0 + u < nsplit ? src[(sp0 + u) * split_stride + j] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp0 + u < nsplit) v = sp0 + u == 0 ? t[u] : v + t[u];
+    }
     return v;
   };
   for (int j = threadIdx.x; j < d.d_c; j += blockDim.x) row[j] = round_to<T>(proj(j));
@@ -178,11 +186,11 @@ hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const flo
   dim3 grid(n_tokens, batch);
   size_t shm = (size_t)(d.d_qk + d.d_r) * sizeof(float);
   if (d.cache_fmt == MLA_CACHE_INT4)
-    append_store_kernel<bf16_t, true><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch, nsplit);
+    append_store_kernel<bf16_t, true><<<grid, 512, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch, nsplit);
   else if (d.dtype == MLA_BF16)
-    append_store_kernel<bf16_t, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
+    append_store_kernel<bf16_t, false><<<grid, 512, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
   else
-    append_store_kernel<float, false><<<grid, 128, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
+    append_store_kernel<float, false><<<grid, 512, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
   return hipGetLastError();
 }
 

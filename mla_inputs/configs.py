@@ -119,8 +119,9 @@ SMALL_CONFIGS = {
     # frame-causal 3-frame chunk over a wrapped 6-frame ring, d_r = 512
     4: LONG_VIDEO.replace(name="long_video_small", n_heads=8, d_model=512,
                           grid_h=3, grid_w=5, window=6, n_frames=9, q_first=6),
-    5: VIDEO_CHUNK.replace(name="int4_video_small", d_model=512, grid_h=5,
-                           grid_w=7, window=4, n_frames=6, q_first=5,
+    # 36-token frames: capacity 144 (a multiple of 8, ragged last key tile)
+    5: VIDEO_CHUNK.replace(name="int4_video_small", d_model=512, grid_h=6,
+                           grid_w=6, window=4, n_frames=6, q_first=5,
                            cache_fmt="int4"),
 }
 

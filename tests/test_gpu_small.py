@@ -61,6 +61,26 @@ def test_partially_filled_ring_with_poisoned_slots(gpu_lib):
     _check_all(cfg, got, om.run(cfg, inp))
 
 
+def test_int4_partially_filled_ring_with_poisoned_slots(gpu_lib):
+    # packed codes and scales of the unwritten slots are 0xFF bytes (NaN scales)
+    cfg = SMALL_CONFIGS[5].replace(name="int4_ring_partial", n_frames=2, q_first=1)
+    _case(cfg.name)
+    inp = make_workload(cfg, seed=12)
+    got = gp.run_gpu(cfg, inp, fill=0xFF, keep_device=True)
+    ref = om.run(cfg, inp)
+    _check_all(cfg, got, ref)
+
+
+def test_int4_capacity_not_multiple_of_8(gpu_lib):
+    # 35-token frames: capacity 140 takes the generic kernel's INT4 path
+    cfg = SMALL_CONFIGS[5].replace(name="int4_cap140", grid_h=5, grid_w=7)
+    _case(cfg.name)
+    inp = make_workload(cfg, seed=13)
+    got = gp.run_gpu(cfg, inp, keep_device=True)
+    ref = om.run(cfg, inp)
+    _check_all(cfg, got, ref)
+
+
 def test_block_causal_two_frames_per_block(gpu_lib):
     cfg = SMALL_CONFIGS[4].replace(name="block2", frames_per_block=2, window=5, n_frames=8, q_first=5)
     _case(cfg.name)
@@ -145,7 +165,7 @@ def gp_bf16(a):
     return bf16_bits_from_f32(np.asarray(a, np.float32))
 
 
-@pytest.mark.parametrize("key,q_shift", [(2, 0), (3, 0), (4, 0), (3, 1), (4, -2), (3, 4)])
+@pytest.mark.parametrize("key,q_shift", [(2, 0), (3, 0), (4, 0), (3, 1), (4, -2), (3, 4), (5, 0), (5, 1)])
 def test_mask_counts_bitexact(gpu_lib, key, q_shift):
     """q_abs = 0 makes every visible score 0, so exp(lse) is the number of
     visible keys exactly (and rows with none give lse = -inf)."""
@@ -193,7 +213,7 @@ def test_fully_masked_rows(gpu_lib):
     assert torch.all(torch.isneginf(lse)).item()
 
 
-@pytest.mark.parametrize("key", [2, 3])
+@pytest.mark.parametrize("key", [2, 3, 5])
 def test_attention_is_deterministic(gpu_lib, key):
     import torch
     from head_latent_attention_cache_amd import api

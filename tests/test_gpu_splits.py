@@ -38,14 +38,14 @@ def _run(key, env_extra, out, tmp_path):
     return np.load(tmp_path / (out + ".npy"))
 
 
-@pytest.mark.parametrize("key", [2, 3])
+@pytest.mark.parametrize("key", [2, 3, 5])
 def test_split_count_invariance(gpu_lib, key, tmp_path):
     outs = [_run(key, {"MLA_ATTN_SPLITS": str(ns)}, f"s{ns}", tmp_path) for ns in (1, 2, 3)]
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) <= 2e-2
 
 
-@pytest.mark.parametrize("key", [2, 3])
+@pytest.mark.parametrize("key", [2, 3, 5])
 def test_mfma_matches_generic_kernel(gpu_lib, key, tmp_path):
     a = _run(key, {}, "mfma", tmp_path)
     g = _run(key, {"MLA_ATTN_KERNEL": "generic"}, "generic", tmp_path)
