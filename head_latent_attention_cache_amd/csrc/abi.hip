@@ -262,8 +262,9 @@ size_t mla_attention_workspace_size(const mla_dims* dims, const mla_geom* geom, 
   Dims d;
   Geo g;
   if (check_dims(dims, &d) != MLA_OK || check_geom(geom, d, &g) != MLA_OK || n_q < 0) return 0;
-  if (!attn_mfma_supported(d, g)) return 0;
-  return attn_mfma_workspace(d, g, geom->batch, n_q * d.H);
+  if (attn_mfma_supported(d, g)) return attn_mfma_workspace(d, g, geom->batch, n_q * d.H);
+  if (attn_dsplit_supported(d)) return attn_dsplit_workspace(d, g, geom->batch, n_q * d.H);
+  return 0;
 }
 
 mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
@@ -299,12 +300,14 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
   a.o_lat = o_lat;
   a.lse = lse;
   hipStream_t st = (hipStream_t)stream;
-  if (attn_mfma_supported(d, g)) {
-    const size_t need = attn_mfma_workspace(d, g, B, a.n_rows);
+  const bool narrow = attn_mfma_supported(d, g), wide = !narrow && attn_dsplit_supported(d);
+  if (narrow || wide) {
+    const size_t need = narrow ? attn_mfma_workspace(d, g, B, a.n_rows) : attn_dsplit_workspace(d, g, B, a.n_rows);
     if (need && (workspace_bytes < need || !workspace))
       return fail(MLA_ERR_WORKSPACE, "attention workspace needs %zu bytes, got %zu", need, workspace_bytes);
     if (need && !aligned16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    return hip_status(launch_attn_mfma(a, workspace, workspace_bytes, st), st, "latent attention (MFMA)");
+    if (narrow) return hip_status(launch_attn_mfma(a, workspace, workspace_bytes, st), st, "latent attention (MFMA)");
+    return hip_status(launch_attn_dsplit(a, workspace, workspace_bytes, st), st, "latent attention (MFMA, split rows)");
   }
   return hip_status(launch_attn_simt(a, st), st, "latent attention");
 }

@@ -1,0 +1,112 @@
+// Pieces shared by the MFMA latent-attention kernels (gfx950): LDS DMA and
+// barrier helpers, the key-tile layout, tile classification and the key-split
+// bookkeeping.
+#pragma once
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace mla {
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+
+constexpr int MF_WAVES = 4;
+constexpr int MF_ROWS = 32 * MF_WAVES;   // rows per work-group
+constexpr int MF_BN = 32;                // keys per tile
+constexpr int MF_MAX_TPS = 2048;         // tiles per split (size of a class table)
+
+// work-group barrier without the memory fence of __syncthreads(): the fence
+// would wait for every outstanding global->LDS load (vmcnt(0)), including the
+// tiles prefetched ahead.  Callers wait explicitly for what they need
+// (vmcnt for the tile being consumed, lgkmcnt for their own LDS writes).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4).  Issued through asm so that the compiler does not
+// track it: it has no result register, and the kernel orders it explicitly
+// with s_waitcnt vmcnt before the barrier that publishes the tile (the
+// compiler's own tracking would add vmcnt(0) waits in front of later
+// transposed LDS reads, draining the prefetch pipeline).
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_base) : "memory");
+}
+// same, with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
+
+// 16-byte chunk swizzle of a key row.  gfx950 LDS serves 16-byte reads with a
+// 128-byte bank period, so the 8 keys read by each 8-lane group must hit 8
+// different chunk positions: position = chunk ^ (key & 7).
+__device__ __forceinline__ int key_swizzle(int key) { return key & 7; }
+
+struct MfmaArgs {
+  AttnArgs a;
+  int n_rb;          // row blocks per sequence
+  int nsplit;        // key splits
+  int tiles;         // key tiles per sequence
+  int tps;           // tiles per split
+  float* ws_o;       // [nsplit][B][n_rows][d_c] partial outputs (normalised), if nsplit > 1
+  float* ws_lse;     // [nsplit][B][n_rows]
+};
+
+// frame range [f_min, f_max] held by the slots of a tile (ring positions rp0..rp1)
+__device__ __forceinline__ void tile_frames(int rp0, int rp1, int newest, int nm, int W, int* fmin,
+                                            int* fmax) {
+  const int f0 = ring_frame(rp0, newest, nm, W), f1 = ring_frame(rp1, newest, nm, W);
+  int lo = f0 < f1 ? f0 : f1, hi = f0 > f1 ? f0 : f1;
+  const int wrap = nm + 1;                // first ring position after the newest frame
+  if (wrap > rp0 && wrap <= rp1) {        // the tile crosses from newest back to oldest
+    const int fa = ring_frame(wrap, newest, nm, W), fb = ring_frame(wrap - 1, newest, nm, W);
+    lo = min(lo, min(fa, fb));
+    hi = max(hi, max(fa, fb));
+  }
+  *fmin = lo;
+  *fmax = hi;
+}
+
+// tile classes
+enum : uint8_t { TILE_SKIP = 0, TILE_FULL = 1, TILE_MASKED = 2, TILE_MASKED_ZERO = 3 };
+
+// class of key tile [k0, k0 + MF_BN) for the query frames [gfq_min, gfq_max]
+// of a work-group: skipped (no visible key), fully visible, masked, or masked
+// with never-written / past-the-end slots (their LDS bytes must be zeroed)
+__device__ __forceinline__ uint8_t classify_tile(int k0, int cap, int P, int newest, int nm, int W, int fpb,
+                                                 int gfq_min, int gfq_max) {
+  const int k1 = min(k0 + MF_BN, cap) - 1;
+  int fmin, fmax;
+  tile_frames(k0 / P, k1 / P, newest, nm, W, &fmin, &fmax);
+  const int fminw = fmin < 0 ? 0 : fmin;
+  if (fmax < 0 || floor_div(fminw, fpb) > floor_div(gfq_max, fpb) || gfq_min - fmax >= W) return TILE_SKIP;
+  if (fmin < 0 || k0 + MF_BN > cap) return TILE_MASKED_ZERO;
+  if (floor_div(fmax, fpb) <= floor_div(gfq_min, fpb) && gfq_max - fmin < W) return TILE_FULL;
+  return TILE_MASKED;
+}
+
+// XCD-aware work-group order: consecutive linear indices land on one XCD
+// (the work-groups sharing a sequence's key range share an L2)
+__device__ __forceinline__ int xcd_linear_block() {
+  const int total = gridDim.x, id = blockIdx.x;
+  const int xcd = id & 7, per = total >> 3, rem = total & 7;
+  return xcd * per + min(xcd, rem) + (id >> 3);
+}
+
+// key-split plan of a launch: row blocks of `rows_per_wg`, MF_BN-key tiles,
+// `ns` splits of `tps` tiles each
+void attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, int* n_rb, int* tiles,
+               int* ns, int* tps);
+// deterministic log-sum-exp merge of the splits' partial outputs
+hipError_t launch_attn_merge(const MfmaArgs& ma, hipStream_t st);
+
+}  // namespace mla

@@ -41,86 +41,12 @@
 //  * Optional split of the key range over work-groups with a deterministic
 //    log-sum-exp merge (decode and load balance); the block order is
 //    XCD-aware so that the work-groups sharing a key range share an L2.
-#include <cstdlib>
-#include <cstring>
-
-#include "launch.hpp"
+#include "attention_common.hpp"
 
 namespace mla {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-#define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
-
-constexpr int MF_WAVES = 4;
-constexpr int MF_ROWS = 32 * MF_WAVES;   // rows per work-group
-constexpr int MF_BN = 32;                // keys per tile
-
-// work-group barrier without the memory fence of __syncthreads(): the fence
-// would wait for every outstanding global->LDS load (vmcnt(0)), including the
-// tiles prefetched ahead.  Callers wait explicitly for what they need
-// (vmcnt for the tile being consumed, lgkmcnt for their own LDS writes).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
-// (global_load_lds_dwordx4).  Issued through asm so that the compiler does not
-// track it: it has no result register, and the kernel orders it explicitly
-// with s_waitcnt vmcnt before the barrier that publishes the tile (the
-// compiler's own tracking would add vmcnt(0) waits in front of later
-// transposed LDS reads, draining the prefetch pipeline).
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_base) : "memory");
-}
-// same, with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
-__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
-}
-
-// 16-byte chunk swizzle of a key row.  gfx950 LDS serves 16-byte reads with a
-// 128-byte bank period, so the 8 keys read by each 8-lane group must hit 8
-// different chunk positions: position = chunk ^ (key & 7).
-__device__ __forceinline__ int key_swizzle(int key) { return key & 7; }
-
-struct MfmaArgs {
-  AttnArgs a;
-  int n_rb;          // row blocks per sequence
-  int nsplit;        // key splits
-  int tiles;         // key tiles per sequence
-  int tps;           // tiles per split
-  float* ws_o;       // [nsplit][B][n_rows][d_c] partial outputs (normalised), if nsplit > 1
-  float* ws_lse;     // [nsplit][B][n_rows]
-};
-
-// frame range [f_min, f_max] held by the slots of a tile (ring positions rp0..rp1)
-__device__ __forceinline__ void tile_frames(int rp0, int rp1, int newest, int nm, int W, int* fmin,
-                                            int* fmax) {
-  const int f0 = ring_frame(rp0, newest, nm, W), f1 = ring_frame(rp1, newest, nm, W);
-  int lo = f0 < f1 ? f0 : f1, hi = f0 > f1 ? f0 : f1;
-  const int wrap = nm + 1;                // first ring position after the newest frame
-  if (wrap > rp0 && wrap <= rp1) {        // the tile crosses from newest back to oldest
-    const int fa = ring_frame(wrap, newest, nm, W), fb = ring_frame(wrap - 1, newest, nm, W);
-    lo = min(lo, min(fa, fb));
-    hi = max(hi, max(fa, fb));
-  }
-  *fmin = lo;
-  *fmax = hi;
-}
-
 constexpr int MF_NBUF = 3;               // LDS tile buffers (loads run two tiles ahead)
-constexpr int MF_MAX_TPS = 2048;         // tiles per split (size of the class table)
 constexpr int MF_QLDS_STEPS = 8;         // query 16-dim steps kept in LDS (per wave 8 KB)
-
-// tile classes
-enum : uint8_t { TILE_SKIP = 0, TILE_FULL = 1, TILE_MASKED = 2, TILE_MASKED_ZERO = 3 };
 
 // LDS bytes of one packed INT4 tile (staging): codes [key][DQK / 2 B], then
 // the content scales [key][DC / 32] fp16, then the rotary scales [key] fp16
@@ -164,11 +90,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int g = lane >> 5;                   // half of the wave
   const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
 
-  // ---- XCD-aware block order: consecutive linear indices land on one XCD ----
-  const int total = gridDim.x;
-  const int id = blockIdx.x;
-  const int xcd = id & 7, per = total >> 3, rem = total & 7;
-  const int lin = xcd * per + min(xcd, rem) + (id >> 3);
+  const int lin = xcd_linear_block();
   const int per_b = ma.nsplit * ma.n_rb;
   const int b = lin / per_b;
   const int split = (lin / ma.n_rb) % ma.nsplit;
@@ -191,24 +113,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int ntl = min(t_begin + ma.tps, ma.tiles) - t_begin;   // tiles of this split
 
   // ---- classify every tile of the split once ----
-  for (int i = tid; i < ntl; i += 256) {
-    const int k0 = (t_begin + i) * MF_BN;
-    const int k1 = min(k0 + MF_BN, cap) - 1;
-    int fmin, fmax;
-    tile_frames(k0 / P, k1 / P, newest, nm, W, &fmin, &fmax);
-    uint8_t c;
-    const int fminw = fmin < 0 ? 0 : fmin;
-    if (fmax < 0 || floor_div(fminw, fpb) > floor_div(gfq_max, fpb) || gfq_min - fmax >= W) {
-      c = TILE_SKIP;
-    } else if (fmin < 0 || k0 + MF_BN > cap) {
-      c = TILE_MASKED_ZERO;
-    } else if (floor_div(fmax, fpb) <= floor_div(gfq_min, fpb) && gfq_max - fmin < W) {
-      c = TILE_FULL;
-    } else {
-      c = TILE_MASKED;
-    }
-    cls[i] = c;
-  }
+  for (int i = tid; i < ntl; i += 256)
+    cls[i] = classify_tile((t_begin + i) * MF_BN, cap, P, newest, nm, W, fpb, gfq_min, gfq_max);
 
   // ---- queries of this lane's row: B fragments of the score steps ----
   const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (row_ok ? row : 0)) * DQK;
@@ -613,15 +519,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// MLA_ATTN_KERNEL=generic routes every shape to the generic kernel (testing)
 // Shapes with an MFMA kernel: bf16, d_c = 512, d_r = 64; the packed INT4
 // cache also needs capacity % 8 == 0 (16-byte aligned scale rows).
 bool attn_mfma_supported(const Dims& d, const Geo& g) {
-  static const bool generic = [] {
+  // MLA_ATTN_KERNEL=generic or =dsplit routes these shapes to another kernel (testing)
+  static const bool other = [] {
     const char* e = getenv("MLA_ATTN_KERNEL");
-    return e && strcmp(e, "generic") == 0;
+    return e && (strcmp(e, "generic") == 0 || strcmp(e, "dsplit") == 0);
   }();
-  if (generic || d.dtype != MLA_BF16 || d.d_c != 512 || d.d_r != 64) return false;
+  if (other || d.dtype != MLA_BF16 || d.d_c != 512 || d.d_r != 64) return false;
   return d.cache_fmt == MLA_CACHE_DENSE || (d.cache_fmt == MLA_CACHE_INT4 && g.capacity % 8 == 0);
 }
 
@@ -655,15 +561,19 @@ static int forced_splits() {
   return v;
 }
 
-static void plan(const Dims& d, const Geo& g, int batch, int n_rows, int* n_rb, int* tiles, int* ns,
-                 int* tps) {
-  *n_rb = (n_rows + MF_ROWS - 1) / MF_ROWS;
+void attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, int* n_rb, int* tiles,
+               int* ns, int* tps) {
+  *n_rb = (n_rows + rows_per_wg - 1) / rows_per_wg;
   *tiles = (g.capacity + MF_BN - 1) / MF_BN;
   *ns = forced_splits() > 0 ? min(forced_splits(), *tiles) : choose_splits(batch * *n_rb, *tiles, batch * n_rows, d.d_c);
   const int min_ns = (*tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // the class table holds MF_MAX_TPS tiles
   if (*ns < min_ns) *ns = min_ns;
   *tps = (*tiles + *ns - 1) / *ns;
   *ns = (*tiles + *tps - 1) / *tps;
+}
+
+static void plan(const Dims& d, const Geo& g, int batch, int n_rows, int* n_rb, int* tiles, int* ns, int* tps) {
+  attn_plan(d, g, batch, n_rows, MF_ROWS, n_rb, tiles, ns, tps);
 }
 
 size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows) {
@@ -694,8 +604,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStr
   kern<<<blocks, 256, shm, st>>>(ma);
   e = hipGetLastError();
   if (e != hipSuccess || ma.nsplit == 1) return e;
-  const size_t rows = (size_t)a.batch * a.n_rows;
-  attn_merge_kernel<DC><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(ma);
+  return launch_attn_merge(ma, st);
+}
+
+hipError_t launch_attn_merge(const MfmaArgs& ma, hipStream_t st) {
+  if (ma.a.d.d_c != 512) return hipErrorInvalidValue;
+  const size_t rows = (size_t)ma.a.batch * ma.a.n_rows;
+  attn_merge_kernel<512><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(ma);
   return hipGetLastError();
 }
 

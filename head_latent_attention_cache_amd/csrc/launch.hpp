@@ -45,5 +45,8 @@ hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t st);
 bool attn_mfma_supported(const Dims& d, const Geo& g);
 size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows);
 hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
+bool attn_dsplit_supported(const Dims& d);
+size_t attn_dsplit_workspace(const Dims& d, const Geo& g, int batch, int n_rows);
+hipError_t launch_attn_dsplit(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace mla

@@ -38,15 +38,24 @@ def _run(key, env_extra, out, tmp_path):
     return np.load(tmp_path / (out + ".npy"))
 
 
-@pytest.mark.parametrize("key", [2, 3, 5])
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
 def test_split_count_invariance(gpu_lib, key, tmp_path):
     outs = [_run(key, {"MLA_ATTN_SPLITS": str(ns)}, f"s{ns}", tmp_path) for ns in (1, 2, 3)]
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) <= 2e-2
 
 
-@pytest.mark.parametrize("key", [2, 3, 5])
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
 def test_mfma_matches_generic_kernel(gpu_lib, key, tmp_path):
     a = _run(key, {}, "mfma", tmp_path)
     g = _run(key, {"MLA_ATTN_KERNEL": "generic"}, "generic", tmp_path)
     assert np.max(np.abs(a - g)) <= 2e-2 + 1e-2 * np.max(np.abs(g))
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_split_row_kernel_on_narrow_rows(gpu_lib, key, tmp_path):
+    # the wide-row kernel (score contraction split over the waves) forced on
+    # d_r = 64 shapes: the child checks it against the oracle
+    d = _run(key, {"MLA_ATTN_KERNEL": "dsplit"}, "dsplit", tmp_path)
+    a = _run(key, {}, "mfma", tmp_path)
+    assert np.max(np.abs(a - d)) <= 2e-2 + 1e-2 * np.max(np.abs(a))
