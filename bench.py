@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+                    help="also run a plain 256 MiB device copy kernel (for HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -238,14 +238,18 @@ def main():
     }
 
     if args.copy_calibration:
-        n = 1 << 30
-        src_t = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        # a plain copy kernel of known size for scaling HBM byte counters:
+        # [131072, 1024] bf16 into the first 1024 columns of a [131072, 1152]
+        # array (an elementwise copy kernel; 256 MiB read, 256 MiB written)
+        rows = 131072
+        src_t = torch.ones((rows, 1024), dtype=torch.bfloat16, device=dev)
+        big = torch.empty((rows, 1152), dtype=torch.bfloat16, device=dev)
         for _ in range(3):
-            dst_t.copy_(src_t)
+            big[:, :1024] = src_t
         torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = n
-        del src_t, dst_t
+        out["copy_calibration"] = {"kernel": "elementwise copy, bf16 [131072, 1024] into a [131072, 1152] view",
+                                   "read_bytes": rows * 1024 * 2, "write_bytes": rows * 1024 * 2}
+        del src_t, big
 
     # ---- CPU oracle on a bounded sample ----
     if not args.no_cpu_baseline:

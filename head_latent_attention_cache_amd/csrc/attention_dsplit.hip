@@ -1,12 +1,13 @@
 // Latent attention on bf16 MFMA for wide cache rows: the score contraction
 // split over the waves of a work-group.
 //
-// VideoMLA page, The architecture: the long-horizon cache row is a 512-wide
-// content latent plus a 512-wide shared positional key, so the score of a
-// query against a cache row is a 1024-long dot product ("Multi-Head Latent
-// Attention" concept page, The RoPE problem, and the decoupled fix: one dot
-// product with the concatenated row), while the output still sums only the
-// 512-wide content latents.  A wave cannot keep a 1024-wide query block in
+// "VideoMLA: Compressing Video Diffusion Memory by 92.7% with Low-Rank Latent
+// Attention" (review), Core Mechanism: the long-horizon cache row is a
+// 512-wide content latent plus a 512-wide shared positional key, so the score
+// of a query against a cache row is a 1024-long dot product ("Multi-Head
+// Latent Attention" concept page, The RoPE problem, and the decoupled fix: one
+// dot product with the concatenated row), while the output still sums only
+// the 512-wide content latents.  A wave cannot keep a 1024-wide query block in
 // registers next to its output accumulators, so here the row is cut in four:
 //
 // Work-group: 4 waves, 64 rows (2 blocks of 32), 32-key tiles.

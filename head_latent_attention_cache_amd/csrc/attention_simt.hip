@@ -2,7 +2,7 @@
 //
 // "Multi-Head Latent Attention" concept page, Low-rank joint compression:
 // with W^UK absorbed into the query every head scores the shared cache row
-// directly ("attend directly in latent space"), and The RoPE problem, and the
+// directly, in latent space, and The RoPE problem, and the
 // decoupled fix: the score is the content term plus the rotary term, i.e. one
 // dot product with the concatenated row [c_kv | k_rope].  The value of a key is
 // its content latent c_kv (W^UV is applied after attention).

@@ -165,9 +165,10 @@ mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream
                         const void* w_uk, void* q_abs);
 
 /*
- * mla_attention: [MLA concept, Low-rank joint compression] ("attend directly in
- * latent space") and [The RoPE problem, and the decoupled fix] (score = content
- * term + rotary term); [MLA explainer, Decoupling RoPE] (concatenation).
+ * mla_attention: [MLA concept, Low-rank joint compression] (with both
+ * up-projections absorbed, decode-time attention runs on the latents
+ * themselves) and [The RoPE problem, and the decoupled fix] (score = content
+ * term + rotary term); [MLA explainer, Decoupling RoPE] (concatenated rows).
  * For every (b, t, h), over the slots s visible to frame q_first[b] + t / P:
  *     a_s = scale * q_abs[b, t, h] . cache_row[b, s]          (width d_c + d_r)
  *     o_lat[b, t, h] = sum_s softmax(a)_s * cache_row[b, s, 0 : d_c]
@@ -184,8 +185,8 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
                          void* o_lat, float* lse, void* workspace, size_t workspace_bytes);
 
 /*
- * mla_unabsorb_out: [MLA concept, Low-rank joint compression] ("the same trick
- * folds W^UV into the output projection"); [MLA explainer, On-the-Fly
+ * mla_unabsorb_out: [MLA concept, Low-rank joint compression] (W^UV is absorbed
+ * on the output side, as W^UK is on the query side); [MLA explainer, On-the-Fly
  * Reconstruction and Matrix Absorption].
  *     o_heads[b, t, h*d_v : (h+1)*d_v] = w_uv[h] . o_lat[b, t, h]
  *     y[b, t] = w_o . o_heads[b, t]

@@ -13,7 +13,7 @@ Parity status: every function is pinned by ``tests/test_oracle_*.py``
 (brute-force scalar loops, algebraic identities, rotary-embedding invariants,
 closed forms of softmax special cases, library cross-checks and planted
 mistakes).  The rotary pairing/frequency convention and the INT4 rounding
-conventions are readings, not facts printed by the pages; they bind both paths
-and are listed with the other readings in the design notes.
+conventions are readings, not facts printed by the pages: they bind both
+paths, and no value printed by the pages pins them (parity unpinned there).
 """
 from . import int4, mla  # noqa: F401

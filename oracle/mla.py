@@ -203,8 +203,8 @@ def absorb_query(cfg, q_nope, q_rope, w_uk, q_first: int) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # attention with materialised per-head keys/values (the plain definition):
-# [MLA concept, The RoPE problem, and the decoupled fix] query and key are the
-# concatenation of a content channel and the shared rotary channel;
+# [MLA concept, The RoPE problem, and the decoupled fix] each head's query and
+# key join a content part and the rotary part shared by all heads;
 # [MLA explainer, On-the-Fly Reconstruction] K and V are up-projections of c.
 # ---------------------------------------------------------------------------
 def softmax_scale(cfg) -> float:
