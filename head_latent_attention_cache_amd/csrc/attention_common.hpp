@@ -46,11 +46,24 @@ __device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint3
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
-// 16-byte chunk swizzle of a key row.  gfx950 LDS serves 16-byte reads with a
-// 128-byte bank period, so the 8 keys read by each 8-lane group must hit 8
-// different chunk positions: position = chunk ^ (key & 7).
-__device__ __forceinline__ int key_swizzle(int key) { return key & 7; }
+// 16-byte chunk swizzle of a key row: chunk c of key k sits at position
+// c ^ key_swizzle(k) of the row's 128 bytes.  gfx950 LDS has a 128-byte bank
+// period, so
+//  * the 16-byte key reads of the scores (8 consecutive keys per 8-lane
+//    phase, one chunk each) need 8 distinct swizzles over any 8 consecutive
+//    keys, and
+//  * the transposed 8-byte value reads (4 consecutive keys x 2 adjacent
+//    chunks {2i, 2i+1} per 16-lane phase) need distinct chunk pairs over any 4
+//    aligned consecutive keys, i.e. distinct key_swizzle(k) >> 1.
+// (k & 3) << 1 | (k >> 2 & 1) meets both.
+__device__ __forceinline__ int key_swizzle(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
 
+// Launch plan of an attention kernel: work-group (b, split, row block)
+// attends the split's key tiles; with nsplit > 1 it writes a normalised
+// partial output and LSE per row, merged afterwards in a fixed split order.
+// (Measured on the chunk workloads: a schedule of whole row blocks with a
+// stream-K tail ran slower than key splits, because work-groups at staggered
+// key offsets no longer share L2 lines.)
 struct MfmaArgs {
   AttnArgs a;
   int n_rb;          // row blocks per sequence
@@ -60,6 +73,34 @@ struct MfmaArgs {
   float* ws_o;       // [nsplit][B][n_rows][d_c] partial outputs (normalised), if nsplit > 1
   float* ws_lse;     // [nsplit][B][n_rows]
 };
+
+// one contiguous key range of one row block handled by a work-group; the
+// partial pointers address the row block's first row (null: final output)
+struct Piece {
+  int rbg;           // global row block: b * n_rb + rb
+  int t0, t1;        // key tiles [t0, t1)
+  float* part_o;
+  float* part_lse;
+};
+
+// the piece of linear work-group `lin`
+__device__ __forceinline__ Piece wg_piece(const MfmaArgs& ma, int lin, int rows_per_wg) {
+  const int B = ma.a.batch, n_rows = ma.a.n_rows, DC = ma.a.d.d_c;
+  const int per_b = ma.nsplit * ma.n_rb;
+  const int b = lin / per_b, split = (lin / ma.n_rb) % ma.nsplit, rb = lin % ma.n_rb;
+  Piece pc;
+  pc.rbg = b * ma.n_rb + rb;
+  pc.t0 = split * ma.tps;
+  pc.t1 = min(pc.t0 + ma.tps, ma.tiles);
+  pc.part_o = nullptr;
+  pc.part_lse = nullptr;
+  if (ma.nsplit > 1) {
+    const size_t row0 = ((size_t)split * B + b) * n_rows + (size_t)rb * rows_per_wg;
+    pc.part_o = ma.ws_o + row0 * DC;
+    pc.part_lse = ma.ws_lse + row0;
+  }
+  return pc;
+}
 
 // frame range [f_min, f_max] held by the slots of a tile (ring positions rp0..rp1)
 __device__ __forceinline__ void tile_frames(int rp0, int rp1, int newest, int nm, int W, int* fmin,
@@ -102,10 +143,13 @@ __device__ __forceinline__ int xcd_linear_block() {
   return xcd * per + min(xcd, rem) + (id >> 3);
 }
 
-// key-split plan of a launch: row blocks of `rows_per_wg`, MF_BN-key tiles,
-// `ns` splits of `tps` tiles each
-void attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, int* n_rb, int* tiles,
-               int* ns, int* tps);
+// launch plan (key-split fields of MfmaArgs) for row blocks of `rows_per_wg`
+// and MF_BN-key tiles; returns the number of work-groups
+int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma);
+// workspace bytes of a plan
+size_t attn_plan_workspace(const MfmaArgs& ma);
+// point the plan's partial buffers into the workspace
+void attn_plan_bind(MfmaArgs* ma, void* ws);
 // deterministic log-sum-exp merge of the splits' partial outputs
 hipError_t launch_attn_merge(const MfmaArgs& ma, hipStream_t st);
 

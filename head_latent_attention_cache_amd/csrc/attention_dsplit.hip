@@ -67,10 +67,9 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
 
   const int lin = xcd_linear_block();
-  const int per_b = ma.nsplit * ma.n_rb;
-  const int b = lin / per_b;
-  const int split = (lin / ma.n_rb) % ma.nsplit;
-  const int rb = lin % ma.n_rb;
+  const Piece pc = wg_piece(ma, lin, DS_ROWS);
+  const int b = pc.rbg / ma.n_rb;
+  const int rb = pc.rbg % ma.n_rb;
 
   const int newest = a.newest[b];
   int nm = newest % W;
@@ -81,8 +80,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int gfq_min = qf0 + (row0 / H) / P;
   const int gfq_max = qf0 + (min(row0 + DS_ROWS - 1, n_rows - 1) / H) / P;
 
-  const int t_begin = split * ma.tps;
-  const int ntl = min(t_begin + ma.tps, ma.tiles) - t_begin;
+  const int t_begin = pc.t0;
+  const int ntl = pc.t1 - pc.t0;
   for (int i = tid; i < ntl; i += 256)
     cls[i] = classify_tile((t_begin + i) * MF_BN, cap, P, newest, nm, W, fpb, gfq_min, gfq_max);
 
@@ -337,10 +336,10 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     if (g == 0) lrow[wave * 32 + lane] = l_tot;
     if (g == 0 && srow < n_rows) {
-      if (ma.nsplit == 1) {
+      if (!pc.part_o) {
         if (a.lse) a.lse[(size_t)b * n_rows + srow] = lse;
       } else {
-        ma.ws_lse[((size_t)split * a.batch + b) * n_rows + srow] = lse;
+        pc.part_lse[srow - row0] = lse;
       }
     }
   }
@@ -351,7 +350,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     if (orow >= n_rows) continue;
     const float lt = lrow[r * 32 + (lane & 31)];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (ma.nsplit == 1) {
+    if (!pc.part_o) {
       bf16_t* out = (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
@@ -365,7 +364,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
           *(u32x2_t*)(out + dim) = pk;
         }
     } else {
-      float* out = ma.ws_o + (((size_t)split * a.batch + b) * n_rows + orow) * DC + wave * WDIMS;
+      float* out = pc.part_o + (size_t)(orow - row0) * DC + wave * WDIMS;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -402,19 +401,20 @@ bool attn_dsplit_supported(const Dims& d) {
 }
 
 size_t attn_dsplit_workspace(const Dims& d, const Geo& g, int batch, int n_rows) {
-  int n_rb, tiles, ns, tps;
-  attn_plan(d, g, batch, n_rows, DS_ROWS, &n_rb, &tiles, &ns, &tps);
-  if (ns <= 1) return 0;
-  return (size_t)ns * batch * n_rows * (d.d_c + 1) * sizeof(float);
+  MfmaArgs ma;
+  ma.a.d = d;
+  ma.a.batch = batch;
+  ma.a.n_rows = n_rows;
+  attn_plan(d, g, batch, n_rows, DS_ROWS, &ma);
+  return attn_plan_workspace(ma);
 }
 
 template <int DC, int DR>
-static hipError_t launch_dsplit_shape(const MfmaArgs& ma, hipStream_t st) {
+static hipError_t launch_dsplit_shape(const MfmaArgs& ma, int blocks, hipStream_t st) {
   const size_t shm = attn_dsplit_lds_bytes<DC, DR>();
   auto kern = attn_dsplit_kernel<DC, DR>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  const int blocks = ma.a.batch * ma.nsplit * ma.n_rb;
   kern<<<blocks, 256, shm, st>>>(ma);
   return hipGetLastError();
 }
@@ -422,16 +422,12 @@ static hipError_t launch_dsplit_shape(const MfmaArgs& ma, hipStream_t st) {
 hipError_t launch_attn_dsplit(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   MfmaArgs ma;
   ma.a = a;
-  attn_plan(a.d, a.g, a.batch, a.n_rows, DS_ROWS, &ma.n_rb, &ma.tiles, &ma.nsplit, &ma.tps);
-  ma.ws_o = nullptr;
-  ma.ws_lse = nullptr;
-  if (ma.nsplit > 1) {
-    if (ws_bytes < attn_dsplit_workspace(a.d, a.g, a.batch, a.n_rows)) return hipErrorInvalidValue;
-    ma.ws_o = (float*)ws;
-    ma.ws_lse = ma.ws_o + (size_t)ma.nsplit * a.batch * a.n_rows * a.d.d_c;
-  }
-  hipError_t e = a.d.d_r == 512 ? launch_dsplit_shape<512, 512>(ma, st) : launch_dsplit_shape<512, 64>(ma, st);
-  if (e != hipSuccess || ma.nsplit == 1) return e;
+  const int blocks = attn_plan(a.d, a.g, a.batch, a.n_rows, DS_ROWS, &ma);
+  if (ws_bytes < attn_plan_workspace(ma)) return hipErrorInvalidValue;
+  attn_plan_bind(&ma, ws);
+  hipError_t e = a.d.d_r == 512 ? launch_dsplit_shape<512, 512>(ma, blocks, st)
+                                : launch_dsplit_shape<512, 64>(ma, blocks, st);
+  if (e != hipSuccess) return e;
   return launch_attn_merge(ma, st);
 }
 

@@ -91,10 +91,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
 
   const int lin = xcd_linear_block();
-  const int per_b = ma.nsplit * ma.n_rb;
-  const int b = lin / per_b;
-  const int split = (lin / ma.n_rb) % ma.nsplit;
-  const int rb = lin % ma.n_rb;
+  const Piece pc = wg_piece(ma, lin, MF_ROWS);
+  const int b = pc.rbg / ma.n_rb;
+  const int rb = pc.rbg % ma.n_rb;
 
   const int newest = a.newest[b];
   int nm = newest % W;
@@ -109,8 +108,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int gfq_min = qf0 + ((rb * MF_ROWS) / H) / P;
   const int gfq_max = qf0 + (min(rb * MF_ROWS + MF_ROWS - 1, n_rows - 1) / H) / P;
 
-  const int t_begin = split * ma.tps;
-  const int ntl = min(t_begin + ma.tps, ma.tiles) - t_begin;   // tiles of this split
+  const int t_begin = pc.t0;
+  const int ntl = pc.t1 - pc.t0;   // tiles of this piece
 
   // ---- classify every tile of the split once ----
   for (int i = tid; i < ntl; i += 256)
@@ -148,23 +147,30 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // (q * 4 + w) = 64-dim group q, keys 8w .. 8w+7, 8 swizzled chunks per key
   const int dma_key = (wave << 3) + (lane >> 3);
   const uint32_t dma_off = (uint32_t)(dma_key * DQK * 2 + (((lane & 7) ^ key_swizzle(dma_key)) << 4));
-  auto issue_loads = [&](int i, int buf) {
+  // Copy of key tile i into LDS buffer `buf`, described as a scalar source
+  // base, a per-lane byte offset and the LDS base; piece q (0..LOADS-1) moves
+  // one 64-dim group.  Past-the-end keys of the last tile read the last slot
+  // (zeroed later).  The pieces are issued between the score MFMAs of the
+  // current tile: each LDS-DMA instruction takes the wave a while to issue,
+  // and there it overlaps the matrix work.
+  struct DmaPlan { const uint8_t* tb; uint32_t voff, lds0; };
+  auto dma_plan = [&](int i, int buf) -> DmaPlan {
     const int k0 = (t_begin + i) * MF_BN;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * TILE_BYTES) + wave * 1024;
-    if (k0 + MF_BN <= cap) {
-      const uint8_t* tb = (const uint8_t*)(cache_b + (size_t)k0 * DQK);
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q)
-        dma16_sv(tb + q * 128, dma_off, lds0 + q * 4096);
-    } else {
-      // past-the-end keys of the last tile read the last slot (zeroed later)
-      const bf16_t* tb = cache_b + (size_t)k0 * DQK;
+    DmaPlan d;
+    d.tb = (const uint8_t*)(cache_b + (size_t)k0 * DQK);
+    d.lds0 = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * TILE_BYTES) + wave * 1024;
+    d.voff = dma_off;
+    if (k0 + MF_BN > cap) {
       const int key = min(dma_key, cap - 1 - k0);
-      const int chunk = (lane & 7) ^ key_swizzle(dma_key);
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q)
-        dma16(tb + key * DQK + q * 64 + chunk * 8, lds0 + q * 4096);
+      d.voff = (uint32_t)(key * DQK * 2 + (((lane & 7) ^ key_swizzle(dma_key)) << 4));
     }
+    return d;
+  };
+  auto dma_piece = [&](const DmaPlan& d, int q) { dma16_sv(d.tb + q * 128, d.voff, d.lds0 + q * 4096); };
+  auto issue_loads = [&](int i, int buf) {
+    const DmaPlan d = dma_plan(i, buf);
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) dma_piece(d, q);
   };
   // per-lane parts of the transposed value-read addresses.  For value dim
   // block d (0..3) and key step j (0..1) the read of keys key0 (key1 = key0 + 8)
@@ -176,87 +182,104 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int vhalf = (li & 1) * 8;
   const int vsw0 = key_swizzle(kq), vsw1 = key_swizzle(kq + 8);
   // O^T[wave's dims][all rows] += V^T . P^T for the tile in `vbuf` whose
-  // probabilities sit in P buffer `pb`; every LDS read is issued up front
-  auto output_product = [&](int vbuf, int pb) {
+  // probabilities sit in P buffer `pb`: fragments are read first (pv_read),
+  // the MFMAs issued later (pv_mfma), so that the softmax of the current tile
+  // can run between them
+  struct PVFrag {
+    bf16x8_t pfr[2][MF_WAVES];
+    i16x4_t v0[2][NDB], v1[2][NDB];
+  };
+  auto pv_read = [&](int vbuf, int pb, PVFrag& f) {
     const LDS_AS uint8_t* vt = (const LDS_AS uint8_t*)(smem + vbuf * TILE_BYTES) + (2 * wave) * MF_BN * 128;
     const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pb * MF_WAVES * 2 * 1024) + lane * 16;
-    bf16x8_t pfr[2][MF_WAVES];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < MF_WAVES; ++r)
-        pfr[j][r] = *(const LDS_AS bf16x8_t*)(pbase + (r * 2 + j) * 1024);
-    i16x4_t v0[2][NDB], v1[2][NDB];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
-        v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        f.v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS_AS i16x4_t*)(gbase + ((((d & 1) * 4 + cpart) ^ vsw0) << 4)));
-        v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        f.v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
       }
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < MF_WAVES; ++r)
+        f.pfr[j][r] = *(const LDS_AS bf16x8_t*)(pbase + (r * 2 + j) * 1024);
+  };
+  auto pv_mfma = [&](const PVFrag& f) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, v0[j][d]), h1 = __builtin_bit_cast(bf16x4_t, v1[j][d]);
+        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[j][d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[j][d]);
         bf16x8_t vf;
         vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
         vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
 #pragma unroll
         for (int r = 0; r < MF_WAVES; ++r)
-          o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[j][r], o[d * MF_WAVES + r], 0, 0, 0);
+          o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, f.pfr[j][r], o[d * MF_WAVES + r], 0, 0, 0);
       }
+  };
+  auto output_product = [&](int vbuf, int pb) {
+    PVFrag f;
+    pv_read(vbuf, pb, f);
+    pv_mfma(f);
   };
 
   // ---- scores of one tile, S^T = K . Q^T (one 32-key block, LDS reads KPF
-  // steps ahead), mask, probabilities against the row's reference maximum
-  // (log2 domain), published to P buffer `pbuf` ----
-  bool overflow = false;
-  auto scores_softmax = [&](const uint8_t* tile, int k0, int cl, int pbuf) {
+  // steps ahead) ----
+  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma) -> f32x16_t {
     f32x16_t s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
-    {
-      const int key = lane & 31;
-      const int sw = key_swizzle(key) ^ g;
-      const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(tile + key * 128);
-      auto kaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
-        return (const LDS_AS bf16x8_t*)(krow + (ks >> 2) * MF_BN * 128 + ((((ks & 3) << 1) ^ sw) << 4));
-      };
-      auto qaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
-        return (const LDS_AS bf16x8_t*)(qw + ((ks - NKS_REG) * 64 + lane) * 16);
-      };
-      constexpr int KPF = 4;
-      bf16x8_t kb[KPF], qb[KPF];
+    const int key = lane & 31;
+    const int sw = key_swizzle(key) ^ g;
+    const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(tile + key * 128);
+    auto kaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
+      return (const LDS_AS bf16x8_t*)(krow + (ks >> 2) * MF_BN * 128 + ((((ks & 3) << 1) ^ sw) << 4));
+    };
+    auto qaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
+      return (const LDS_AS bf16x8_t*)(qw + ((ks - NKS_REG) * 64 + lane) * 16);
+    };
+    constexpr int KPF = 4;
+    bf16x8_t kb[KPF], qb[KPF];
 #pragma unroll
-      for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
-      // scheduling barriers keep every read KPF MFMAs ahead of its use
+    for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
+    // scheduling barriers keep every read KPF MFMAs ahead of its use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8_t cur_k = kb[ks % KPF];
+      const bf16x8_t cur_q = ks < NKS_REG ? qf[ks < NKS_REG ? ks : 0] : qb[ks % KPF];
+      if (ks + KPF < NKS) {
+        kb[ks % KPF] = *kaddr(ks + KPF);
+        if (ks + KPF >= NKS_REG) qb[ks % KPF] = *qaddr(ks + KPF);
+      }
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, cur_q, s, 0, 0, 0);
+      // one piece of the next tile's copy every NKS / LOADS steps
+      if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8_t cur_k = kb[ks % KPF];
-        const bf16x8_t cur_q = ks < NKS_REG ? qf[ks < NKS_REG ? ks : 0] : qb[ks % KPF];
-        if (ks + KPF < NKS) {
-          kb[ks % KPF] = *kaddr(ks + KPF);
-          if (ks + KPF >= NKS_REG) qb[ks % KPF] = *qaddr(ks + KPF);
-        }
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, cur_q, s, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
-    if (cl != TILE_FULL) {
+    return s;
+  };
+  // branch-free (selects only), so the score registers stay put
+  auto mask_scores = [&](f32x16_t& s, int k0) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int sl = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
-        bool vis = sl < cap;
-        if (vis) vis = key_visible(fq, ring_frame(sl / P, newest, nm, W), W, fpb);
-        if (!vis) s[e] = -INFINITY;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int sl = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
+      const int slc = min(sl, cap - 1);
+      const bool vis = (sl < cap) & key_visible(fq, ring_frame(slc / P, newest, nm, W), W, fpb);
+      s[e] = vis ? s[e] : -INFINITY;
     }
+  };
+  // ---- probabilities against the row's reference maximum (log2 domain),
+  // published to P buffer `pbuf` in the B-fragment layout of the output
+  // product ----
+  bool overflow = false;
+  // row maximum of the tile (log2 units), reference update; returns -reference
+  auto softmax_max = [&](const f32x16_t& s) -> float {
     float mloc = s[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, s[e]);
@@ -264,7 +287,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
     m_seen = fmaxf(m_seen, mloc);
     if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
     else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    return m_run == -INFINITY ? 0.f : -m_run;
+  };
+  auto softmax_publish = [&](const f32x16_t& s, float neg_m, int pbuf) {
     float lsum = 0.f;
     LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + (pbuf * MF_WAVES + wave) * 2 * 1024);
 #pragma unroll
@@ -276,11 +301,39 @@ void attn_mfma_kernel(MfmaArgs ma) {
         lsum += p;
         pf[e] = (__bf16)p;
       }
-      // publish in the B-fragment layout of the output product
       *(LDS_AS bf16x8_t*)(pw + (j * 64 + lane) * 16) = pf;
     }
     l_run += lsum;
+  };
+  // one tile: scores, mask and row maximum, then the output product of the
+  // previous tile issued together with this tile's exponentials (independent
+  // work: the VALU runs while the MFMAs execute).  Before the first tile of a
+  // pass the "previous" probabilities are zeros (any finite tile serves as
+  // values).
+  auto tile_step = [&](const uint8_t* tile, int k0, int cl, int pbuf, int vprev, int pprev, const DmaPlan& dp,
+                       bool dma) {
+    f32x16_t s = qk_scores(tile, dp, dma);
+    if (cl != TILE_FULL) mask_scores(s, k0);
+    const float neg_m = softmax_max(s);
+    __builtin_amdgcn_sched_barrier(0);
+    PVFrag f;
+    pv_read(vprev, pprev, f);
+    pv_mfma(f);
+    softmax_publish(s, neg_m, pbuf);
+    // schedule: the fragment reads first, then the MFMAs with the softmax's
+    // VALU work between them
+    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NDB * MF_WAVES; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  // zero probabilities for the output product issued with a pass's first tile
+  auto zero_p = [&](int pbuf) {
+    for (int i = tid; i < MF_WAVES * 2 * 64; i += 256)
+      *(uint4*)(plds + pbuf * MF_WAVES * 2 * 1024 + i * 16) = make_uint4(0, 0, 0, 0);
   };
 
   // ---- packed INT4 tiles: the packed bytes and scales of a tile are copied
@@ -359,6 +412,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   if constexpr (!Q4) {
     int cur = next_tile(0);
     int bcur = 0, bprev = -1, pb = 0;
+    zero_p(1);
     if (cur < ntl) issue_loads(cur, 0);
     while (cur < ntl) {
       const int nxt = next_tile(cur + 1);
@@ -368,7 +422,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
       lds_barrier();
       // buffer of the next tile: the one holding neither this tile nor the previous one
       const int bnext = bprev < 0 ? (bcur + 1) % MF_NBUF : 3 - bcur - bprev;
-      if (nxt < ntl) issue_loads(nxt, bnext);
+      const DmaPlan dp = dma_plan(nxt < ntl ? nxt : cur, bnext);
       uint8_t* tile = smem + bcur * TILE_BYTES;
       const int k0 = (t_begin + cur) * MF_BN;
       const int cl = cls[cur];
@@ -386,10 +440,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
       }
-      // output product of the previous tile: its probabilities were published
-      // before this tile's barrier
-      if (bprev >= 0) output_product(bprev, pb ^ 1);
-      scores_softmax(tile, k0, cl, pb);
+      // the previous tile's probabilities were published before this barrier
+      tile_step(tile, k0, cl, pb, bprev >= 0 ? bprev : bcur, pb ^ 1, dp, nxt < ntl);
       bprev = bcur;
       bcur = bnext;
       pb ^= 1;
@@ -402,6 +454,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   } else {
     // tile sequence number `it` uses bf16 buffer it & 1 and staging it & 1
     int cur = next_tile(0), it = 0, pb = 0;
+    zero_p(1);
     if (cur < ntl) {
       stage_dma(cur, 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -415,8 +468,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
     while (cur < ntl) {
       const int bc = it & 1;
       const int nn = nxt < ntl ? next_tile(nxt + 1) : ntl;
-      if (it > 0) output_product(bc ^ 1, pb ^ 1);
-      scores_softmax(smem + bc * TILE_BYTES, (t_begin + cur) * MF_BN, cls[cur], pb);
+      tile_step(smem + bc * TILE_BYTES, (t_begin + cur) * MF_BN, cls[cur], pb, it > 0 ? (bc ^ 1) : bc, pb ^ 1,
+                DmaPlan{nullptr, 0u, 0u}, false);
       // the previous tile's buffer is free, the next tile's packed bytes
       // have landed, this tile's probabilities are published
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -442,10 +495,10 @@ void attn_mfma_kernel(MfmaArgs ma) {
   if (g == 0) lrow[wave * 32 + lane] = l_tot;
   __syncthreads();
   if (row_ok && g == 0) {
-    if (ma.nsplit == 1) {
+    if (!pc.part_o) {
       if (a.lse) a.lse[(size_t)b * n_rows + row] = lse;
     } else {
-      ma.ws_lse[((size_t)split * a.batch + b) * n_rows + row] = lse;
+      pc.part_lse[row - rb * MF_ROWS] = lse;
     }
   }
 #pragma unroll
@@ -454,7 +507,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     if (orow >= n_rows) continue;
     const float lt = lrow[r * 32 + (lane & 31)];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (ma.nsplit == 1) {
+    if (!pc.part_o) {
       bf16_t* out = (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
@@ -468,7 +521,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
           *(u32x2_t*)(out + dim) = pk;
         }
     } else {
-      float* out = ma.ws_o + (((size_t)split * a.batch + b) * n_rows + orow) * DC + wave * WDIMS;
+      float* out = pc.part_o + (size_t)(orow - rb * MF_ROWS) * DC + wave * WDIMS;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -531,16 +584,19 @@ bool attn_mfma_supported(const Dims& d, const Geo& g) {
   return d.cache_fmt == MLA_CACHE_DENSE || (d.cache_fmt == MLA_CACHE_INT4 && g.capacity % 8 == 0);
 }
 
-// number of key splits: balance whole rounds of work-groups over 256 CUs
+// number of key splits: balance whole rounds of work-groups over the CUs
 // against the cost of writing and merging fp32 partial outputs
 static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
+  const int G = 256;   // CUs of the chip (one work-group each)
   int best = 1;
   double best_cost = 1e30;
   for (int ns = 1; ns <= 64 && ns <= tiles; ++ns) {
     const int tps = (tiles + ns - 1) / ns;
     const long long wgs = (long long)units * ns;
-    const long long rounds = (wgs + 255) / 256;
-    // ~2.5 us per 64-key tile per work-group, +1 tile for the query load/epilogue
+    const long long rounds = (wgs + G - 1) / G;
+    // per 32-key tile per work-group, +1 tile for the query load/epilogue
+    // (a constant fitted to measured split sweeps: 8 splits for the decode
+    // batch, 3 for the video chunk)
     double cost = (double)rounds * (tps + 1) * 2.5e-6;
     if (ns > 1) cost += (double)ns * n_rows_total * d_c * 8.0 / 4.0e12;   // partial write + read
     if (cost < best_cost * 0.98) {
@@ -551,8 +607,8 @@ static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
   return best;
 }
 
-// MLA_ATTN_SPLITS=<n> fixes the number of key splits (testing: results must
-// not depend on it beyond rounding)
+// MLA_ATTN_SPLITS=<n> fixes the key-split schedule with n splits (testing:
+// results must not depend on it beyond rounding)
 static int forced_splits() {
   static int v = [] {
     const char* e = getenv("MLA_ATTN_SPLITS");
@@ -561,54 +617,65 @@ static int forced_splits() {
   return v;
 }
 
-void attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, int* n_rb, int* tiles,
-               int* ns, int* tps) {
-  *n_rb = (n_rows + rows_per_wg - 1) / rows_per_wg;
-  *tiles = (g.capacity + MF_BN - 1) / MF_BN;
-  *ns = forced_splits() > 0 ? min(forced_splits(), *tiles) : choose_splits(batch * *n_rb, *tiles, batch * n_rows, d.d_c);
-  const int min_ns = (*tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // the class table holds MF_MAX_TPS tiles
-  if (*ns < min_ns) *ns = min_ns;
-  *tps = (*tiles + *ns - 1) / *ns;
-  *ns = (*tiles + *tps - 1) / *tps;
+int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma) {
+  ma->n_rb = (n_rows + rows_per_wg - 1) / rows_per_wg;
+  ma->tiles = (g.capacity + MF_BN - 1) / MF_BN;
+  const int nr = batch * ma->n_rb;   // row blocks of the launch
+  int ns = forced_splits() > 0 ? min(forced_splits(), ma->tiles)
+                               : choose_splits(nr, ma->tiles, batch * n_rows, d.d_c);
+  const int min_ns = (ma->tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // a class table holds MF_MAX_TPS tiles
+  if (ns < min_ns) ns = min_ns;
+  ma->tps = (ma->tiles + ns - 1) / ns;
+  ma->nsplit = (ma->tiles + ma->tps - 1) / ma->tps;
+  return nr * ma->nsplit;
 }
 
-static void plan(const Dims& d, const Geo& g, int batch, int n_rows, int* n_rb, int* tiles, int* ns, int* tps) {
-  attn_plan(d, g, batch, n_rows, MF_ROWS, n_rb, tiles, ns, tps);
+size_t attn_plan_workspace(const MfmaArgs& ma) {
+  const int d_c = ma.a.d.d_c;
+  if (ma.nsplit > 1) return (size_t)ma.nsplit * ma.a.batch * ma.a.n_rows * (d_c + 1) * sizeof(float);
+  return 0;
+}
+
+void attn_plan_bind(MfmaArgs* ma, void* ws) {
+  ma->ws_o = nullptr;
+  ma->ws_lse = nullptr;
+  const int d_c = ma->a.d.d_c;
+  if (ma->nsplit > 1) {
+    ma->ws_o = (float*)ws;
+    ma->ws_lse = ma->ws_o + (size_t)ma->nsplit * ma->a.batch * ma->a.n_rows * d_c;
+  }
 }
 
 size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows) {
-  int n_rb, tiles, ns, tps;
-  plan(d, g, batch, n_rows, &n_rb, &tiles, &ns, &tps);
-  if (ns <= 1) return 0;
-  return (size_t)ns * batch * n_rows * (d.d_c + 1) * sizeof(float);
+  MfmaArgs ma;
+  ma.a.d = d;
+  ma.a.batch = batch;
+  ma.a.n_rows = n_rows;
+  attn_plan(d, g, batch, n_rows, MF_ROWS, &ma);
+  return attn_plan_workspace(ma);
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   MfmaArgs ma;
   ma.a = a;
-  plan(a.d, a.g, a.batch, a.n_rows, &ma.n_rb, &ma.tiles, &ma.nsplit, &ma.tps);
-  ma.ws_o = nullptr;
-  ma.ws_lse = nullptr;
-  if (ma.nsplit > 1) {
-    if (ws_bytes < attn_mfma_workspace(a.d, a.g, a.batch, a.n_rows)) return hipErrorInvalidValue;
-    ma.ws_o = (float*)ws;
-    ma.ws_lse = ma.ws_o + (size_t)ma.nsplit * a.batch * a.n_rows * a.d.d_c;
-  }
+  const int blocks = attn_plan(a.d, a.g, a.batch, a.n_rows, MF_ROWS, &ma);
+  if (ws_bytes < attn_plan_workspace(ma)) return hipErrorInvalidValue;
+  attn_plan_bind(&ma, ws);
   constexpr int DC = 512, DR = 64;
   const bool q4 = a.d.cache_fmt == MLA_CACHE_INT4;
   const size_t shm = q4 ? attn_mfma_lds_bytes<DC, DR, true>() : attn_mfma_lds_bytes<DC, DR, false>();
   auto kern = q4 ? attn_mfma_kernel<DC, DR, true> : attn_mfma_kernel<DC, DR, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  const int blocks = a.batch * ma.nsplit * ma.n_rb;
   kern<<<blocks, 256, shm, st>>>(ma);
   e = hipGetLastError();
-  if (e != hipSuccess || ma.nsplit == 1) return e;
+  if (e != hipSuccess) return e;
   return launch_attn_merge(ma, st);
 }
 
 hipError_t launch_attn_merge(const MfmaArgs& ma, hipStream_t st) {
   if (ma.a.d.d_c != 512) return hipErrorInvalidValue;
+  if (ma.nsplit <= 1) return hipSuccess;
   const size_t rows = (size_t)ma.a.batch * ma.a.n_rows;
   attn_merge_kernel<512><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(ma);
   return hipGetLastError();

@@ -59,3 +59,4 @@ def test_split_row_kernel_on_narrow_rows(gpu_lib, key, tmp_path):
     d = _run(key, {"MLA_ATTN_KERNEL": "dsplit"}, "dsplit", tmp_path)
     a = _run(key, {}, "mfma", tmp_path)
     assert np.max(np.abs(a - d)) <= 2e-2 + 1e-2 * np.max(np.abs(a))
+
