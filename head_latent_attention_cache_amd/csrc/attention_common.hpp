@@ -46,6 +46,20 @@ __device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint3
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
+// acc += A . B with v_mfma_f32_32x32x16_bf16, the accumulator in VGPRs (the
+// builtin lets the register allocator pick AGPRs).  A chain of these on one
+// accumulator needs no waits between steps (same-shape source-C forwarding);
+// mfma_vgpr_settle() must follow the last one before any other instruction
+// reads the accumulator.
+__device__ __forceinline__ void mfma_vgpr(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// wait states between an MFMA writing VGPRs and a VALU / memory read of them
+// (the 8-pass 32x32x16 MFMA needs fewer than the 32 given here)
+__device__ __forceinline__ void mfma_vgpr_settle(f32x16_t& acc) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc));
+}
+
 // 16-byte chunk swizzle of a key row: chunk c of key k sits at position
 // c ^ key_swizzle(k) of the row's 128 bytes.  gfx950 LDS has a 128-byte bank
 // period, so

@@ -189,9 +189,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
     bf16x8_t pfr[2][MF_WAVES];
     i16x4_t v0[2][NDB], v1[2][NDB];
   };
-  auto pv_read = [&](int vbuf, int pb, PVFrag& f) {
+  auto pv_read_v = [&](int vbuf, PVFrag& f) {
     const LDS_AS uint8_t* vt = (const LDS_AS uint8_t*)(smem + vbuf * TILE_BYTES) + (2 * wave) * MF_BN * 128;
-    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pb * MF_WAVES * 2 * 1024) + lane * 16;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -202,11 +201,18 @@ void attn_mfma_kernel(MfmaArgs ma) {
         f.v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
       }
+  };
+  auto pv_read_p = [&](int pb, PVFrag& f) {
+    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pb * MF_WAVES * 2 * 1024) + lane * 16;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < MF_WAVES; ++r)
         f.pfr[j][r] = *(const LDS_AS bf16x8_t*)(pbase + (r * 2 + j) * 1024);
+  };
+  auto pv_read = [&](int vbuf, int pb, PVFrag& f) {
+    pv_read_v(vbuf, f);
+    pv_read_p(pb, f);
   };
   auto pv_mfma = [&](const PVFrag& f) {
 #pragma unroll
@@ -231,6 +237,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // ---- scores of one tile, S^T = K . Q^T (one 32-key block, LDS reads KPF
   // steps ahead) ----
   auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma) -> f32x16_t {
+    // the score accumulator lives in VGPRs (mfma_vgpr): the 256 AGPRs hold
+    // the output accumulators, and an AGPR score block would be swapped with
+    // one of them every tile (copies that wait for the MFMA pipe to drain)
     f32x16_t s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -257,11 +266,12 @@ void attn_mfma_kernel(MfmaArgs ma) {
         kb[ks % KPF] = *kaddr(ks + KPF);
         if (ks + KPF >= NKS_REG) qb[ks % KPF] = *qaddr(ks + KPF);
       }
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, cur_q, s, 0, 0, 0);
+      mfma_vgpr(s, cur_k, cur_q);
       // one piece of the next tile's copy every NKS / LOADS steps
       if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
       __builtin_amdgcn_sched_barrier(0);
     }
+    mfma_vgpr_settle(s);
     return s;
   };
   // branch-free (selects only), so the score registers stay put
@@ -312,22 +322,45 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // values).
   auto tile_step = [&](const uint8_t* tile, int k0, int cl, int pbuf, int vprev, int pprev, const DmaPlan& dp,
                        bool dma) {
+    // the previous tile's value fragments (transposed reads, the slow ones)
+    // are read first: they land while the score MFMAs run
+    PVFrag f;
+    pv_read_v(vprev, f);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16_t s = qk_scores(tile, dp, dma);
     if (cl != TILE_FULL) mask_scores(s, k0);
+    pv_read_p(pprev, f);
     const float neg_m = softmax_max(s);
     __builtin_amdgcn_sched_barrier(0);
-    PVFrag f;
-    pv_read(vprev, pprev, f);
-    pv_mfma(f);
-    softmax_publish(s, neg_m, pbuf);
-    // schedule: the fragment reads first, then the MFMAs with the softmax's
-    // VALU work between them
-    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
+    // output MFMAs with one exponential after every other one: the VALU work
+    // runs while the matrix core is busy (scheduling barriers pin the order)
+    float p[16];
+    float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 2 * NDB * MF_WAVES; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      const int j = i / (NDB * MF_WAVES), d = (i / MF_WAVES) % NDB, r = i % MF_WAVES;
+      const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[j][d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[j][d]);
+      bf16x8_t vf;
+      vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
+      vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
+      o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, f.pfr[j][r], o[d * MF_WAVES + r], 0, 0, 0);
+      if ((i & 1) == 0 && i / 2 < 16) {
+        const int e = i / 2;
+        p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c_l2, neg_m));
+        lsum += p[e];
+        asm volatile("" ::"v"(p[e]), "v"(lsum));   // computed here, not sunk to its use
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + (pbuf * MF_WAVES + wave) * 2 * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8_t pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[j * 8 + e];
+      *(LDS_AS bf16x8_t*)(pw + (j * 64 + lane) * 16) = pf;
+    }
+    l_run += lsum;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   // zero probabilities for the output product issued with a pass's first tile

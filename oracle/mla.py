@@ -163,13 +163,21 @@ def store_rows(st, cfg, slots, rows):
     st["values"][:, slots] = stored
 
 
+def project_rows(cfg, x_rows, w_dkr, frames, toks) -> np.ndarray:
+    """Cache rows [c | k] (before storage rounding) of hidden states
+    ``x_rows [..., d_model]`` at (frame, token) positions ``frames``, ``toks``
+    (broadcast against the leading axes): c = h W_DKV, k = RoPE(h W_KR)."""
+    y = np.asarray(x_rows, np.float64) @ np.asarray(w_dkr, np.float64).T
+    c = y[..., :cfg.d_c]
+    k = rope_rotate(y[..., cfg.d_c:], token_coords(cfg, frames, toks), cfg)
+    return np.concatenate([c, k], axis=-1)
+
+
 def append_frame(st, cfg, x_frame, w_dkr, frame: int):
     """x_frame [B, P, d_model]; stores c = h W_DKV and k = RoPE(h W_KR)."""
     P = cfg.tokens_per_frame
-    y = np.asarray(x_frame, np.float64) @ np.asarray(w_dkr, np.float64).T
-    c = y[..., :cfg.d_c]
-    k = rope_rotate(y[..., cfg.d_c:], token_coords(cfg, frame, np.arange(P)), cfg)
-    store_rows(st, cfg, slot_index(cfg, frame, np.arange(P)), np.concatenate([c, k], axis=-1))
+    rows = project_rows(cfg, x_frame, w_dkr, frame, np.arange(P))
+    store_rows(st, cfg, slot_index(cfg, frame, np.arange(P)), rows)
     st["newest"] = max(st["newest"], frame)
 
 
@@ -237,13 +245,14 @@ def materialize_head(cfg, cache_values_b, w_uk, w_uv, h: int):
     return K, V
 
 
-def attend(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, q_first: int, tokens=None):
+def attend(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, q_first: int, tokens=None, heads=None):
     """Per-head attention over the cache with materialised K/V.
 
-    ``tokens``: optional list of (b, t) query tokens to evaluate (all heads);
-    default: every query token.  Returns o_heads [N, H, d_v], o_lat [N, H, d_c]
-    (= sum_s p_s c_s with the same probabilities) and lse [N, H], where N is
-    B * n_q in (b, t) order, or len(tokens).
+    ``tokens``: optional list of (b, t) query tokens to evaluate; default:
+    every query token.  ``heads``: optional list of heads to evaluate
+    (default all; the others stay zero).  Returns o_heads [N, H, d_v], o_lat
+    [N, H, d_c] (= sum_s p_s c_s with the same probabilities) and lse [N, H],
+    where N is B * n_q in (b, t) order, or len(tokens).
     """
     B, H = cfg.batch, cfg.n_heads
     w_uk = np.asarray(w_uk, np.float64)
@@ -261,7 +270,7 @@ def attend(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, q_first: int, tokens=None):
         ts = np.array([tokens[i][1] for i in idx])
         C = st["values"][b, :, :cfg.d_c]
         mask = mask_all[ts]
-        for h in range(H):
+        for h in (range(H) if heads is None else heads):
             K, V = materialize_head(cfg, st["values"][b], w_uk, w_uv, h)
             Q = np.concatenate([q_nope[b, ts, h], q_rope_rot[b, ts, h]], axis=-1)
             o, P, l = attention_core(Q, K, V, mask, softmax_scale(cfg))
