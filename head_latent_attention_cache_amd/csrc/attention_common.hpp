@@ -60,6 +60,18 @@ __device__ __forceinline__ void mfma_vgpr_settle(f32x16_t& acc) {
   asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc));
 }
 
+// max / sum of a value over the two 32-lane halves of a wave (lane l and
+// lane l ^ 32), with v_permlane32_swap (a VALU op; no LDS round trip): the
+// swap of x with itself yields, per lane, the pair {own, other} in some order
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 16-byte chunk swizzle of a key row: chunk c of key k sits at position
 // c ^ key_swizzle(k) of the row's 128 bytes.  gfx950 LDS has a 128-byte bank
 // period, so

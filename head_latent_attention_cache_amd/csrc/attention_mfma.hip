@@ -293,7 +293,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     float mloc = s[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, s[e]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * c_l2;
+    mloc = halves_max(mloc) * c_l2;
     m_seen = fmaxf(m_seen, mloc);
     if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
     else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
@@ -523,7 +523,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   }
 
   // ---- epilogue: row sums to every wave, then O / l ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halves_sum(l_run);
   const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   if (g == 0) lrow[wave * 32 + lane] = l_tot;
   __syncthreads();
