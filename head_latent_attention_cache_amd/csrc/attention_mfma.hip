@@ -112,24 +112,18 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int ntl = pc.t1 - pc.t0;   // tiles of this piece
 
   // ---- classify every tile of the split once ----
-  for (int i = tid; i < ntl; i += 256)
-    cls[i] = classify_tile((t_begin + i) * MF_BN, cap, P, newest, nm, W, fpb, gfq_min, gfq_max);
-
-  // ---- queries of this lane's row: B fragments of the score steps ----
-  const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (row_ok ? row : 0)) * DQK;
-  bf16x8_t qf[NKS_REG];
-  LDS_AS uint8_t* qw = (LDS_AS uint8_t*)(qlds + wave * NKS_LDS * 1024);
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    bf16x8_t v = *(const bf16x8_t*)(qrow + ks * 16 + g * 8);
-    if (!row_ok) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
-    }
-    if (ks < NKS_REG) qf[ks] = v;
-    else *(LDS_AS bf16x8_t*)(qw + ((ks - NKS_REG) * 64 + lane) * 16) = v;
+  bool not_full = false;
+  for (int i = tid; i < ntl; i += 256) {
+    const uint8_t c = classify_tile((t_begin + i) * MF_BN, cap, P, newest, nm, W, fpb, gfq_min, gfq_max);
+    cls[i] = c;
+    not_full |= c != TILE_FULL;
   }
-  __syncthreads();
+  // the first tile with a visible key (every thread finds the same one)
+  int first = 0;
+  while (first < ntl &&
+         classify_tile((t_begin + first) * MF_BN, cap, P, newest, nm, W, fpb, gfq_min, gfq_max) == TILE_SKIP)
+    ++first;
+
 
   // O^T blocks: [output-dim block of this wave][row block of the work-group]
   f32x16_t o[NDB * MF_WAVES];
@@ -172,6 +166,25 @@ void attn_mfma_kernel(MfmaArgs ma) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) dma_piece(d, q);
   };
+  // the first tile's copy is in flight while the queries load
+  if (!Q4 && first < ntl) issue_loads(first, 0);
+
+  // ---- queries of this lane's row: B fragments of the score steps ----
+  const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (row_ok ? row : 0)) * DQK;
+  bf16x8_t qf[NKS_REG];
+  LDS_AS uint8_t* qw = (LDS_AS uint8_t*)(qlds + wave * NKS_LDS * 1024);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    bf16x8_t v = *(const bf16x8_t*)(qrow + ks * 16 + g * 8);
+    if (!row_ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+    }
+    if (ks < NKS_REG) qf[ks] = v;
+    else *(LDS_AS bf16x8_t*)(qw + ((ks - NKS_REG) * 64 + lane) * 16) = v;
+  }
+  // every work-group tile is fully visible: no per-tile class lookups
+  const bool all_full = !__syncthreads_or(not_full);
   // per-lane parts of the transposed value-read addresses.  For value dim
   // block d (0..3) and key step j (0..1) the read of keys key0 (key1 = key0 + 8)
   // lands at: group (2 * wave + d / 2), key j * 16 + kq, 16-byte chunk
@@ -416,18 +429,20 @@ void attn_mfma_kernel(MfmaArgs ma) {
       const uint16_t sbits = c < DC / 8
           ? *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + key * (DC / 16) + (c >> 2) * 2)
           : *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + Q4_CS_BYTES + key * 2);
-      const float sc = __half2float(__ushort_as_half(sbits));
-      bool ok = true;
+      float sc = __half2float(__ushort_as_half(sbits));
       if (zero_check) {
+        // never-written slots hold arbitrary bytes: a zero scale gives zeros
         const int sl = k0 + key;
-        ok = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0;
+        sc = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0 ? sc : 0.f;
       }
       bf16x8_t v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // element e = nibble e of the little-endian word (low nibble first), sign-extended
-        const int q = ((int)(codes << (28 - 4 * e))) >> 28;
-        v[e] = __builtin_bit_cast(__bf16, ok ? f32_to_bf16((float)q * sc) : (bf16_t)0);
+        // element e = nibble e of the little-endian word (low nibble first),
+        // sign-extended; q * s is exact in fp32 (4 x 11 significant bits) and
+        // rounds once to bf16 (nearest even, v_cvt_pk_bf16_f32)
+        const int q = __builtin_amdgcn_sbfe((int)codes, 4 * e, 4);
+        v[e] = (__bf16)((float)q * sc);
       }
       *(LDS_AS bf16x8_t*)(tp + ((c >> 3) * MF_BN + key) * 128 + (((c & 7) ^ key_swizzle(key)) << 4)) = v;
     }
@@ -443,12 +458,12 @@ void attn_mfma_kernel(MfmaArgs ma) {
   overflow = false;
 
   if constexpr (!Q4) {
-    int cur = next_tile(0);
+    int cur = first;
     int bcur = 0, bprev = -1, pb = 0;
     zero_p(1);
-    if (cur < ntl) issue_loads(cur, 0);
+    if (pass > 0 && cur < ntl) issue_loads(cur, 0);
     while (cur < ntl) {
-      const int nxt = next_tile(cur + 1);
+      const int nxt = all_full ? cur + 1 : next_tile(cur + 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       // one barrier per tile: this tile is in LDS, the previous tile's
       // probabilities are published, and the buffer two tiles back is free
@@ -458,7 +473,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
       const DmaPlan dp = dma_plan(nxt < ntl ? nxt : cur, bnext);
       uint8_t* tile = smem + bcur * TILE_BYTES;
       const int k0 = (t_begin + cur) * MF_BN;
-      const int cl = cls[cur];
+      const int cl = all_full ? (int)TILE_FULL : (int)cls[cur];
       if (cl == TILE_MASKED_ZERO) {
         // zero never-written (or past-the-end) keys of this tile
         for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
