@@ -393,9 +393,20 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const uint8_t* q4_codes = (const uint8_t*)a.cache + (size_t)b * cap * (DQK / 2);
   const uint8_t* q4_cs = (const uint8_t*)a.aux + (size_t)b * cap * (DC / 16);
   const uint8_t* q4_rs = (const uint8_t*)a.aux + (size_t)a.batch * cap * (DC / 16) + (size_t)b * cap * 2;
+  static_assert(Q4_CODE_CH == 576 && Q4_CS_CH == 64 && Q4_RS_CH == 4, "staging chunk counts");
   auto stage_dma = [&](int t, int sidx) {
     const int k0 = (t_begin + t) * MF_BN;
     const uint32_t lds_stage = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
+    if (k0 + MF_BN <= cap) {
+      // whole tile: each plane is one contiguous run; chunk j lands at 16 j
+      const uint8_t* cb = q4_codes + (size_t)k0 * (DQK / 2);
+      dma16_sv(cb, (uint32_t)tid * 16, lds_stage + wave * 1024);                  // chunks 0 .. 255
+      dma16_sv(cb, 4096u + (uint32_t)tid * 16, lds_stage + 4096 + wave * 1024);   // 256 .. 511
+      if (wave == 0) dma16_sv(cb, 8192u + (uint32_t)lane * 16, lds_stage + 8192);  // codes 512 .. 575
+      if (wave == 1) dma16_sv(q4_cs + (size_t)k0 * (DC / 16), (uint32_t)lane * 16, lds_stage + 576 * 16);
+      if (wave == 2 && lane < Q4_RS_CH) dma16_sv(q4_rs + (size_t)k0 * 2, (uint32_t)lane * 16, lds_stage + 640 * 16);
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < (Q4_CH + 255) / 256; ++r) {
       if (r * 256 + wave * 64 >= Q4_CH) break;   // wave-uniform
@@ -415,26 +426,30 @@ void attn_mfma_kernel(MfmaArgs ma) {
       if (j < Q4_CH) dma16(src, lds_stage + (r * 256 + wave * 64) * 16);
     }
   };
+  // dequantisation of a staged tile into the bf16 tile layout: thread tid
+  // converts key tid / 8, 16-byte output chunks c = tid % 8 + 8 i (i = 0 .. 8,
+  // i.e. 64-dim group i), so every LDS address is a per-thread base plus a
+  // constant offset; the rotary group (last) uses the per-token scale
+  static_assert(MF_BN * 8 == 256 && DQK == 8 * 72 && DC == 512, "one key per 8 threads, 9 groups");
+  const int dq_key = tid >> 3, dq_cb = tid & 7;
   auto dequant = [&](int t, int sidx, int tbuf) {
-    const int k0 = (t_begin + t) * MF_BN;
-    const bool zero_check = cls[t] == TILE_MASKED_ZERO;
     const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
-    LDS_AS uint8_t* tp = (LDS_AS uint8_t*)(smem + tbuf * TILE_BYTES);
-    constexpr int CPK = DQK / 8;   // 16-byte bf16 chunks per key
+    const LDS_AS uint8_t* cp = sp + dq_key * (DQK / 2) + dq_cb * 4;                    // + 32 i
+    const LDS_AS uint8_t* scp = sp + Q4_CODE_BYTES + dq_key * (DC / 16) + (dq_cb >> 2) * 2;  // + 4 i
+    LDS_AS uint8_t* tp = (LDS_AS uint8_t*)(smem + tbuf * TILE_BYTES) + dq_key * 128 +
+                         ((dq_cb ^ key_swizzle(dq_key)) << 4);                             // + 4096 i
+    float keep = 1.f;
+    if (cls[t] == TILE_MASKED_ZERO) {
+      // never-written slots hold arbitrary bytes: a zero scale gives zeros
+      const int sl = (t_begin + t) * MF_BN + dq_key;
+      keep = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0 ? 1.f : 0.f;
+    }
 #pragma unroll 3
-    for (int i = 0; i < MF_BN * CPK / 256; ++i) {
-      const int L = i * 256 + tid;
-      const int key = L / CPK, c = L % CPK;
-      const uint32_t codes = *(const LDS_AS uint32_t*)(sp + key * (DQK / 2) + c * 4);
-      const uint16_t sbits = c < DC / 8
-          ? *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + key * (DC / 16) + (c >> 2) * 2)
-          : *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + Q4_CS_BYTES + key * 2);
-      float sc = __half2float(__ushort_as_half(sbits));
-      if (zero_check) {
-        // never-written slots hold arbitrary bytes: a zero scale gives zeros
-        const int sl = k0 + key;
-        sc = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0 ? sc : 0.f;
-      }
+    for (int i = 0; i < NCG; ++i) {
+      const uint32_t codes = *(const LDS_AS uint32_t*)(cp + 32 * i);
+      const uint16_t sbits = i < DC / 64 ? *(const LDS_AS uint16_t*)(scp + 4 * i)
+                                         : *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + Q4_CS_BYTES + dq_key * 2);
+      const float sc = keep != 0.f ? __half2float(__ushort_as_half(sbits)) : 0.f;
       bf16x8_t v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -444,7 +459,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
         const int q = __builtin_amdgcn_sbfe((int)codes, 4 * e, 4);
         v[e] = (__bf16)((float)q * sc);
       }
-      *(LDS_AS bf16x8_t*)(tp + ((c >> 3) * MF_BN + key) * 128 + (((c & 7) ^ key_swizzle(key)) << 4)) = v;
+      *(LDS_AS bf16x8_t*)(tp + i * MF_BN * 128) = v;
     }
   };
 
