@@ -54,10 +54,15 @@ __device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint3
 __device__ __forceinline__ void mfma_vgpr(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-// wait states between an MFMA writing VGPRs and a VALU / memory read of them
-// (the 8-pass 32x32x16 MFMA needs fewer than the 32 given here)
+// first step of a chain: acc = A . B (the accumulator operand is the inline
+// constant 0, so acc needs no zeroing; early-clobber keeps it off A and B)
+__device__ __forceinline__ void mfma_vgpr_zero(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+// wait states between an MFMA writing VGPRs and a VALU / memory read of them:
+// the 8-pass 32x32x16 MFMA needs about a dozen, 20 are given here
 __device__ __forceinline__ void mfma_vgpr_settle(f32x16_t& acc) {
-  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(acc));
+  asm volatile("s_nop 15\n\ts_nop 3" : "+v"(acc));
 }
 
 // max / sum of a value over the two 32-lane halves of a wave (lane l and

@@ -202,18 +202,20 @@ void attn_mfma_kernel(MfmaArgs ma) {
     bf16x8_t pfr[2][MF_WAVES];
     i16x4_t v0[2][NDB], v1[2][NDB];
   };
-  auto pv_read_v = [&](int vbuf, PVFrag& f) {
+  // value fragments of key step j, output-dim block d
+  auto pv_read_v1 = [&](int vbuf, PVFrag& f, int j, int d) {
     const LDS_AS uint8_t* vt = (const LDS_AS uint8_t*)(smem + vbuf * TILE_BYTES) + (2 * wave) * MF_BN * 128;
+    const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
+    f.v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS i16x4_t*)(gbase + ((((d & 1) * 4 + cpart) ^ vsw0) << 4)));
+    f.v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
+  };
+  auto pv_read_v = [&](int vbuf, PVFrag& f) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
-        f.v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)(gbase + ((((d & 1) * 4 + cpart) ^ vsw0) << 4)));
-        f.v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
-      }
+      for (int d = 0; d < NDB; ++d) pv_read_v1(vbuf, f, j, d);
   };
   auto pv_read_p = [&](int pb, PVFrag& f) {
     const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pb * MF_WAVES * 2 * 1024) + lane * 16;
@@ -248,14 +250,14 @@ void attn_mfma_kernel(MfmaArgs ma) {
   };
 
   // ---- scores of one tile, S^T = K . Q^T (one 32-key block, LDS reads KPF
-  // steps ahead) ----
-  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma) -> f32x16_t {
+  // steps ahead).  The previous tile's value fragments (buffer vprev) are
+  // read two per step over the first steps: they land while the chain runs
+  // and do not hold up its first MFMA ----
+  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma, PVFrag& f, int vprev) -> f32x16_t {
     // the score accumulator lives in VGPRs (mfma_vgpr): the 256 AGPRs hold
     // the output accumulators, and an AGPR score block would be swapped with
     // one of them every tile (copies that wait for the MFMA pipe to drain)
     f32x16_t s;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.f;
     const int key = lane & 31;
     const int sw = key_swizzle(key) ^ g;
     const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(tile + key * 128);
@@ -279,9 +281,11 @@ void attn_mfma_kernel(MfmaArgs ma) {
         kb[ks % KPF] = *kaddr(ks + KPF);
         if (ks + KPF >= NKS_REG) qb[ks % KPF] = *qaddr(ks + KPF);
       }
-      mfma_vgpr(s, cur_k, cur_q);
+      if (ks == 0) mfma_vgpr_zero(s, cur_k, cur_q);
+      else mfma_vgpr(s, cur_k, cur_q);
       // one piece of the next tile's copy every NKS / LOADS steps
       if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
+      if (ks >= 1 && ks <= 2 * NDB) pv_read_v1(vprev, f, (ks - 1) / NDB, (ks - 1) % NDB);
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_vgpr_settle(s);
@@ -335,12 +339,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // values).
   auto tile_step = [&](const uint8_t* tile, int k0, int cl, int pbuf, int vprev, int pprev, const DmaPlan& dp,
                        bool dma) {
-    // the previous tile's value fragments (transposed reads, the slow ones)
-    // are read first: they land while the score MFMAs run
     PVFrag f;
-    pv_read_v(vprev, f);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16_t s = qk_scores(tile, dp, dma);
+    f32x16_t s = qk_scores(tile, dp, dma, f, vprev);
     if (cl != TILE_FULL) mask_scores(s, k0);
     pv_read_p(pprev, f);
     const float neg_m = softmax_max(s);
