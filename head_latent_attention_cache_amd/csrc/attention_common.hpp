@@ -91,7 +91,8 @@ __device__ __forceinline__ int key_swizzle(int key) { return ((key & 3) << 1) | 
 
 // Launch plan of an attention kernel: work-group (b, split, row block)
 // attends the split's key tiles; with nsplit > 1 it writes a normalised
-// partial output and LSE per row, merged afterwards in a fixed split order.
+// partial output (bf16, the output precision) and an fp32 LSE per row,
+// merged afterwards in a fixed split order with fp32 weights.
 // (Measured on the chunk workloads: a schedule of whole row blocks with a
 // stream-K tail ran slower than key splits, because work-groups at staggered
 // key offsets no longer share L2 lines.)
@@ -101,7 +102,7 @@ struct MfmaArgs {
   int nsplit;        // key splits
   int tiles;         // key tiles per sequence
   int tps;           // tiles per split
-  float* ws_o;       // [nsplit][B][n_rows][d_c] partial outputs (normalised), if nsplit > 1
+  bf16_t* ws_o;      // [nsplit][B][n_rows][d_c] partial outputs (normalised, bf16), if nsplit > 1
   float* ws_lse;     // [nsplit][B][n_rows]
 };
 
@@ -110,7 +111,7 @@ struct MfmaArgs {
 struct Piece {
   int rbg;           // global row block: b * n_rb + rb
   int t0, t1;        // key tiles [t0, t1)
-  float* part_o;
+  bf16_t* part_o;
   float* part_lse;
 };
 

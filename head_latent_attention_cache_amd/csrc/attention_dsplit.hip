@@ -350,31 +350,20 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     if (orow >= n_rows) continue;
     const float lt = lrow[r * 32 + (lane & 31)];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (!pc.part_o) {
-      bf16_t* out = (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
+    // final output, or this split's partial output (same bf16 row layout)
+    bf16_t* out = pc.part_o ? pc.part_o + (size_t)(orow - row0) * DC + wave * WDIMS
+                            : (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int dim = d * 32 + 8 * q + 4 * g;
-          const f32x16_t& ob = o[d * 2 + r];
-          u32x2_t pk;
-          pk[0] = (uint32_t)f32_to_bf16(ob[4 * q] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 1] * inv) << 16);
-          pk[1] = (uint32_t)f32_to_bf16(ob[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 3] * inv) << 16);
-          *(u32x2_t*)(out + dim) = pk;
-        }
-    } else {
-      float* out = pc.part_o + (size_t)(orow - row0) * DC + wave * WDIMS;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int dim = d * 32 + 8 * q + 4 * g;
-          const f32x16_t& ob = o[d * 2 + r];
-          *(float4*)(out + dim) = make_float4(ob[4 * q] * inv, ob[4 * q + 1] * inv, ob[4 * q + 2] * inv,
-                                              ob[4 * q + 3] * inv);
-        }
-    }
+      for (int q = 0; q < 4; ++q) {
+        const int dim = d * 32 + 8 * q + 4 * g;
+        const f32x16_t& ob = o[d * 2 + r];
+        u32x2_t pk;
+        pk[0] = (uint32_t)f32_to_bf16(ob[4 * q] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 1] * inv) << 16);
+        pk[1] = (uint32_t)f32_to_bf16(ob[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 3] * inv) << 16);
+        *(u32x2_t*)(out + dim) = pk;
+      }
   }
 }
 

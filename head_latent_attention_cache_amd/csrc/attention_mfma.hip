@@ -570,38 +570,28 @@ void attn_mfma_kernel(MfmaArgs ma) {
     if (orow >= n_rows) continue;
     const float lt = lrow[r * 32 + (lane & 31)];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (!pc.part_o) {
-      bf16_t* out = (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
+    // final output, or this split's partial output (same bf16 row layout)
+    bf16_t* out = pc.part_o ? pc.part_o + (size_t)(orow - rb * MF_ROWS) * DC + wave * WDIMS
+                            : (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int dim = d * 32 + 8 * q + 4 * g;
-          const f32x16_t& ob = o[d * MF_WAVES + r];
-          u32x2_t pk;
-          pk[0] = (uint32_t)f32_to_bf16(ob[4 * q] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 1] * inv) << 16);
-          pk[1] = (uint32_t)f32_to_bf16(ob[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 3] * inv) << 16);
-          *(u32x2_t*)(out + dim) = pk;
-        }
-    } else {
-      float* out = pc.part_o + (size_t)(orow - rb * MF_ROWS) * DC + wave * WDIMS;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int dim = d * 32 + 8 * q + 4 * g;
-          const f32x16_t& ob = o[d * MF_WAVES + r];
-          *(float4*)(out + dim) = make_float4(ob[4 * q] * inv, ob[4 * q + 1] * inv, ob[4 * q + 2] * inv,
-                                              ob[4 * q + 3] * inv);
-        }
-    }
+      for (int q = 0; q < 4; ++q) {
+        const int dim = d * 32 + 8 * q + 4 * g;
+        const f32x16_t& ob = o[d * MF_WAVES + r];
+        u32x2_t pk;
+        pk[0] = (uint32_t)f32_to_bf16(ob[4 * q] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 1] * inv) << 16);
+        pk[1] = (uint32_t)f32_to_bf16(ob[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 3] * inv) << 16);
+        *(u32x2_t*)(out + dim) = pk;
+      }
   }
 }
 
 // merge of the key splits: o = sum_i w_i o_i / sum_i w_i, w_i = exp(lse_i - max)
-// one wave per row; fixed split order (deterministic)
+// one wave per row, 8 consecutive dims per lane; fixed split order (deterministic)
 template <int DC>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
+  static_assert(DC == 64 * 8, "8 dims per lane");
   const AttnArgs& a = ma.a;
   const int lane = threadIdx.x & 63;
   const size_t rows = (size_t)a.batch * a.n_rows;
@@ -609,9 +599,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
   if (r >= rows) return;
   float mx = -INFINITY;
   for (int sp = 0; sp < ma.nsplit; ++sp) mx = fmaxf(mx, ma.ws_lse[(size_t)sp * rows + r]);
-  float acc[DC / 64];
+  float acc[8];
 #pragma unroll
-  for (int u = 0; u < DC / 64; ++u) acc[u] = 0.f;
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
   float wsum = 0.f;
   if (mx != -INFINITY) {
     for (int sp = 0; sp < ma.nsplit; ++sp) {
@@ -619,16 +609,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
       const float w = expf(l - mx);
       wsum += w;
       if (w > 0.f) {
-        const float* src = ma.ws_o + ((size_t)sp * rows + r) * DC;
+        const uint4 v = *(const uint4*)(ma.ws_o + ((size_t)sp * rows + r) * DC + lane * 8);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int u = 0; u < DC / 64; ++u) acc[u] = fmaf(w, src[lane + 64 * u], acc[u]);
+        for (int u = 0; u < 4; ++u) {
+          acc[2 * u] = fmaf(w, bf16_to_f32((bf16_t)(wd[u] & 0xffffu)), acc[2 * u]);
+          acc[2 * u + 1] = fmaf(w, bf16_to_f32((bf16_t)(wd[u] >> 16)), acc[2 * u + 1]);
+        }
       }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  bf16_t* out = (bf16_t*)a.o_lat + r * DC;
+  uint32_t pk[4];
 #pragma unroll
-  for (int u = 0; u < DC / 64; ++u) out[lane + 64 * u] = f32_to_bf16(acc[u] * inv);
+  for (int u = 0; u < 4; ++u)
+    pk[u] = (uint32_t)f32_to_bf16(acc[2 * u] * inv) | ((uint32_t)f32_to_bf16(acc[2 * u + 1] * inv) << 16);
+  *(uint4*)((bf16_t*)a.o_lat + r * DC + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   if (a.lse && lane == 0) a.lse[r] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
@@ -648,7 +644,7 @@ bool attn_mfma_supported(const Dims& d, const Geo& g) {
 }
 
 // number of key splits: balance whole rounds of work-groups over the CUs
-// against the cost of writing and merging fp32 partial outputs
+// against the cost of writing and merging bf16 partial outputs
 static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
   const int G = 256;   // CUs of the chip (one work-group each)
   int best = 1;
@@ -661,7 +657,7 @@ static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
     // (a constant fitted to measured split sweeps: 8 splits for the decode
     // batch, 3 for the video chunk)
     double cost = (double)rounds * (tps + 1) * 2.5e-6;
-    if (ns > 1) cost += (double)ns * n_rows_total * d_c * 8.0 / 4.0e12;   // partial write + read
+    if (ns > 1) cost += (double)ns * n_rows_total * d_c * 4.0 / 4.0e12;   // partial write + read
     if (cost < best_cost * 0.98) {
       best_cost = cost;
       best = ns;
@@ -695,7 +691,7 @@ int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_w
 
 size_t attn_plan_workspace(const MfmaArgs& ma) {
   const int d_c = ma.a.d.d_c;
-  if (ma.nsplit > 1) return (size_t)ma.nsplit * ma.a.batch * ma.a.n_rows * (d_c + 1) * sizeof(float);
+  if (ma.nsplit > 1) return (size_t)ma.nsplit * ma.a.batch * ma.a.n_rows * (d_c * sizeof(bf16_t) + sizeof(float));
   return 0;
 }
 
@@ -704,8 +700,8 @@ void attn_plan_bind(MfmaArgs* ma, void* ws) {
   ma->ws_lse = nullptr;
   const int d_c = ma->a.d.d_c;
   if (ma->nsplit > 1) {
-    ma->ws_o = (float*)ws;
-    ma->ws_lse = ma->ws_o + (size_t)ma->nsplit * ma->a.batch * ma->a.n_rows * d_c;
+    ma->ws_o = (bf16_t*)ws;
+    ma->ws_lse = (float*)(ma->ws_o + (size_t)ma->nsplit * ma->a.batch * ma->a.n_rows * d_c);
   }
 }
 
