@@ -249,11 +249,104 @@ void attn_mfma_kernel(MfmaArgs ma) {
     pv_mfma(f);
   };
 
+  // ---- packed INT4 tiles: the packed bytes and scales of a tile are copied
+  // into a staging buffer (global_load_lds), then dequantised into the bf16
+  // tile layout.  Requires capacity % 8 == 0 (16-byte aligned scale rows).
+  constexpr int Q4_CODE_CH = MF_BN * DQK / 32;          // 16-byte chunks of codes
+  constexpr int Q4_CS_CH = MF_BN * DC / 256;            // of content scales
+  constexpr int Q4_RS_CH = MF_BN * 2 / 16;              // of rotary scales
+  constexpr int Q4_CH = Q4_CODE_CH + Q4_CS_CH + Q4_RS_CH;
+  constexpr int Q4_CODE_BYTES = MF_BN * DQK / 2, Q4_CS_BYTES = MF_BN * DC / 16;
+  const uint8_t* q4_codes = (const uint8_t*)a.cache + (size_t)b * cap * (DQK / 2);
+  const uint8_t* q4_cs = (const uint8_t*)a.aux + (size_t)b * cap * (DC / 16);
+  const uint8_t* q4_rs = (const uint8_t*)a.aux + (size_t)a.batch * cap * (DC / 16) + (size_t)b * cap * 2;
+  static_assert(Q4_CODE_CH == 576 && Q4_CS_CH == 64 && Q4_RS_CH == 4, "staging chunk counts");
+  auto stage_dma = [&](int t, int sidx) {
+    const int k0 = (t_begin + t) * MF_BN;
+    const uint32_t lds_stage = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
+    if (k0 + MF_BN <= cap) {
+      // whole tile: each plane is one contiguous run; chunk j lands at 16 j
+      const uint8_t* cb = q4_codes + (size_t)k0 * (DQK / 2);
+      dma16_sv(cb, (uint32_t)tid * 16, lds_stage + wave * 1024);                  // chunks 0 .. 255
+      dma16_sv(cb, 4096u + (uint32_t)tid * 16, lds_stage + 4096 + wave * 1024);   // 256 .. 511
+      if (wave == 0) dma16_sv(cb, 8192u + (uint32_t)lane * 16, lds_stage + 8192);  // codes 512 .. 575
+      if (wave == 1) dma16_sv(q4_cs + (size_t)k0 * (DC / 16), (uint32_t)lane * 16, lds_stage + 576 * 16);
+      if (wave == 2 && lane < Q4_RS_CH) dma16_sv(q4_rs + (size_t)k0 * 2, (uint32_t)lane * 16, lds_stage + 640 * 16);
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < (Q4_CH + 255) / 256; ++r) {
+      if (r * 256 + wave * 64 >= Q4_CH) break;   // wave-uniform
+      const int j = r * 256 + wave * 64 + lane;
+      const uint8_t* src;
+      if (j < Q4_CODE_CH) {
+        const int key = j / (DQK / 32), off = j % (DQK / 32);
+        src = q4_codes + (size_t)min(k0 + key, cap - 1) * (DQK / 2) + off * 16;
+      } else if (j < Q4_CODE_CH + Q4_CS_CH) {
+        const int jj = j - Q4_CODE_CH, key = jj / (DC / 256);
+        src = q4_cs + (size_t)min(k0 + key, cap - 1) * (DC / 16) + (jj % (DC / 256)) * 16;
+      } else {
+        // 8 keys per chunk; past-the-end chunks re-read the last 8 keys
+        const int jj = min(j - Q4_CODE_CH - Q4_CS_CH, Q4_RS_CH - 1);
+        src = q4_rs + (size_t)min(k0 + 8 * jj, cap - 8) * 2;
+      }
+      if (j < Q4_CH) dma16(src, lds_stage + (r * 256 + wave * 64) * 16);
+    }
+  };
+  // dequantisation of a staged tile into the bf16 tile layout: thread tid
+  // converts key tid / 8, 16-byte output chunks c = tid % 8 + 8 i (i = 0 .. 8,
+  // i.e. 64-dim group i), so every LDS address is a per-thread base plus a
+  // constant offset; the rotary group (last) uses the per-token scale
+  static_assert(MF_BN * 8 == 256 && DQK == 8 * 72 && DC == 512, "one key per 8 threads, 9 groups");
+  const int dq_key = tid >> 3, dq_cb = tid & 7;
+  struct DqPlan { const LDS_AS uint8_t *sp, *cp, *scp; LDS_AS uint8_t* tp; float keep; };
+  auto dequant_plan = [&](int t, int sidx, int tbuf) -> DqPlan {
+    DqPlan d;
+    d.sp = (const LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
+    d.cp = d.sp + dq_key * (DQK / 2) + dq_cb * 4;                        // + 32 i
+    d.scp = d.sp + Q4_CODE_BYTES + dq_key * (DC / 16) + (dq_cb >> 2) * 2;  // + 4 i
+    d.tp = (LDS_AS uint8_t*)(smem + tbuf * TILE_BYTES) + dq_key * 128 +
+           ((dq_cb ^ key_swizzle(dq_key)) << 4);                             // + 4096 i
+    d.keep = 1.f;
+    if (cls[t] == TILE_MASKED_ZERO) {
+      // never-written slots hold arbitrary bytes: a zero scale gives zeros
+      const int sl = (t_begin + t) * MF_BN + dq_key;
+      d.keep = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0 ? 1.f : 0.f;
+    }
+    return d;
+  };
+  // 64-dim group i of this thread's key
+  auto dequant_chunk = [&](const DqPlan& d, int i) {
+    const uint32_t codes = *(const LDS_AS uint32_t*)(d.cp + 32 * i);
+    const uint16_t sbits = i < DC / 64 ? *(const LDS_AS uint16_t*)(d.scp + 4 * i)
+                                       : *(const LDS_AS uint16_t*)(d.sp + Q4_CODE_BYTES + Q4_CS_BYTES + dq_key * 2);
+    const float sc = d.keep != 0.f ? __half2float(__ushort_as_half(sbits)) : 0.f;
+    bf16x8_t v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // element e = nibble e of the little-endian word (low nibble first),
+      // sign-extended; q * s is exact in fp32 (4 x 11 significant bits) and
+      // rounds once to bf16 (nearest even, v_cvt_pk_bf16_f32)
+      const int q = __builtin_amdgcn_sbfe((int)codes, 4 * e, 4);
+      v[e] = (__bf16)((float)q * sc);
+    }
+    *(LDS_AS bf16x8_t*)(d.tp + i * MF_BN * 128) = v;
+  };
+  auto dequant = [&](int t, int sidx, int tbuf) {
+    const DqPlan d = dequant_plan(t, sidx, tbuf);
+#pragma unroll 3
+    for (int i = 0; i < NCG; ++i) dequant_chunk(d, i);
+  };
+
   // ---- scores of one tile, S^T = K . Q^T (one 32-key block, LDS reads KPF
   // steps ahead).  The previous tile's value fragments (buffer vprev) are
   // read two per step over the first steps: they land while the chain runs
   // and do not hold up its first MFMA ----
-  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma, PVFrag& f, int vprev) -> f32x16_t {
+  // INT4: with do_dq, the next tile is dequantised into buffer vprev during
+  // the chain: once every wave holds its value fragments of vprev (a barrier
+  // after their reads), one 64-dim group every third step.
+  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma, PVFrag& f, int vprev, bool do_dq,
+                       const DqPlan& dqp) -> f32x16_t {
     // the score accumulator lives in VGPRs (mfma_vgpr): the 256 AGPRs hold
     // the output accumulators, and an AGPR score block would be swapped with
     // one of them every tile (copies that wait for the MFMA pipe to drain)
@@ -286,6 +379,16 @@ void attn_mfma_kernel(MfmaArgs ma) {
       // one piece of the next tile's copy every NKS / LOADS steps
       if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
       if (ks >= 1 && ks <= 2 * NDB) pv_read_v1(vprev, f, (ks - 1) / NDB, (ks - 1) % NDB);
+      if constexpr (Q4) {
+        static_assert(2 * NDB + 3 * NCG <= NKS, "dequantisation steps");
+        if (do_dq) {
+          if (ks == 2 * NDB) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+          }
+          if (ks > 2 * NDB && (ks - 2 * NDB - 1) % 3 == 0) dequant_chunk(dqp, (ks - 2 * NDB - 1) / 3);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_vgpr_settle(s);
@@ -338,9 +441,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // pass the "previous" probabilities are zeros (any finite tile serves as
   // values).
   auto tile_step = [&](const uint8_t* tile, int k0, int cl, int pbuf, int vprev, int pprev, const DmaPlan& dp,
-                       bool dma) {
+                       bool dma, bool do_dq, const DqPlan& dqp) {
     PVFrag f;
-    f32x16_t s = qk_scores(tile, dp, dma, f, vprev);
+    f32x16_t s = qk_scores(tile, dp, dma, f, vprev, do_dq, dqp);
     if (cl != TILE_FULL) mask_scores(s, k0);
     pv_read_p(pprev, f);
     const float neg_m = softmax_max(s);
@@ -380,87 +483,6 @@ void attn_mfma_kernel(MfmaArgs ma) {
   auto zero_p = [&](int pbuf) {
     for (int i = tid; i < MF_WAVES * 2 * 64; i += 256)
       *(uint4*)(plds + pbuf * MF_WAVES * 2 * 1024 + i * 16) = make_uint4(0, 0, 0, 0);
-  };
-
-  // ---- packed INT4 tiles: the packed bytes and scales of a tile are copied
-  // into a staging buffer (global_load_lds), then dequantised into the bf16
-  // tile layout.  Requires capacity % 8 == 0 (16-byte aligned scale rows).
-  constexpr int Q4_CODE_CH = MF_BN * DQK / 32;          // 16-byte chunks of codes
-  constexpr int Q4_CS_CH = MF_BN * DC / 256;            // of content scales
-  constexpr int Q4_RS_CH = MF_BN * 2 / 16;              // of rotary scales
-  constexpr int Q4_CH = Q4_CODE_CH + Q4_CS_CH + Q4_RS_CH;
-  constexpr int Q4_CODE_BYTES = MF_BN * DQK / 2, Q4_CS_BYTES = MF_BN * DC / 16;
-  const uint8_t* q4_codes = (const uint8_t*)a.cache + (size_t)b * cap * (DQK / 2);
-  const uint8_t* q4_cs = (const uint8_t*)a.aux + (size_t)b * cap * (DC / 16);
-  const uint8_t* q4_rs = (const uint8_t*)a.aux + (size_t)a.batch * cap * (DC / 16) + (size_t)b * cap * 2;
-  static_assert(Q4_CODE_CH == 576 && Q4_CS_CH == 64 && Q4_RS_CH == 4, "staging chunk counts");
-  auto stage_dma = [&](int t, int sidx) {
-    const int k0 = (t_begin + t) * MF_BN;
-    const uint32_t lds_stage = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
-    if (k0 + MF_BN <= cap) {
-      // whole tile: each plane is one contiguous run; chunk j lands at 16 j
-      const uint8_t* cb = q4_codes + (size_t)k0 * (DQK / 2);
-      dma16_sv(cb, (uint32_t)tid * 16, lds_stage + wave * 1024);                  // chunks 0 .. 255
-      dma16_sv(cb, 4096u + (uint32_t)tid * 16, lds_stage + 4096 + wave * 1024);   // 256 .. 511
-      if (wave == 0) dma16_sv(cb, 8192u + (uint32_t)lane * 16, lds_stage + 8192);  // codes 512 .. 575
-      if (wave == 1) dma16_sv(q4_cs + (size_t)k0 * (DC / 16), (uint32_t)lane * 16, lds_stage + 576 * 16);
-      if (wave == 2 && lane < Q4_RS_CH) dma16_sv(q4_rs + (size_t)k0 * 2, (uint32_t)lane * 16, lds_stage + 640 * 16);
-      return;
-    }
-#pragma unroll
-    for (int r = 0; r < (Q4_CH + 255) / 256; ++r) {
-      if (r * 256 + wave * 64 >= Q4_CH) break;   // wave-uniform
-      const int j = r * 256 + wave * 64 + lane;
-      const uint8_t* src;
-      if (j < Q4_CODE_CH) {
-        const int key = j / (DQK / 32), off = j % (DQK / 32);
-        src = q4_codes + (size_t)min(k0 + key, cap - 1) * (DQK / 2) + off * 16;
-      } else if (j < Q4_CODE_CH + Q4_CS_CH) {
-        const int jj = j - Q4_CODE_CH, key = jj / (DC / 256);
-        src = q4_cs + (size_t)min(k0 + key, cap - 1) * (DC / 16) + (jj % (DC / 256)) * 16;
-      } else {
-        // 8 keys per chunk; past-the-end chunks re-read the last 8 keys
-        const int jj = min(j - Q4_CODE_CH - Q4_CS_CH, Q4_RS_CH - 1);
-        src = q4_rs + (size_t)min(k0 + 8 * jj, cap - 8) * 2;
-      }
-      if (j < Q4_CH) dma16(src, lds_stage + (r * 256 + wave * 64) * 16);
-    }
-  };
-  // dequantisation of a staged tile into the bf16 tile layout: thread tid
-  // converts key tid / 8, 16-byte output chunks c = tid % 8 + 8 i (i = 0 .. 8,
-  // i.e. 64-dim group i), so every LDS address is a per-thread base plus a
-  // constant offset; the rotary group (last) uses the per-token scale
-  static_assert(MF_BN * 8 == 256 && DQK == 8 * 72 && DC == 512, "one key per 8 threads, 9 groups");
-  const int dq_key = tid >> 3, dq_cb = tid & 7;
-  auto dequant = [&](int t, int sidx, int tbuf) {
-    const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
-    const LDS_AS uint8_t* cp = sp + dq_key * (DQK / 2) + dq_cb * 4;                    // + 32 i
-    const LDS_AS uint8_t* scp = sp + Q4_CODE_BYTES + dq_key * (DC / 16) + (dq_cb >> 2) * 2;  // + 4 i
-    LDS_AS uint8_t* tp = (LDS_AS uint8_t*)(smem + tbuf * TILE_BYTES) + dq_key * 128 +
-                         ((dq_cb ^ key_swizzle(dq_key)) << 4);                             // + 4096 i
-    float keep = 1.f;
-    if (cls[t] == TILE_MASKED_ZERO) {
-      // never-written slots hold arbitrary bytes: a zero scale gives zeros
-      const int sl = (t_begin + t) * MF_BN + dq_key;
-      keep = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0 ? 1.f : 0.f;
-    }
-#pragma unroll 3
-    for (int i = 0; i < NCG; ++i) {
-      const uint32_t codes = *(const LDS_AS uint32_t*)(cp + 32 * i);
-      const uint16_t sbits = i < DC / 64 ? *(const LDS_AS uint16_t*)(scp + 4 * i)
-                                         : *(const LDS_AS uint16_t*)(sp + Q4_CODE_BYTES + Q4_CS_BYTES + dq_key * 2);
-      const float sc = keep != 0.f ? __half2float(__ushort_as_half(sbits)) : 0.f;
-      bf16x8_t v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // element e = nibble e of the little-endian word (low nibble first),
-        // sign-extended; q * s is exact in fp32 (4 x 11 significant bits) and
-        // rounds once to bf16 (nearest even, v_cvt_pk_bf16_f32)
-        const int q = __builtin_amdgcn_sbfe((int)codes, 4 * e, 4);
-        v[e] = (__bf16)((float)q * sc);
-      }
-      *(LDS_AS bf16x8_t*)(tp + i * MF_BN * 128) = v;
-    }
   };
 
   for (int pass = 0;; ++pass) {
@@ -504,7 +526,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
         lds_barrier();
       }
       // the previous tile's probabilities were published before this barrier
-      tile_step(tile, k0, cl, pb, bprev >= 0 ? bprev : bcur, pb ^ 1, dp, nxt < ntl);
+      tile_step(tile, k0, cl, pb, bprev >= 0 ? bprev : bcur, pb ^ 1, dp, nxt < ntl, false, DqPlan{});
       bprev = bcur;
       bcur = bnext;
       pb ^= 1;
@@ -515,7 +537,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
       output_product(bprev, pb ^ 1);
     }
   } else {
-    // tile sequence number `it` uses bf16 buffer it & 1 and staging it & 1
+    // tile sequence number `it` uses bf16 buffer it & 1 and staging it & 1;
+    // the copy of tile it + 2 is issued at the top of step it, tile it + 1 is
+    // dequantised during the score chain of step it
     int cur = next_tile(0), it = 0, pb = 0;
     zero_p(1);
     if (cur < ntl) {
@@ -527,26 +551,27 @@ void attn_mfma_kernel(MfmaArgs ma) {
     int nxt = next_tile(cur + 1);
     if (nxt < ntl) stage_dma(nxt, 1);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_barrier();
     while (cur < ntl) {
       const int bc = it & 1;
       const int nn = nxt < ntl ? next_tile(nxt + 1) : ntl;
-      tile_step(smem + bc * TILE_BYTES, (t_begin + cur) * MF_BN, cls[cur], pb, it > 0 ? (bc ^ 1) : bc, pb ^ 1,
-                DmaPlan{nullptr, 0u, 0u}, false);
-      // the previous tile's buffer is free, the next tile's packed bytes
-      // have landed, this tile's probabilities are published
+      // this tile is dequantised, the next tile's packed bytes have landed,
+      // the previous probabilities are published, staging it & 1 is free
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();
-      if (nxt < ntl) dequant(nxt, (it + 1) & 1, bc ^ 1);
-      if (nn < ntl) stage_dma(nn, it & 1);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      lds_barrier();
+      if (nn < ntl) stage_dma(nn, bc);
+      const bool do_dq = nxt < ntl;
+      const DqPlan dqp = do_dq ? dequant_plan(nxt, bc ^ 1, bc ^ 1) : DqPlan{};
+      tile_step(smem + bc * TILE_BYTES, (t_begin + cur) * MF_BN, cls[cur], pb, it > 0 ? (bc ^ 1) : bc, pb ^ 1,
+                DmaPlan{nullptr, 0u, 0u}, false, do_dq, dqp);
       ++it;
       pb ^= 1;
       cur = nxt;
       nxt = nn;
     }
-    if (it > 0) output_product((it - 1) & 1, pb ^ 1);
+    if (it > 0) {
+      lds_barrier();
+      output_product((it - 1) & 1, pb ^ 1);
+    }
   }
   __syncthreads();
   if (!__syncthreads_or(overflow)) break;
