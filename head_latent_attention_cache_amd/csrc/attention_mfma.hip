@@ -299,6 +299,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // constant offset; the rotary group (last) uses the per-token scale
   static_assert(MF_BN * 8 == 256 && DQK == 8 * 72 && DC == 512, "one key per 8 threads, 9 groups");
   const int dq_key = tid >> 3, dq_cb = tid & 7;
+  // split of a tile's dequantisation: DQ_QK groups during the score chain
+  // (one every DQ_GAP steps), the others one every DQ_PV_GAP output MFMAs
+  constexpr int DQ_QK = 5, DQ_GAP = 5, DQ_PV_GAP = 6;
   struct DqPlan { const LDS_AS uint8_t *sp, *cp, *scp; LDS_AS uint8_t* tp; float keep; };
   auto dequant_plan = [&](int t, int sidx, int tbuf) -> DqPlan {
     DqPlan d;
@@ -380,13 +383,15 @@ void attn_mfma_kernel(MfmaArgs ma) {
       if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
       if (ks >= 1 && ks <= 2 * NDB) pv_read_v1(vprev, f, (ks - 1) / NDB, (ks - 1) % NDB);
       if constexpr (Q4) {
-        static_assert(2 * NDB + 3 * NCG <= NKS, "dequantisation steps");
+        static_assert(2 * NDB + DQ_GAP * DQ_QK <= NKS, "dequantisation steps");
         if (do_dq) {
           if (ks == 2 * NDB) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             lds_barrier();
           }
-          if (ks > 2 * NDB && (ks - 2 * NDB - 1) % 3 == 0) dequant_chunk(dqp, (ks - 2 * NDB - 1) / 3);
+          // groups 0 .. DQ_QK - 1 here, one every DQ_GAP steps; the rest with the output MFMAs
+          if (ks > 2 * NDB && (ks - 2 * NDB - 1) % DQ_GAP == 0 && (ks - 2 * NDB - 1) / DQ_GAP < DQ_QK)
+            dequant_chunk(dqp, (ks - 2 * NDB - 1) / DQ_GAP);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -460,6 +465,10 @@ void attn_mfma_kernel(MfmaArgs ma) {
       vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
       vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
       o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, f.pfr[j][r], o[d * MF_WAVES + r], 0, 0, 0);
+      if constexpr (Q4) {
+        static_assert(DQ_PV_GAP * (NCG - DQ_QK) <= 2 * NDB * MF_WAVES, "dequantisation steps");
+        if (do_dq && i % DQ_PV_GAP == 3 && DQ_QK + i / DQ_PV_GAP < NCG) dequant_chunk(dqp, DQ_QK + i / DQ_PV_GAP);
+      }
       if ((i & 1) == 0 && i / 2 < 16) {
         const int e = i / 2;
         p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c_l2, neg_m));
