@@ -8,9 +8,12 @@ before timing starts.  Default workload: LLM decode (batch 32, 128 heads,
 4096 cached tokens per sequence, d_c 512, d_r 64, bf16).  ``--config 3``
 times the video-chunk workload (1560 query tokens over a 12-frame window).
 
-The "roofline" object covers the attention kernel: algorithmic bytes (decode)
-or FLOPs (chunk) per launch divided by its mean launch time, measured with
-HIP events on the stream the library launches on.  "cpu_baseline" is the
+Steps are timed as replays of HIP graphs that capture one step's library
+calls (``--eager``: direct calls).  The per-call breakdown comes from a pass
+of direct calls with HIP events between them.  The "roofline" object covers
+the attention kernel: algorithmic bytes (decode) or FLOPs (chunk) per launch
+divided by its mean launch time, measured with HIP events on the stream the
+library launches on.  "cpu_baseline" is the
 float64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -42,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy kernel (for HBM counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as direct library calls instead of replays of a captured HIP graph")
     return ap.parse_args()
 
 
@@ -166,15 +171,35 @@ def main():
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    # direct calls, with events between the calls: the per-call times
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
         step(args.warmup + i, True)
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    eager_ms_per_step = start.elapsed_time(end) / args.steps
     call_ms = {k: float(np.mean([e0.elapsed_time(e1) for e0, e1 in v])) for k, v in ev.items()}
+    ms_per_step, timing = eager_ms_per_step, "direct calls"
+    if not args.eager:
+        # the same steps captured once per cache set into HIP graphs and
+        # replayed: the launch gaps between the step's kernels go away
+        graphs = []
+        for k in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k, False)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            graphs[(args.warmup + i) % n_sets].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step, timing = start.elapsed_time(end) / args.steps, "HIP graph replay"
 
     # ---- algorithmic work of the attention call ----
     qf = np.arange(cfg.n_q) // P + cfg.q_first
@@ -234,6 +259,7 @@ def main():
                       "query_tokens_per_s": round(queries / attn_s, 1),
                       "algorithmic_per_launch": alg_per_launch, "source_hash": src},
         "breakdown_ms": {k: round(v, 5) for k, v in call_ms.items()},
+        "timing": {"step": timing, "direct_calls_ms_per_step": round(eager_ms_per_step, 5)},
         "roofline": roof,
     }
 
