@@ -47,6 +47,7 @@ namespace mla {
 
 constexpr int MF_NBUF = 3;               // LDS tile buffers (loads run two tiles ahead)
 constexpr int MF_QLDS_STEPS = 8;         // query 16-dim steps kept in LDS (per wave 8 KB)
+constexpr int PREAD_AHEAD = 3;           // score steps between the probability reads and the chain's end
 
 // LDS bytes of one packed INT4 tile (staging): codes [key][DQK / 2 B], then
 // the content scales [key][DC / 32] fp16, then the rotary scales [key] fp16
@@ -343,13 +344,14 @@ void attn_mfma_kernel(MfmaArgs ma) {
 
   // ---- scores of one tile, S^T = K . Q^T (one 32-key block, LDS reads KPF
   // steps ahead).  The previous tile's value fragments (buffer vprev) are
-  // read two per step over the first steps: they land while the chain runs
-  // and do not hold up its first MFMA ----
+  // read two per step over the first steps, its probabilities (P buffer
+  // pprev) PREAD_AHEAD steps before the end: both land while the chain runs
+  // and neither holds up the first MFMA that needs them ----
   // INT4: with do_dq, the next tile is dequantised into buffer vprev during
   // the chain: once every wave holds its value fragments of vprev (a barrier
   // after their reads), one 64-dim group every third step.
-  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma, PVFrag& f, int vprev, bool do_dq,
-                       const DqPlan& dqp) -> f32x16_t {
+  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma, PVFrag& f, int vprev, int pprev,
+                       bool do_dq, const DqPlan& dqp) -> f32x16_t {
     // the score accumulator lives in VGPRs (mfma_vgpr): the 256 AGPRs hold
     // the output accumulators, and an AGPR score block would be swapped with
     // one of them every tile (copies that wait for the MFMA pipe to drain)
@@ -382,6 +384,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
       // one piece of the next tile's copy every NKS / LOADS steps
       if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
       if (ks >= 1 && ks <= 2 * NDB) pv_read_v1(vprev, f, (ks - 1) / NDB, (ks - 1) % NDB);
+      if (!Q4 && ks == NKS - PREAD_AHEAD) pv_read_p(pprev, f);   // (INT4: registers are short)
       if constexpr (Q4) {
         static_assert(2 * NDB + DQ_GAP * DQ_QK <= NKS, "dequantisation steps");
         if (do_dq) {
@@ -448,9 +451,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
   auto tile_step = [&](const uint8_t* tile, int k0, int cl, int pbuf, int vprev, int pprev, const DmaPlan& dp,
                        bool dma, bool do_dq, const DqPlan& dqp) {
     PVFrag f;
-    f32x16_t s = qk_scores(tile, dp, dma, f, vprev, do_dq, dqp);
+    f32x16_t s = qk_scores(tile, dp, dma, f, vprev, pprev, do_dq, dqp);
     if (cl != TILE_FULL) mask_scores(s, k0);
-    pv_read_p(pprev, f);
+    if constexpr (Q4) pv_read_p(pprev, f);
     const float neg_m = softmax_max(s);
     __builtin_amdgcn_sched_barrier(0);
     // output MFMAs with one exponential after every other one: the VALU work
