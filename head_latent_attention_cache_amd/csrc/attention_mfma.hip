@@ -625,10 +625,13 @@ void attn_mfma_kernel(MfmaArgs ma) {
 }
 
 // merge of the key splits: o = sum_i w_i o_i / sum_i w_i, w_i = exp(lse_i - max)
-// one wave per row, 8 consecutive dims per lane; fixed split order (deterministic)
+// one wave per row, 8 consecutive dims per lane; fixed split order
+// (deterministic).  The splits' partial rows are loaded in groups of MG before
+// any is used, so their latencies overlap.
 template <int DC>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
   static_assert(DC == 64 * 8, "8 dims per lane");
+  constexpr int MG = 8;
   const AttnArgs& a = ma.a;
   const int lane = threadIdx.x & 63;
   const size_t rows = (size_t)a.batch * a.n_rows;
@@ -641,17 +644,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
   for (int u = 0; u < 8; ++u) acc[u] = 0.f;
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    for (int sp = 0; sp < ma.nsplit; ++sp) {
-      const float l = ma.ws_lse[(size_t)sp * rows + r];
-      const float w = expf(l - mx);
-      wsum += w;
-      if (w > 0.f) {
-        const uint4 v = *(const uint4*)(ma.ws_o + ((size_t)sp * rows + r) * DC + lane * 8);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    for (int sp0 = 0; sp0 < ma.nsplit; sp0 += MG) {
+      uint4 v[MG];
+      float w[MG];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          acc[2 * u] = fmaf(w, bf16_to_f32((bf16_t)(wd[u] & 0xffffu)), acc[2 * u]);
-          acc[2 * u + 1] = fmaf(w, bf16_to_f32((bf16_t)(wd[u] >> 16)), acc[2 * u + 1]);
+      for (int u = 0; u < MG; ++u) {
+        const int sp = min(sp0 + u, ma.nsplit - 1);
+        v[u] = *(const uint4*)(ma.ws_o + ((size_t)sp * rows + r) * DC + lane * 8);
+        w[u] = sp0 + u < ma.nsplit ? expf(ma.ws_lse[(size_t)sp * rows + r] - mx) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < MG; ++u) {
+        wsum += w[u];
+        const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        // a split with no visible key has w = 0 and a zero partial row
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(w[u], bf16_to_f32((bf16_t)(wd[e] & 0xffffu)), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w[u], bf16_to_f32((bf16_t)(wd[e] >> 16)), acc[2 * e + 1]);
         }
       }
     }

@@ -214,7 +214,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
   constexpr int NB = BN / 32;                  // 32-column MFMA blocks
   constexpr int TSTEPS = SEG / 64;             // 16-wide MFMA steps per wave and stage
   static_assert(BN % 32 == 0 && SEG % 64 == 0 && (BN * CPR) % 256 == 0, "skinny tile");
-  __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][BN * SEG * 2];
+  // two weight stages; the wave-partial reduction at the end reuses the space
+  constexpr int WB_BYTES = BN * SEG * 2, RED_BYTES = 4 * NB * 64 * 17 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t wsm[2 * WB_BYTES > RED_BYTES ? 2 * WB_BYTES : RED_BYTES];
+  uint8_t (*wbuf)[WB_BYTES] = (uint8_t (*)[WB_BYTES])wsm;
   const int z = blockIdx.z;
   const bf16_t* A = (const bf16_t*)a.A + (size_t)z * a.sA;
   const bf16_t* B = (const bf16_t*)a.B + (size_t)z * a.sB;
@@ -318,8 +321,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
   }
   // sum the four wave partials (fixed order) and store
   __syncthreads();
-  float* red = (float*)wbuf;   // [4 waves][NB][64 lanes][17]
-  static_assert(4 * NB * 64 * 17 * 4 <= 2 * BN * SEG * 2, "reduction buffer");
+  float* red = (float*)wsm;   // [4 waves][NB][64 lanes][17]
 #pragma unroll
   for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -367,7 +369,8 @@ hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st) {
     // pipelines cost occupancy), one when the work-group has a single stage
     const int kst = (a.K + SK_SEG - 1) / SK_SEG;
     const int wg_st = (kst + a.ksplit - 1) / a.ksplit;
-    if (wg_st >= 2) gemm_skinny_bf16_kernel<2, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
+    if (a.K <= 128 && a.ksplit == 1) gemm_skinny_bf16_kernel<1, SK_BN, 128><<<grid, 256, 0, st>>>(a);   // one short stage
+    else if (wg_st >= 2) gemm_skinny_bf16_kernel<2, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
     else gemm_skinny_bf16_kernel<1, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
