@@ -15,33 +15,32 @@
 
 namespace mla {
 
-// angles of all d_r/2 rotary pairs of one token, computed in fp64
-__device__ void rope_table(const Dims& d, const double* coord, float* cosv, float* sinv) {
-  const int npair = d.d_r / 2;
-  for (int i = threadIdx.x; i < npair; i += blockDim.x) {
-    int axis = 0, ii = i, band = d.band0;
-    if (d.rope_dims == 3) {
-      if (ii >= d.band0 / 2) {
-        ii -= d.band0 / 2;
-        axis = 1;
-        band = d.band1;
-        if (ii >= d.band1 / 2) {
-          ii -= d.band1 / 2;
-          axis = 2;
-          band = d.band2;
-        }
+// cosine and sine of rotary pair i of one token: angle in fp64, reduced to
+// [-pi, pi] in fp64, then an fp32 sine/cosine
+__device__ __forceinline__ void rope_pair(const Dims& d, const double* coord, int i, float* c, float* s) {
+  int axis = 0, ii = i, band = d.band0;
+  if (d.rope_dims == 3) {
+    if (ii >= d.band0 / 2) {
+      ii -= d.band0 / 2;
+      axis = 1;
+      band = d.band1;
+      if (ii >= d.band1 / 2) {
+        ii -= d.band1 / 2;
+        axis = 2;
+        band = d.band2;
       }
     }
-    // angle in fp64, reduced to [-pi, pi] in fp64, then an fp32 sine/cosine
-    const double freq = exp2(-2.0 * (double)ii / (double)band * log2((double)d.theta));
-    const double ang = coord[axis] * freq;
-    const double two_pi = 6.283185307179586476925286766559;
-    const float r = (float)(ang - two_pi * rint(ang / two_pi));
-    float s, c;
-    sincosf(r, &s, &c);
-    cosv[i] = c;
-    sinv[i] = s;
   }
+  const double freq = exp2(-2.0 * (double)ii / (double)band * log2((double)d.theta));
+  const double ang = coord[axis] * freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  const float r = (float)(ang - two_pi * rint(ang / two_pi));
+  sincosf(r, s, c);
+}
+
+// angles of all d_r/2 rotary pairs of one token
+__device__ void rope_table(const Dims& d, const double* coord, float* cosv, float* sinv) {
+  for (int i = threadIdx.x; i < d.d_r / 2; i += blockDim.x) rope_pair(d, coord, i, &cosv[i], &sinv[i]);
 }
 
 // quantise n values (n even) of an LDS row to INT4 codes + one fp16 scale
@@ -62,54 +61,65 @@ __device__ __forceinline__ void quant_int4(const float* v, int n, uint8_t* codes
 }
 
 // ---------------------------------------------------------------------------
-// finish the append: rotate the k_rope columns of the projected rows, round to
-// the storage type and store the row at its ring slot.
-// grid (n_tokens, B); y: [B, n_tokens, d_qk] fp32 projection x . w_dkr^T
+// finish the append: sum the K-split partials of the projected row, rotate its
+// k_rope columns, round to the storage type and store it at its ring slot.
+// grid (n_tokens, B); y: [nsplit][B, n_tokens, d_qk] fp32 partials of
+// x . w_dkr^T.  One work item per thread: a content element, or a rotary pair
+// (whose angle the same thread computes); every partial of an item is loaded
+// before the sum (fixed split order), so the work-group waits for one round
+// of loads.
 // ---------------------------------------------------------------------------
 template <typename T, bool INT4>
 __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, int n_tokens,
                                     const int* __restrict__ frame, void* __restrict__ cache,
                                     __half* __restrict__ aux, int batch, int nsplit) {
-  extern __shared__ float smem[];
-  float* row = smem;                       // d_qk
-  float* cosv = row + d.d_qk;              // d_r / 2
-  float* sinv = cosv + d.d_r / 2;
+  extern __shared__ float row[];           // d_qk (INT4: the rounded row, quantised at the end)
+  constexpr int PG = 16;                   // partials loaded together
   const int i = blockIdx.x, b = blockIdx.y;
   const int f = frame[b] + i / g.P, tok = i % g.P;
-  double coord[3];
-  token_coords(d.rope_dims, g.P, g.grid_w, f, tok, coord);
-  rope_table(d, coord, cosv, sinv);
-  // projection of this token: the sum of the K-split partials (fixed order)
   const float* src = y + ((size_t)b * n_tokens + i) * d.d_qk;
   const size_t split_stride = (size_t)batch * n_tokens * d.d_qk;
-  // (loads of 8 partials are issued together, then summed in split order)
   auto proj = [&](int j) {
+    if (nsplit == 1) return src[j];
     float v = 0.f;
-    for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
-      float t[8];
+    for (int sp0 = 0; sp0 < nsplit; sp0 += PG) {
+      float t[PG];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = sp0 + u < nsplit ? src[(sp0 + u) * split_stride + j] : 0.f;
+      for (int u = 0; u < PG; ++u) t[u] = src[(size_t)min(sp0 + u, nsplit - 1) * split_stride + j];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < PG; ++u)
         if (sp0 + u < nsplit) v = sp0 + u == 0 ? t[u] : v + t[u];
     }
     return v;
   };
-  for (int j = threadIdx.x; j < d.d_c; j += blockDim.x) row[j] = round_to<T>(proj(j));
-  __syncthreads();
-  for (int p = threadIdx.x; p < d.d_r / 2; p += blockDim.x) {
-    float x0 = proj(d.d_c + 2 * p), x1 = proj(d.d_c + 2 * p + 1);
-    float c = cosv[p], s = sinv[p];
-    row[d.d_c + 2 * p] = round_to<T>(x0 * c - x1 * s);
-    row[d.d_c + 2 * p + 1] = round_to<T>(x0 * s + x1 * c);
-  }
-  __syncthreads();
   const int slot = ring_slot(g, f, tok);
   const size_t srow = (size_t)b * g.capacity + slot;
-  if (!INT4) {
-    T* out = (T*)cache + srow * d.d_qk;
-    for (int j = threadIdx.x; j < d.d_qk; j += blockDim.x) Elem<T>::store(out, j, row[j]);
-  } else {
+  T* out = (T*)cache + srow * d.d_qk;
+  const int n_items = d.d_c + d.d_r / 2;
+  for (int it = threadIdx.x; it < n_items; it += blockDim.x) {
+    if (it < d.d_c) {
+      const float v = round_to<T>(proj(it));
+      if (INT4) row[it] = v;
+      else Elem<T>::store(out, it, v);
+    } else {
+      const int p = it - d.d_c;
+      const float x0 = proj(d.d_c + 2 * p), x1 = proj(d.d_c + 2 * p + 1);
+      double coord[3];
+      token_coords(d.rope_dims, g.P, g.grid_w, f, tok, coord);
+      float c, s;
+      rope_pair(d, coord, p, &c, &s);
+      const float r0 = round_to<T>(x0 * c - x1 * s), r1 = round_to<T>(x0 * s + x1 * c);
+      if (INT4) {
+        row[d.d_c + 2 * p] = r0;
+        row[d.d_c + 2 * p + 1] = r1;
+      } else {
+        Elem<T>::store(out, d.d_c + 2 * p, r0);
+        Elem<T>::store(out, d.d_c + 2 * p + 1, r1);
+      }
+    }
+  }
+  if (INT4) {
+    __syncthreads();
     uint8_t* codes = (uint8_t*)cache + srow * (d.d_qk / 2);
     const int ng = d.d_c / 32;
     __half* cscale = aux + srow * ng;
@@ -184,13 +194,16 @@ __global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict_
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
                                const int* frame, void* cache, void* aux, int nsplit, hipStream_t st) {
   dim3 grid(n_tokens, batch);
-  size_t shm = (size_t)(d.d_qk + d.d_r) * sizeof(float);
+  const size_t shm = d.cache_fmt == MLA_CACHE_INT4 ? (size_t)d.d_qk * sizeof(float) : 0;
+  // one thread per work item (content element or rotary pair), at most 1024
+  const int items = d.d_c + d.d_r / 2;
+  const int threads = min(1024, (items + 63) / 64 * 64);
   if (d.cache_fmt == MLA_CACHE_INT4)
-    append_store_kernel<bf16_t, true><<<grid, 512, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch, nsplit);
+    append_store_kernel<bf16_t, true><<<grid, threads, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch, nsplit);
   else if (d.dtype == MLA_BF16)
-    append_store_kernel<bf16_t, false><<<grid, 512, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
+    append_store_kernel<bf16_t, false><<<grid, threads, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
   else
-    append_store_kernel<float, false><<<grid, 512, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
+    append_store_kernel<float, false><<<grid, threads, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
   return hipGetLastError();
 }
 
