@@ -363,14 +363,19 @@ hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st) {
     else gemm_nt_f32_kernel<float><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
+  if (a.M <= 32 && a.K <= 128 && a.ksplit == 1) {
+    // one short K stage per work-group (absorbed query): 128 columns each
+    dim3 grid((a.N + 127) / 128, 1, a.batch);
+    gemm_skinny_bf16_kernel<1, 128, 128><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
   if (a.M <= 32) {
     dim3 grid((a.N + SK_BN - 1) / SK_BN, a.ksplit, a.batch);
     // two K stages in flight (measured best for the 64-column tile: deeper
     // pipelines cost occupancy), one when the work-group has a single stage
     const int kst = (a.K + SK_SEG - 1) / SK_SEG;
     const int wg_st = (kst + a.ksplit - 1) / a.ksplit;
-    if (a.K <= 128 && a.ksplit == 1) gemm_skinny_bf16_kernel<1, SK_BN, 128><<<grid, 256, 0, st>>>(a);   // one short stage
-    else if (wg_st >= 2) gemm_skinny_bf16_kernel<2, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
+    if (wg_st >= 2) gemm_skinny_bf16_kernel<2, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
     else gemm_skinny_bf16_kernel<1, SK_BN, SK_SEG><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
