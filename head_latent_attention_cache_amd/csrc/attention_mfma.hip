@@ -538,7 +538,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
         lds_barrier();
       }
       // the previous tile's probabilities were published before this barrier
-      tile_step(tile, k0, cl, pb, bprev >= 0 ? bprev : bcur, pb ^ 1, dp, nxt < ntl, false, DqPlan{});
+      // (the copy is issued every step: after the last tile it copies this
+      // tile again into the free buffer, which costs less than a branch per piece)
+      tile_step(tile, k0, cl, pb, bprev >= 0 ? bprev : bcur, pb ^ 1, dp, true, false, DqPlan{});
       bprev = bcur;
       bcur = bnext;
       pb ^= 1;
@@ -626,8 +628,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
 
 // merge of the key splits: o = sum_i w_i o_i / sum_i w_i, w_i = exp(lse_i - max)
 // one wave per row, 8 consecutive dims per lane; fixed split order
-// (deterministic).  The splits' partial rows are loaded in groups of MG before
-// any is used, so their latencies overlap.
+// (deterministic).  The LSEs and partial rows of MG splits are loaded
+// together, before any is used, so their latencies overlap.
 template <int DC>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
   static_assert(DC == 64 * 8, "8 dims per lane");
@@ -637,32 +639,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
   const size_t rows = (size_t)a.batch * a.n_rows;
   const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
+  const int ns = ma.nsplit;
   float mx = -INFINITY;
-  for (int sp = 0; sp < ma.nsplit; ++sp) mx = fmaxf(mx, ma.ws_lse[(size_t)sp * rows + r]);
   float acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = 0.f;
   float wsum = 0.f;
-  if (mx != -INFINITY) {
-    for (int sp0 = 0; sp0 < ma.nsplit; sp0 += MG) {
-      uint4 v[MG];
-      float w[MG];
+  for (int sp0 = 0; sp0 < ns; sp0 += MG) {
+    uint4 v[MG];
+    float l[MG];
 #pragma unroll
-      for (int u = 0; u < MG; ++u) {
-        const int sp = min(sp0 + u, ma.nsplit - 1);
-        v[u] = *(const uint4*)(ma.ws_o + ((size_t)sp * rows + r) * DC + lane * 8);
-        w[u] = sp0 + u < ma.nsplit ? expf(ma.ws_lse[(size_t)sp * rows + r] - mx) : 0.f;
-      }
+    for (int u = 0; u < MG; ++u) {
+      const int sp = min(sp0 + u, ns - 1);
+      l[u] = ma.ws_lse[(size_t)sp * rows + r];
+      v[u] = *(const uint4*)(ma.ws_o + ((size_t)sp * rows + r) * DC + lane * 8);
+    }
+    if (sp0 == 0) {
+      // the maximum over every split (the first group's are in registers)
 #pragma unroll
-      for (int u = 0; u < MG; ++u) {
-        wsum += w[u];
-        const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        // a split with no visible key has w = 0 and a zero partial row
+      for (int u = 0; u < MG; ++u) mx = fmaxf(mx, l[u]);
+      for (int sp = MG; sp < ns; ++sp) mx = fmaxf(mx, ma.ws_lse[(size_t)sp * rows + r]);
+      if (mx == -INFINITY) break;   // no visible key in any split
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(w[u], bf16_to_f32((bf16_t)(wd[e] & 0xffffu)), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(w[u], bf16_to_f32((bf16_t)(wd[e] >> 16)), acc[2 * e + 1]);
-        }
+    for (int u = 0; u < MG; ++u) {
+      // a split with no visible key has w = 0 and a zero partial row
+      const float w = sp0 + u < ns ? expf(l[u] - mx) : 0.f;
+      wsum += w;
+      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(w, bf16_to_f32((bf16_t)(wd[e] & 0xffffu)), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(w, bf16_to_f32((bf16_t)(wd[e] >> 16)), acc[2 * e + 1]);
       }
     }
   }
