@@ -13,6 +13,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
@@ -75,6 +76,14 @@ __device__ __forceinline__ float halves_max(float x) {
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// four floats to four bf16 (round to nearest even, v_cvt_pk_bf16_f32; the
+// same bits as the bit-level rounding for every finite value), packed
+__device__ __forceinline__ u32x2_t pack4_bf16(float x0, float x1, float x2, float x3) {
+  bf16x4_t v;
+  v[0] = (__bf16)x0; v[1] = (__bf16)x1; v[2] = (__bf16)x2; v[3] = (__bf16)x3;
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 // 16-byte chunk swizzle of a key row: chunk c of key k sits at position

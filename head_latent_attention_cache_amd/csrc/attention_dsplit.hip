@@ -344,26 +344,34 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     }
   }
   __syncthreads();
+  // normalised bf16 rows staged in LDS ([row][DC], 16-byte chunks XOR-swizzled
+  // by row & 7, in the free tile buffers), then each wave writes 16 rows, one
+  // 1 KB row per instruction (the final output or this split's partial)
+  static_assert(DC == 512 && 2 * TILE_BYTES >= DS_ROWS * DC * 2, "output staging");
+  LDS_AS uint8_t* ost = (LDS_AS uint8_t*)smem;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int orow = row0 + r * 32 + (lane & 31);
-    if (orow >= n_rows) continue;
-    const float lt = lrow[r * 32 + (lane & 31)];
+    const int lr = r * 32 + (lane & 31);
+    const float lt = lrow[lr];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    // final output, or this split's partial output (same bf16 row layout)
-    bf16_t* out = pc.part_o ? pc.part_o + (size_t)(orow - row0) * DC + wave * WDIMS
-                            : (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int dim = d * 32 + 8 * q + 4 * g;
+        const int dim = wave * WDIMS + d * 32 + 8 * q + 4 * g;
         const f32x16_t& ob = o[d * 2 + r];
-        u32x2_t pk;
-        pk[0] = (uint32_t)f32_to_bf16(ob[4 * q] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 1] * inv) << 16);
-        pk[1] = (uint32_t)f32_to_bf16(ob[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 3] * inv) << 16);
-        *(u32x2_t*)(out + dim) = pk;
+        const u32x2_t pk = pack4_bf16(ob[4 * q] * inv, ob[4 * q + 1] * inv, ob[4 * q + 2] * inv, ob[4 * q + 3] * inv);
+        *(LDS_AS u32x2_t*)(ost + lr * (DC * 2) + (((dim >> 3) ^ (lr & 7)) << 4) + (dim & 7) * 2) = pk;
       }
+  }
+  __syncthreads();
+  for (int i = 0; i < DS_ROWS / 4; ++i) {
+    const int lr = wave * (DS_ROWS / 4) + i;
+    const int orow = row0 + lr;
+    if (orow >= n_rows) break;
+    const u32x4_t v = *(const LDS_AS u32x4_t*)(ost + lr * (DC * 2) + ((lane ^ (lr & 7)) << 4));
+    bf16_t* out = pc.part_o ? pc.part_o + (size_t)lr * DC : (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC;
+    *(u32x4_t*)(out + lane * 8) = v;
   }
 }
 

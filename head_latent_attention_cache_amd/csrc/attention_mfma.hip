@@ -603,26 +603,37 @@ void attn_mfma_kernel(MfmaArgs ma) {
       pc.part_lse[row - rb * MF_ROWS] = lse;
     }
   }
+  // normalised bf16 rows staged in LDS ([row][DC], 16-byte chunks XOR-swizzled
+  // by row & 7; the tile buffers are free now), then each wave writes 32 rows,
+  // one 1 KB row per instruction (the final output or this split's partial)
+  LDS_AS uint8_t* ost = (LDS_AS uint8_t*)smem;
+  static_assert(DC == 512, "one 16-byte chunk per lane per row");
+  static_assert((size_t)NTB * TILE_BYTES + 2 * STG_BYTES + MF_WAVES * NKS_LDS * 1024 + 2 * MF_WAVES * 2 * 1024 >=
+                    (size_t)MF_ROWS * DC * 2,
+                "the staged output stays below the row sums");
 #pragma unroll
   for (int r = 0; r < MF_WAVES; ++r) {
-    const int orow = rb * MF_ROWS + r * 32 + (lane & 31);
-    if (orow >= n_rows) continue;
-    const float lt = lrow[r * 32 + (lane & 31)];
+    const int lr = r * 32 + (lane & 31);
+    const float lt = lrow[lr];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    // final output, or this split's partial output (same bf16 row layout)
-    bf16_t* out = pc.part_o ? pc.part_o + (size_t)(orow - rb * MF_ROWS) * DC + wave * WDIMS
-                            : (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC + wave * WDIMS;
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int dim = d * 32 + 8 * q + 4 * g;
+        const int dim = wave * WDIMS + d * 32 + 8 * q + 4 * g;
         const f32x16_t& ob = o[d * MF_WAVES + r];
-        u32x2_t pk;
-        pk[0] = (uint32_t)f32_to_bf16(ob[4 * q] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 1] * inv) << 16);
-        pk[1] = (uint32_t)f32_to_bf16(ob[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16(ob[4 * q + 3] * inv) << 16);
-        *(u32x2_t*)(out + dim) = pk;
+        const u32x2_t pk = pack4_bf16(ob[4 * q] * inv, ob[4 * q + 1] * inv, ob[4 * q + 2] * inv, ob[4 * q + 3] * inv);
+        *(LDS_AS u32x2_t*)(ost + lr * (DC * 2) + (((dim >> 3) ^ (lr & 7)) << 4) + (dim & 7) * 2) = pk;
       }
+  }
+  __syncthreads();
+  for (int i = 0; i < 32; ++i) {
+    const int lr = wave * 32 + i;
+    const int orow = rb * MF_ROWS + lr;
+    if (orow >= n_rows) break;
+    const u32x4_t v = *(const LDS_AS u32x4_t*)(ost + lr * (DC * 2) + ((lane ^ (lr & 7)) << 4));
+    bf16_t* out = pc.part_o ? pc.part_o + (size_t)lr * DC : (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC;
+    *(u32x4_t*)(out + lane * 8) = v;
   }
 }
 
@@ -675,11 +686,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint32_t pk[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    pk[u] = (uint32_t)f32_to_bf16(acc[2 * u] * inv) | ((uint32_t)f32_to_bf16(acc[2 * u + 1] * inv) << 16);
-  *(uint4*)((bf16_t*)a.o_lat + r * DC + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  const u32x2_t lo = pack4_bf16(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  const u32x2_t hi = pack4_bf16(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  *(uint4*)((bf16_t*)a.o_lat + r * DC + lane * 8) = make_uint4(lo[0], lo[1], hi[0], hi[1]);
   if (a.lse && lane == 0) a.lse[r] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
