@@ -23,9 +23,17 @@
 //    publishes the bf16 probabilities.
 //  * O^T (d_c x 64 rows): wave w owns d_c / 4 output dims of both row blocks;
 //    value fragments come from the same LDS tile with ds_read_b64_tr_b16.
+//  * The output product runs one tile behind: in the step of tile i every
+//    wave first reads its value fragments of tile i - 1 into registers, and
+//    after the partial scores of tile i are exchanged, waves 2 and 3 issue
+//    the output MFMAs of tile i - 1 while waves 0 and 1 run the softmax of
+//    tile i (then their own output MFMAs).  Probabilities are double
+//    buffered; two barriers per tile (tile ready and previous probabilities
+//    published; partial scores ready and previous values read).
 //  * Key tiles stream into two LDS buffers with global_load_lds_dwordx4, one
-//    tile ahead; three barriers per tile (tile ready, partial scores ready,
-//    probabilities ready).
+//    tile ahead (the copy of tile i + 1 overwrites tile i - 1 once its value
+//    fragments are in registers).  Tile classes are computed when needed
+//    (wave-uniform integer arithmetic), which keeps the LDS at 160 KB.
 //  * Key splits over work-groups with the deterministic log-sum-exp merge,
 //    XCD-aware block order, as in the narrow kernel.
 #include "attention_common.hpp"
@@ -37,10 +45,8 @@ constexpr int DS_ROWS = 64;   // rows per work-group (2 blocks of 32)
 template <int DC, int DR>
 constexpr size_t attn_dsplit_lds_bytes() {
   return 2 * (size_t)((DC + DR) / 64) * MF_BN * 128   // two key tiles
-         + 6 * 4096                                     // partial scores
-         + 2 * 2048                                     // probabilities of the two row blocks
-         + DS_ROWS * sizeof(float)                      // row sums
-         + MF_MAX_TPS;                                  // tile classes
+         + 6 * 4096                                     // partial scores (row sums at the end)
+         + 2 * 2 * 2048;                                // probabilities [buffer][row block]
 }
 
 template <int DC, int DR>
@@ -57,9 +63,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sx = smem + 2 * TILE_BYTES;                 // [2 blocks][3 sources][4][64][16 B]
-  uint8_t* plds = sx + 6 * 4096;                       // [2 blocks][2 steps][64][16 B]
-  float* lrow = (float*)(plds + 2 * 2048);             // [64] row sums
-  uint8_t* cls = (uint8_t*)(lrow + DS_ROWS);
+  uint8_t* plds = sx + 6 * 4096;                       // [2 buffers][2 blocks][2 steps][64][16 B]
+  float* lrow = (float*)sx;                            // [64] row sums (epilogue, over the partials)
   const AttnArgs& a = ma.a;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -82,8 +87,22 @@ void attn_dsplit_kernel(MfmaArgs ma) {
 
   const int t_begin = pc.t0;
   const int ntl = pc.t1 - pc.t0;
-  for (int i = tid; i < ntl; i += 256)
-    cls[i] = classify_tile((t_begin + i) * MF_BN, cap, P, newest, nm, W, fpb, gfq_min, gfq_max);
+  // work-group OR through four flags in the partial-score area (free where
+  // this is called); HIP's __syncthreads_or would add static LDS beyond 160 KB
+  auto block_any = [&](bool v) -> bool {
+    const bool wv = __builtin_amdgcn_ballot_w64(v) != 0;
+    __syncthreads();
+    if (lane == 0) ((int*)sx)[wave] = wv ? 1 : 0;
+    __syncthreads();
+    const bool r = (((int*)sx)[0] | ((int*)sx)[1] | ((int*)sx)[2] | ((int*)sx)[3]) != 0;
+    __syncthreads();
+    return r;
+  };
+  auto tile_class = [&](int i) -> int {
+    return classify_tile((t_begin + i) * MF_BN, cap, P, newest, nm, W, fpb, gfq_min, gfq_max);
+  };
+  bool not_full = false;
+  for (int i = tid; i < ntl; i += 256) not_full |= tile_class(i) != TILE_FULL;
 
   // row of this lane in the softmax waves (wave r < 2 owns row block r)
   const int srow = row0 + (wave & 1) * 32 + (lane & 31);
@@ -106,7 +125,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       qf[r][ks] = v;
     }
   }
-  __syncthreads();
+  // every tile fully visible: no class computation in the loop
+  const bool all_full = !block_any(not_full);
 
   f32x16_t o[NDB * 2];                      // O^T blocks [output-dim block][row block]
   float m_run = -INFINITY, l_run = 0.f, m_seen = -INFINITY;
@@ -115,7 +135,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int gg = lane >> 4, li = lane & 15;
 
   auto next_tile = [&](int i) -> int {
-    while (i < ntl && cls[i] == TILE_SKIP) ++i;
+    if (all_full) return i;
+    while (i < ntl && tile_class(i) == TILE_SKIP) ++i;
     return i;
   };
   // DMA of a key tile: load q of wave w fills 1 KB block (q * 4 + w) = 64-dim
@@ -145,32 +166,35 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int cpart = 2 * (gg & 1) + ((li >> 1) & 1);
   const int vhalf = (li & 1) * 8;
   const int vsw0 = key_swizzle(kq), vsw1 = key_swizzle(kq + 8);
-  auto output_product = [&](int vbuf) {
+  // value fragments of the tile in `vbuf` (registers), then the output
+  // MFMAs with the probabilities of P buffer `pbuf`
+  struct VFrag { i16x4_t v0[2][NDB], v1[2][NDB]; };
+  auto read_values = [&](int vbuf, VFrag& f) {
     const LDS_AS uint8_t* vt =
         (const LDS_AS uint8_t*)(smem + vbuf * TILE_BYTES) + (WDIMS / 64) * wave * MF_BN * 128;
-    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)plds + lane * 16;
-    bf16x8_t pfr[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) pfr[j][r] = *(const LDS_AS bf16x8_t*)(pbase + (r * 2 + j) * 1024);
-    i16x4_t v0[2][NDB], v1[2][NDB];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
-        v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        f.v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS_AS i16x4_t*)(gbase + ((((d & 1) * 4 + cpart) ^ vsw0) << 4)));
-        v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        f.v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
       }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto output_mfma = [&](const VFrag& f, int pbuf) {
+    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pbuf * 4096) + lane * 16;
+    bf16x8_t pfr[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) pfr[j][r] = *(const LDS_AS bf16x8_t*)(pbase + (r * 2 + j) * 1024);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, v0[j][d]), h1 = __builtin_bit_cast(bf16x4_t, v1[j][d]);
+        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[j][d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[j][d]);
         bf16x8_t vf;
         vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
         vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
@@ -195,18 +219,22 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   m_run = pass == 0 ? -INFINITY : m_seen;
   bool overflow = false;
 
-  int cur = next_tile(0), bc = 0;
+  int cur = next_tile(0), bc = 0, pb = 0;
+  bool first = true;
+  // P buffer 1: zeros, for the output product issued in the first step
+  for (int i = tid; i < 2 * 2 * 64; i += 256)
+    *(uint4*)(plds + 4096 + i * 16) = make_uint4(0, 0, 0, 0);
   if (cur < ntl) issue_loads(cur, 0);
   while (cur < ntl) {
     const int nxt = next_tile(cur + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // barrier 1: this tile is in LDS; every wave is done with the previous
-    // tile (its buffer takes the next one)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // barrier 1: this tile is in LDS; the previous probabilities are
+    // published; every wave is done with the previous step
     lds_barrier();
-    if (nxt < ntl) issue_loads(nxt, bc ^ 1);
     uint8_t* tile = smem + bc * TILE_BYTES;
     const int k0 = (t_begin + cur) * MF_BN;
-    const int cl = cls[cur];
+    const int cl = all_full ? (int)TILE_FULL : tile_class(cur);
     if (cl == TILE_MASKED_ZERO) {
       // zero never-written (or past-the-end) keys of this tile
       for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
@@ -221,6 +249,10 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       lds_barrier();
     }
+    // value fragments of the previous tile (first step: this tile, which the
+    // zero probabilities cancel)
+    VFrag vf;
+    read_values(first ? bc : bc ^ 1, vf);
 
     // ---- partial scores of both row blocks over this wave's quarter ----
     f32x16_t s0, s1;
@@ -262,8 +294,10 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         *(LDS_AS f32x4_t*)(dst + q * 1024) = f32x4_t{s1[4 * q], s1[4 * q + 1], s1[4 * q + 2], s1[4 * q + 3]};
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // barrier 2: partial scores complete
+    // barrier 2: partial scores complete; every wave holds its value
+    // fragments of the previous tile, so its buffer takes the next tile
     lds_barrier();
+    if (nxt < ntl) issue_loads(nxt, bc ^ 1);
 
     if (wave < 2) {
       // full scores of row block `wave`: quarters summed in dim order
@@ -304,7 +338,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
       const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
       float lsum = 0.f;
-      LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + wave * 2 * 1024);
+      LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + pb * 4096 + wave * 2 * 1024);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8_t pf;
@@ -318,16 +352,23 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         *(LDS_AS bf16x8_t*)(pw + (j * 64 + lane) * 16) = pf;
       }
       l_run += lsum;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    // barrier 3: probabilities published
-    lds_barrier();
-    output_product(bc);
+    // the previous tile's output product (waves 2 and 3 meanwhile the softmax above)
+    output_mfma(vf, pb ^ 1);
     bc ^= 1;
+    pb ^= 1;
     cur = nxt;
+    first = false;
   }
-  __syncthreads();
-  if (!__syncthreads_or(overflow)) break;
+  if (!first) {
+    // the last tile's output product
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    VFrag vf;
+    read_values(bc ^ 1, vf);
+    output_mfma(vf, pb ^ 1);
+  }
+  if (!block_any(overflow)) break;
   }
 
   // ---- epilogue: row sums to every wave, then O / l ----
