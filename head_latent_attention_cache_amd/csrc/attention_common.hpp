@@ -99,21 +99,33 @@ __device__ __forceinline__ u32x2_t pack4_bf16(float x0, float x1, float x2, floa
 __device__ __forceinline__ int key_swizzle(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
 
 // Launch plan of an attention kernel: work-group (b, split, row block)
-// attends the split's key tiles; with nsplit > 1 it writes a normalised
-// partial output (bf16, the output precision) and an fp32 LSE per row,
-// merged afterwards in a fixed split order with fp32 weights.
+// attends the split's key tiles; where a row block has more than one split it
+// writes a normalised partial output (bf16, the output precision) and an fp32
+// LSE per row, merged afterwards in a fixed split order with fp32 weights.
+// Two groups of row blocks may use different split counts: rows blocks
+// [0, n_a) of every sequence with ns_a splits (the large pieces, dispatched
+// first on every XCD), [n_a, n_rb) with ns_b (the small pieces that fill the
+// last round).  ns_a == ns_b is the uniform plan.
 // (Measured on the chunk workloads: a schedule of whole row blocks with a
 // stream-K tail ran slower than key splits, because work-groups at staggered
 // key offsets no longer share L2 lines.)
 struct MfmaArgs {
   AttnArgs a;
   int n_rb;          // row blocks per sequence
-  int nsplit;        // key splits
+  int rows_wg;       // rows per row block (work-group)
   int tiles;         // key tiles per sequence
-  int tps;           // tiles per split
-  bf16_t* ws_o;      // [nsplit][B][n_rows][d_c] partial outputs (normalised, bf16), if nsplit > 1
+  int n_a;           // row blocks per sequence in the first group
+  int ns_a, tps_a;   // splits and tiles per split of the first group
+  int ns_b, tps_b;   // of the second group
+  int nsplit;        // max(ns_a, ns_b): split slots of the partial buffers
+  bf16_t* ws_o;      // [nsplit][B][n_rows][d_c] partial outputs (normalised, bf16)
   float* ws_lse;     // [nsplit][B][n_rows]
 };
+
+// split count of row block rb (of any sequence)
+__host__ __device__ __forceinline__ int plan_splits(const MfmaArgs& ma, int rb) {
+  return rb < ma.n_a ? ma.ns_a : ma.ns_b;
+}
 
 // one contiguous key range of one row block handled by a work-group; the
 // partial pointers address the row block's first row (null: final output)
@@ -124,19 +136,42 @@ struct Piece {
   float* part_lse;
 };
 
-// the piece of linear work-group `lin`
-__device__ __forceinline__ Piece wg_piece(const MfmaArgs& ma, int lin, int rows_per_wg) {
+// the piece of this work-group.  Work-group id runs on XCD id % 8 as number
+// id / 8 of that XCD; every XCD takes its share of the first group's pieces
+// first, then of the second group's, each group in (b, split, rb) order
+// (consecutive work-groups of an XCD attend the same key range).
+__device__ __forceinline__ Piece wg_piece(const MfmaArgs& ma) {
   const int B = ma.a.batch, n_rows = ma.a.n_rows, DC = ma.a.d.d_c;
-  const int per_b = ma.nsplit * ma.n_rb;
-  const int b = lin / per_b, split = (lin / ma.n_rb) % ma.nsplit, rb = lin % ma.n_rb;
+  const int N = gridDim.x, id = blockIdx.x;
+  const int x = id & 7, j = id >> 3;
+  const int NB = B * ma.n_a * ma.ns_a;
+  const int big_x = NB / 8 + (x < NB % 8 ? 1 : 0);
+  const int big_before = x * (NB / 8) + min(x, NB % 8);
+  int b, split, rb, tps;
+  if (j < big_x) {
+    const int k = big_before + j;
+    const int per_b = ma.ns_a * ma.n_a;
+    b = k / per_b;
+    split = (k % per_b) / ma.n_a;
+    rb = k % ma.n_a;
+    tps = ma.tps_a;
+  } else {
+    const int n_b = ma.n_rb - ma.n_a;
+    const int k = (x * (N / 8) + min(x, N % 8)) - big_before + (j - big_x);
+    const int per_b = ma.ns_b * n_b;
+    b = k / per_b;
+    split = (k % per_b) / n_b;
+    rb = ma.n_a + k % n_b;
+    tps = ma.tps_b;
+  }
   Piece pc;
   pc.rbg = b * ma.n_rb + rb;
-  pc.t0 = split * ma.tps;
-  pc.t1 = min(pc.t0 + ma.tps, ma.tiles);
+  pc.t0 = split * tps;
+  pc.t1 = min(pc.t0 + tps, ma.tiles);
   pc.part_o = nullptr;
   pc.part_lse = nullptr;
-  if (ma.nsplit > 1) {
-    const size_t row0 = ((size_t)split * B + b) * n_rows + (size_t)rb * rows_per_wg;
+  if (plan_splits(ma, rb) > 1) {
+    const size_t row0 = ((size_t)split * B + b) * n_rows + (size_t)rb * ma.rows_wg;
     pc.part_o = ma.ws_o + row0 * DC;
     pc.part_lse = ma.ws_lse + row0;
   }
@@ -176,16 +211,9 @@ __device__ __forceinline__ uint8_t classify_tile(int k0, int cap, int P, int new
   return TILE_MASKED;
 }
 
-// XCD-aware work-group order: consecutive linear indices land on one XCD
-// (the work-groups sharing a sequence's key range share an L2)
-__device__ __forceinline__ int xcd_linear_block() {
-  const int total = gridDim.x, id = blockIdx.x;
-  const int xcd = id & 7, per = total >> 3, rem = total & 7;
-  return xcd * per + min(xcd, rem) + (id >> 3);
-}
-
 // launch plan (key-split fields of MfmaArgs) for row blocks of `rows_per_wg`
-// and MF_BN-key tiles; returns the number of work-groups
+// and MF_BN-key tiles; returns the number of work-groups (the grid must be
+// exactly that: wg_piece derives each work-group's piece from it)
 int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma);
 // workspace bytes of a plan
 size_t attn_plan_workspace(const MfmaArgs& ma);

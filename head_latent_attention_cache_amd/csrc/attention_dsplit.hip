@@ -71,8 +71,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int g = lane >> 5;
   const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
 
-  const int lin = xcd_linear_block();
-  const Piece pc = wg_piece(ma, lin, DS_ROWS);
+  const Piece pc = wg_piece(ma);
   const int b = pc.rbg / ma.n_rb;
   const int rb = pc.rbg % ma.n_rb;
 

@@ -41,6 +41,11 @@
 //  * Optional split of the key range over work-groups with a deterministic
 //    log-sum-exp merge (decode and load balance); the block order is
 //    XCD-aware so that the work-groups sharing a key range share an L2.
+#include <algorithm>
+#include <cstdio>
+#include <mutex>
+#include <vector>
+
 #include "attention_common.hpp"
 
 namespace mla {
@@ -91,8 +96,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int g = lane >> 5;                   // half of the wave
   const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
 
-  const int lin = xcd_linear_block();
-  const Piece pc = wg_piece(ma, lin, MF_ROWS);
+  const Piece pc = wg_piece(ma);
   const int b = pc.rbg / ma.n_rb;
   const int rb = pc.rbg % ma.n_rb;
 
@@ -650,7 +654,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
   const size_t rows = (size_t)a.batch * a.n_rows;
   const size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const int ns = ma.nsplit;
+  const int ns = plan_splits(ma, (int)(r % a.n_rows) / ma.rows_wg);
+  if (ns <= 1) return;   // a single split wrote the final row itself
   float mx = -INFINITY;
   float acc[8];
 #pragma unroll
@@ -707,31 +712,43 @@ bool attn_mfma_supported(const Dims& d, const Geo& g) {
   return d.cache_fmt == MLA_CACHE_DENSE || (d.cache_fmt == MLA_CACHE_INT4 && g.capacity % 8 == 0);
 }
 
-// number of key splits: balance whole rounds of work-groups over the CUs
-// against the cost of writing and merging bf16 partial outputs
-static int choose_splits(int units, int tiles, int n_rows_total, int d_c) {
-  const int G = 256;   // CUs of the chip (one work-group each)
-  int best = 1;
-  double best_cost = 1e30;
-  for (int ns = 1; ns <= 64 && ns <= tiles; ++ns) {
-    const int tps = (tiles + ns - 1) / ns;
-    const long long wgs = (long long)units * ns;
-    const long long rounds = (wgs + G - 1) / G;
-    // per 32-key tile per work-group, +1 tile for the query load/epilogue
-    // (a constant fitted to measured split sweeps: 8 splits for the decode
-    // batch, 3 for the video chunk)
-    double cost = (double)rounds * (tps + 1) * 2.5e-6;
-    if (ns > 1) cost += (double)ns * n_rows_total * d_c * 4.0 / 4.0e12;   // partial write + read
-    if (cost < best_cost * 0.98) {
-      best_cost = cost;
-      best = ns;
-    }
+// cost model of a plan (seconds): the busiest CU's queue under greedy
+// dispatch (each XCD's 32 CUs take its work-groups in order, large pieces
+// first), at a fitted time per 32-key tile (+1 tile per piece for the query
+// load and the epilogue), plus the bf16 partial outputs written and merged
+static double plan_cost(int B, int n_rb, int rows_wg, int n_rows, int tiles, int d_c, int n_a, int ns_a,
+                        int ns_b) {
+  constexpr int XCDS = 8, CUS = 32;
+  constexpr double T_TILE = 2.5e-6;
+  const int tps_a = (tiles + ns_a - 1) / ns_a, tps_b = (tiles + ns_b - 1) / ns_b;
+  const long long NB = (long long)B * n_a * ns_a, NS = (long long)B * (n_rb - n_a) * ns_b, N = NB + NS;
+  double worst = 0.0;
+  for (int x = 0; x < XCDS; x += XCDS - 1) {   // the XCDs with the most and the fewest large pieces
+    const long long cnt = N / XCDS + (x < N % XCDS ? 1 : 0);
+    const long long big = NB / XCDS + (x < NB % XCDS ? 1 : 0);
+    const long long small = cnt - big;
+    if (small < 0) return 1e30;
+    double load[CUS] = {0.0};
+    auto put = [&](double w) {
+      int m = 0;
+      for (int c = 1; c < CUS; ++c)
+        if (load[c] < load[m]) m = c;
+      load[m] += w;
+    };
+    for (long long i = 0; i < big; ++i) put(tps_a + 1.0);
+    for (long long i = 0; i < small; ++i) put(tps_b + 1.0);
+    for (int c = 0; c < CUS; ++c) worst = load[c] > worst ? load[c] : worst;
   }
-  return best;
+  const double rows_a = (double)B * std::min(n_a * rows_wg, n_rows);
+  const double rows_b = (double)B * n_rows - rows_a;
+  double part = 0.0;
+  if (ns_a > 1) part += rows_a * ns_a;
+  if (ns_b > 1) part += rows_b * ns_b;
+  return worst * T_TILE + part * d_c * 4.0 / 4.0e12;   // bf16 partial written and read
 }
 
-// MLA_ATTN_SPLITS=<n> fixes the key-split schedule with n splits (testing:
-// results must not depend on it beyond rounding)
+// MLA_ATTN_SPLITS=<n> fixes a uniform plan with n splits (testing: results
+// must not depend on it beyond rounding)
 static int forced_splits() {
   static int v = [] {
     const char* e = getenv("MLA_ATTN_SPLITS");
@@ -740,17 +757,83 @@ static int forced_splits() {
   return v;
 }
 
+// the plan of a shape: the best uniform split count, then two-group plans
+// with 1 or 2 more splits for the last row blocks of every sequence; chosen
+// once per shape (the search runs a small dispatch simulation) and cached
+struct PlanKey { int B, n_rb, rows_wg, n_rows, tiles, d_c; };
+struct PlanVal { int n_a, ns_a, ns_b; };
+static PlanVal search_plan(const PlanKey& k) {
+  const int min_ns = (k.tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // a class table holds MF_MAX_TPS tiles
+  auto cost = [&](int n_a, int ns_a, int ns_b) {
+    return plan_cost(k.B, k.n_rb, k.rows_wg, k.n_rows, k.tiles, k.d_c, n_a, ns_a, ns_b);
+  };
+  PlanVal best{k.n_rb, min_ns, min_ns};
+  double best_cost = cost(k.n_rb, min_ns, min_ns);
+  for (int ns = min_ns + 1; ns <= 64 && ns <= k.tiles; ++ns) {
+    const double c = cost(k.n_rb, ns, ns);
+    if (c < best_cost * 0.98) {
+      best_cost = c;
+      best = PlanVal{k.n_rb, ns, ns};
+    }
+  }
+  // the cheapest two-group plan, taken if it beats the uniform one by 2 %
+  const int ns0 = best.ns_a;
+  PlanVal mixed = best;
+  double mixed_cost = 1e30;
+  for (int extra = 1; extra <= 2; ++extra) {
+    const int ns_b = ns0 + extra;
+    if (ns_b > k.tiles) break;
+    for (int n_a = 0; n_a < k.n_rb; ++n_a) {
+      const double c = cost(n_a, ns0, ns_b);
+      if (c < mixed_cost) {
+        mixed_cost = c;
+        mixed = PlanVal{n_a, ns0, ns_b};
+      }
+    }
+  }
+  return mixed_cost < best_cost * 0.98 ? mixed : best;
+}
+
+static PlanVal cached_plan(const PlanKey& k) {
+  static std::mutex mu;
+  static std::vector<std::pair<PlanKey, PlanVal>> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (memcmp(&e.first, &k, sizeof(PlanKey)) == 0) return e.second;
+  const PlanVal v = search_plan(k);
+  if (cache.size() < 256) cache.push_back({k, v});
+  return v;
+}
+
 int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma) {
   ma->n_rb = (n_rows + rows_per_wg - 1) / rows_per_wg;
+  ma->rows_wg = rows_per_wg;
   ma->tiles = (g.capacity + MF_BN - 1) / MF_BN;
-  const int nr = batch * ma->n_rb;   // row blocks of the launch
-  int ns = forced_splits() > 0 ? min(forced_splits(), ma->tiles)
-                               : choose_splits(nr, ma->tiles, batch * n_rows, d.d_c);
-  const int min_ns = (ma->tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // a class table holds MF_MAX_TPS tiles
-  if (ns < min_ns) ns = min_ns;
-  ma->tps = (ma->tiles + ns - 1) / ns;
-  ma->nsplit = (ma->tiles + ma->tps - 1) / ma->tps;
-  return nr * ma->nsplit;
+  PlanVal v;
+  static const char* forced_plan = getenv("MLA_ATTN_PLAN");   // "n_a:ns_a:ns_b" (testing)
+  int fa = 0, fsa = 0, fsb = 0;
+  if (forced_plan && sscanf(forced_plan, "%d:%d:%d", &fa, &fsa, &fsb) == 3 && fsa > 0 && fsb > 0) {
+    const int min_ns = (ma->tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;
+    v = PlanVal{std::max(0, std::min(fa, ma->n_rb)), std::max(min_ns, std::min(fsa, ma->tiles)),
+                std::max(min_ns, std::min(fsb, ma->tiles))};
+  } else if (forced_splits() > 0) {
+    const int min_ns = (ma->tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;
+    const int ns = std::max(min_ns, std::min(forced_splits(), ma->tiles));
+    v = PlanVal{ma->n_rb, ns, ns};
+  } else {
+    PlanKey k;
+    memset(&k, 0, sizeof(k));
+    k.B = batch; k.n_rb = ma->n_rb; k.rows_wg = rows_per_wg; k.n_rows = n_rows; k.tiles = ma->tiles; k.d_c = d.d_c;
+    v = cached_plan(k);
+  }
+  ma->n_a = v.n_a;
+  ma->tps_a = (ma->tiles + v.ns_a - 1) / v.ns_a;
+  ma->ns_a = (ma->tiles + ma->tps_a - 1) / ma->tps_a;   // splits that hold tiles
+  ma->tps_b = (ma->tiles + v.ns_b - 1) / v.ns_b;
+  ma->ns_b = (ma->tiles + ma->tps_b - 1) / ma->tps_b;
+  if (ma->n_a == ma->n_rb) ma->ns_b = ma->ns_a, ma->tps_b = ma->tps_a;   // uniform
+  ma->nsplit = std::max(ma->ns_a, ma->ns_b);
+  return batch * (ma->n_a * ma->ns_a + (ma->n_rb - ma->n_a) * ma->ns_b);
 }
 
 size_t attn_plan_workspace(const MfmaArgs& ma) {

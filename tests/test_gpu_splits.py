@@ -60,3 +60,13 @@ def test_split_row_kernel_on_narrow_rows(gpu_lib, key, tmp_path):
     a = _run(key, {}, "mfma", tmp_path)
     assert np.max(np.abs(a - d)) <= 2e-2 + 1e-2 * np.max(np.abs(a))
 
+
+
+@pytest.mark.parametrize("key,plan", [(3, "1:2:3"), (3, "0:1:3"), (5, "1:1:4"), (4, "2:2:3"), (2, "0:3:5")])
+def test_two_group_split_plan(gpu_lib, key, plan, tmp_path):
+    # row blocks [0, n_a) of every sequence with ns_a splits, the rest with
+    # ns_b (the work-group order and the merge both follow the plan); the
+    # child checks against the oracle, and the output matches one split
+    d = _run(key, {"MLA_ATTN_PLAN": plan}, "plan", tmp_path)
+    one = _run(key, {"MLA_ATTN_SPLITS": "1"}, "one", tmp_path)
+    assert np.max(np.abs(d - one)) <= 2e-2
