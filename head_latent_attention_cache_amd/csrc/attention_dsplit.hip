@@ -405,13 +405,26 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       }
   }
   __syncthreads();
-  for (int i = 0; i < DS_ROWS / 4; ++i) {
-    const int lr = wave * (DS_ROWS / 4) + i;
-    const int orow = row0 + lr;
-    if (orow >= n_rows) break;
-    const u32x4_t v = *(const LDS_AS u32x4_t*)(ost + lr * (DC * 2) + ((lane ^ (lr & 7)) << 4));
-    bf16_t* out = pc.part_o ? pc.part_o + (size_t)lr * DC : (bf16_t*)a.o_lat + ((size_t)b * n_rows + orow) * DC;
-    *(u32x4_t*)(out + lane * 8) = v;
+  // eight staged rows read, then their eight stores issued
+  constexpr int WROWS = (DS_ROWS / 4);
+  const int nvalid = min(WROWS, max(0, n_rows - (row0 + wave * WROWS)));
+#pragma unroll
+  for (int i0 = 0; i0 < WROWS; i0 += 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int lr = wave * WROWS + i0 + u;
+      v[u] = *(const LDS_AS u32x4_t*)(ost + lr * (DC * 2) + ((lane ^ (lr & 7)) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int lr = wave * WROWS + i0 + u;
+      if (i0 + u < nvalid) {
+        bf16_t* out = pc.part_o ? pc.part_o + (size_t)lr * DC
+                                : (bf16_t*)a.o_lat + ((size_t)b * n_rows + row0 + lr) * DC;
+        *(u32x4_t*)(out + lane * 8) = v[u];
+      }
+    }
   }
 }
 
