@@ -37,7 +37,7 @@ class MLAConfig:
     q_first: int         # absolute frame index of the first query frame
     q_frames: int        # number of consecutive query frames
     dtype: str           # "f32" or "bf16": storage/I-O type, fp32 accumulate
-    cache_fmt: str = "dense"   # "dense" or "int4"
+    cache_fmt: str = "dense"   # "dense", "int4", or "int2" (INT2 content latent, INT4 rotary key)
     cache_given: bool = False  # decode: earlier positions' rows are given; only the
                                # newest frame is appended
 
@@ -70,7 +70,7 @@ class MLAConfig:
         assert len(self.bands) == self.rope_dims
         assert all(b % 2 == 0 for b in self.bands)
         assert self.dtype in ("f32", "bf16")
-        assert self.cache_fmt in ("dense", "int4")
+        assert self.cache_fmt in ("dense", "int4", "int2")
         assert 0 <= self.q_first and self.q_first + self.q_frames <= self.n_frames
 
 
@@ -105,6 +105,10 @@ INT4_VIDEO = VIDEO_CHUNK.replace(name="int4_video_chunk", cache_fmt="int4")
 
 CONFIGS = {1: TINY_VIDEO, 2: LLM_DECODE, 3: VIDEO_CHUNK, 4: LONG_VIDEO, 5: INT4_VIDEO}
 
+# the deeper low-bit variant: INT2 content latent, INT4 rotary key (video-chunk shape)
+INT2_VIDEO = VIDEO_CHUNK.replace(name="int2_video_chunk", cache_fmt="int2")
+EXTRA_CONFIGS = {6: INT2_VIDEO}
+
 # --------------------------------------------------------------------------
 # reduced shapes (same latent widths) for whole-output parity against the oracle
 # --------------------------------------------------------------------------
@@ -123,6 +127,10 @@ SMALL_CONFIGS = {
     5: VIDEO_CHUNK.replace(name="int4_video_small", d_model=512, grid_h=6,
                            grid_w=6, window=4, n_frames=6, q_first=5,
                            cache_fmt="int4"),
+    # INT2 content latent (INT4 rotary key), same shape as the INT4 case
+    6: VIDEO_CHUNK.replace(name="int2_video_small", d_model=512, grid_h=6,
+                           grid_w=6, window=4, n_frames=6, q_first=5,
+                           cache_fmt="int2"),
 }
 
 
@@ -130,8 +138,8 @@ def get_config(key) -> MLAConfig:
     if isinstance(key, MLAConfig):
         return key
     if isinstance(key, int):
-        return CONFIGS[key]
-    for c in list(CONFIGS.values()) + list(SMALL_CONFIGS.values()):
+        return CONFIGS[key] if key in CONFIGS else EXTRA_CONFIGS[key]
+    for c in list(CONFIGS.values()) + list(EXTRA_CONFIGS.values()) + list(SMALL_CONFIGS.values()):
         if c.name == key:
             return c
     raise KeyError(key)

@@ -1,17 +1,25 @@
-"""INT4 latent-cache quantiser of the oracle (test infrastructure only).
+"""Low-bit (INT4, INT2) latent-cache quantiser of the oracle (test
+infrastructure only).
 
 Source: the QuantMLA abstract on the "Multi-Head Latent Attention" topic page
 (thelatestinai.com) quantises both cache paths of MLA, the content latent and
-the decoupled rotary key, to INT4, and dequantises them inside attention.  The
-page does not give the number format; the workload fixes "symmetric, fp16
-scale per 32-element group" for c_kv and "one fp16 scale per token" for
-k_rope.  The remaining choices are readings shared with the HIP path:
+the decoupled rotary key, to INT4 and dequantises them inside attention; the
+same abstract reports a deeper variant with the content latent in INT2 and the
+rotary key in INT4.  The page does not give the number format; the workload
+fixes "symmetric, fp16 scale per 32-element group" for c_kv and "one fp16
+scale per token" for k_rope.  The remaining choices are readings shared with
+the HIP path, written for b bits (qmax = 2^(b-1) - 1, qmin = -2^(b-1)):
 
-* scale  s = fp16_round_to_nearest_even( fp32(amax) / 7.0f )
-* code   q = clamp( round_half_even( fp32(x) / fp32(s) ), -8, 7 ), IEEE fp32 divide;
-           a zero scale gives all-zero codes
+* scale  s = fp16_round_to_nearest_even( fp32(amax) / qmax )   (INT4: amax / 7,
+           INT2: amax / 1)
+* code   q = clamp( round_half_even( fp32(x) / fp32(s) ), qmin, qmax ), IEEE
+           fp32 divide; a zero scale gives all-zero codes (INT2: |x / s| <= 1,
+           so the codes are -1, 0, 1)
 * value  x_hat = q * s   (exact: |q| <= 8 and s has an 11-bit significand)
-* packing: element 2j in the low nibble, 2j+1 in the high nibble, two's complement
+* packing, two's complement, element order from the low bits up: INT4 element
+  2j in the low nibble of byte j; INT2 element 4j + k in bits 2k .. 2k + 1
+* row layout: content codes (d_c * b / 8 bytes) then the INT4 rotary codes
+  (d_r / 2 bytes)
 
 All arithmetic is float32 NumPy so that the decisions (the integer codes) are
 taken in the precision the kernel takes them in.
@@ -21,24 +29,27 @@ from __future__ import annotations
 import numpy as np
 
 
-def quantize_groups(x, group: int):
-    """Quantise the last axis in groups of ``group`` elements.
+def quantize_groups(x, group: int, bits: int = 4):
+    """Quantise the last axis in groups of ``group`` elements to ``bits``-bit
+    symmetric codes.
 
     ``x``: float array whose values are exactly representable in float32
     (the bf16-rounded cache values).  Returns (codes int8 [..., n], scales
     float16 [..., n // group]).
     """
+    qmax = (1 << (bits - 1)) - 1
+    qmin = -(1 << (bits - 1))
     x = np.asarray(x, dtype=np.float32)
     n = x.shape[-1]
     assert n % group == 0
     g = x.reshape(x.shape[:-1] + (n // group, group))
     amax = np.max(np.abs(g), axis=-1)
-    scale16 = (amax / np.float32(7.0)).astype(np.float16)
+    scale16 = (amax / np.float32(qmax)).astype(np.float16)
     s = scale16.astype(np.float32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint(g / s)
     q = np.where(s == 0, np.float32(0), q)
-    q = np.clip(q, -8, 7).astype(np.int8)
+    q = np.clip(q, qmin, qmax).astype(np.int8)
     return q.reshape(x.shape), scale16
 
 
@@ -72,30 +83,63 @@ def unpack_nibbles(packed):
     return out.astype(np.int8)
 
 
-def quantize_cache_rows(rows, d_c: int, group: int = 32):
-    """Quantise cache rows ``[..., d_c + d_r]`` (bf16 values).
+def pack_crumbs(codes):
+    """int8 codes in [-2, 1], length a multiple of 4 on the last axis -> uint8
+    bytes (element 4j + k in bits 2k .. 2k + 1 of byte j)."""
+    c = np.asarray(codes).astype(np.int16)
+    assert c.shape[-1] % 4 == 0
+    out = np.zeros(c.shape[:-1] + (c.shape[-1] // 4,), dtype=np.int16)
+    for k in range(4):
+        out |= (c[..., k::4] & 0x3) << (2 * k)
+    return out.astype(np.uint8)
+
+
+def unpack_crumbs(packed):
+    """uint8 bytes -> int8 2-bit codes (lowest bits first), sign-extended."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int16)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 4,), dtype=np.int16)
+    for k in range(4):
+        out[..., k::4] = (b >> (2 * k)) & 0x3
+    out = np.where(out >= 2, out - 4, out)
+    return out.astype(np.int8)
+
+
+def _pack(codes, bits):
+    return pack_nibbles(codes) if bits == 4 else pack_crumbs(codes)
+
+
+def _unpack(packed, bits):
+    return unpack_nibbles(packed) if bits == 4 else unpack_crumbs(packed)
+
+
+def quantize_cache_rows(rows, d_c: int, group: int = 32, content_bits: int = 4):
+    """Quantise cache rows ``[..., d_c + d_r]`` (bf16 values): the content
+    latent to ``content_bits`` (4 or 2) in groups of ``group``, the rotary key
+    to INT4 with one scale per row.
 
     Returns dict with
-      codes  uint8 [..., (d_c + d_r) / 2]  content codes then rotary codes
-      cscale float16 [..., d_c / group]    per-group content scales
-      rscale float16 [...]                 per-token rotary scale
-      values float64 [..., d_c + d_r]      dequantised row values
+      codes  uint8 [..., d_c * content_bits / 8 + d_r / 2]  content then rotary codes
+      cscale float16 [..., d_c / group]                     per-group content scales
+      rscale float16 [...]                                  per-token rotary scale
+      values float64 [..., d_c + d_r]                       dequantised row values
     """
     rows = np.asarray(rows)
     c = rows[..., :d_c]
     r = rows[..., d_c:]
-    qc, sc = quantize_groups(c, group)
+    qc, sc = quantize_groups(c, group) if content_bits == 4 else quantize_groups(c, group, content_bits)
     qr, sr = quantize_groups(r, r.shape[-1])
     values = np.concatenate(
         [dequantize_groups(qc, sc, group), dequantize_groups(qr, sr, r.shape[-1])], axis=-1)
-    codes = np.concatenate([pack_nibbles(qc), pack_nibbles(qr)], axis=-1)
+    codes = np.concatenate([_pack(qc, content_bits), pack_nibbles(qr)], axis=-1)
     return {"codes": codes, "cscale": sc, "rscale": sr[..., 0], "values": values}
 
 
-def dequantize_cache_rows(codes, cscale, rscale, d_c: int, group: int = 32):
+def dequantize_cache_rows(codes, cscale, rscale, d_c: int, group: int = 32, content_bits: int = 4):
     """Inverse of the storage: packed bytes + scales -> float64 row values."""
-    q = unpack_nibbles(codes)
-    qc, qr = q[..., :d_c], q[..., d_c:]
+    codes = np.asarray(codes)
+    nb = d_c * content_bits // 8
+    qc = _unpack(codes[..., :nb], content_bits)
+    qr = unpack_nibbles(codes[..., nb:])
     c = dequantize_groups(qc, cscale, group)
     r = dequantize_groups(qr, np.asarray(rscale)[..., None], qr.shape[-1])
     return np.concatenate([c, r], axis=-1)

@@ -141,11 +141,16 @@ def rope_rotate(u, coords, cfg) -> np.ndarray:
 # Low-Rank Joint Compression] (down-project to one latent, cache only it),
 # [MLA explainer, Decoupling RoPE] (the small rotary key is cached beside it).
 # ---------------------------------------------------------------------------
+def content_bits(cfg) -> int:
+    """Bits per content-latent code of a low-bit cache (the rotary key is INT4)."""
+    return {"int4": 4, "int2": 2}[cfg.cache_fmt]
+
+
 def new_cache(cfg) -> dict:
     B, cap = cfg.batch, cfg.capacity
     st = {"values": np.zeros((B, cap, cfg.d_qk)), "newest": -1}
-    if cfg.cache_fmt == "int4":
-        st["codes"] = np.zeros((B, cap, cfg.d_qk // 2), np.uint8)
+    if cfg.cache_fmt in ("int4", "int2"):
+        st["codes"] = np.zeros((B, cap, cfg.d_c * content_bits(cfg) // 8 + cfg.d_r // 2), np.uint8)
         st["cscale"] = np.zeros((B, cap, cfg.d_c // INT4_GROUP), np.float16)
         st["rscale"] = np.zeros((B, cap), np.float16)
     return st
@@ -154,8 +159,8 @@ def new_cache(cfg) -> dict:
 def store_rows(st, cfg, slots, rows):
     """Round rows to the cache format and write them at ``slots``."""
     stored = round_to_storage(rows, cfg.dtype)
-    if cfg.cache_fmt == "int4":
-        q = int4.quantize_cache_rows(stored, cfg.d_c, INT4_GROUP)
+    if cfg.cache_fmt in ("int4", "int2"):
+        q = int4.quantize_cache_rows(stored, cfg.d_c, INT4_GROUP, content_bits(cfg))
         st["codes"][:, slots] = q["codes"]
         st["cscale"][:, slots] = q["cscale"]
         st["rscale"][:, slots] = q["rscale"]

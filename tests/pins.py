@@ -55,8 +55,10 @@ def _tiny_video():
     return CONFIGS[1]
 
 
+TINY_INT2 = TINY_INT4.replace(name="tiny_int2", cache_fmt="int2")
+
 BRUTE_CASES = [_tiny_video, lambda: TINIER, lambda: TINIER_BLOCK, lambda: TINY_DECODE,
-               lambda: TINY_INT4]
+               lambda: TINY_INT4, lambda: TINY_INT2]
 
 
 # ---------------------------------------------------------------------------
@@ -89,16 +91,17 @@ def _bf_coords(cfg, frame, tok):
     return (frame * cfg.tokens_per_frame + tok,)
 
 
-def _bf_int4(vals):
+def _bf_lowbit(vals, bits=4):
+    qmax, qmin = 2 ** (bits - 1) - 1, -2 ** (bits - 1)
     amax = max(abs(v) for v in vals)
-    s = float(np.float16(np.float32(amax) / np.float32(7.0)))
+    s = float(np.float16(np.float32(amax) / np.float32(qmax)))
     if s == 0.0:
         return [0.0] * len(vals)
     out = []
     for v in vals:
         q = float(np.float32(v) / np.float32(s))
         r = round(q)                      # ties to even
-        r = max(-8, min(7, r))
+        r = max(qmin, min(qmax, r))
         out.append(r * s)
     return out
 
@@ -125,11 +128,11 @@ def brute_force(cfg, inp):
                           for n in range(dc + dr)]
                     row = yv[:dc] + _bf_rotate(yv[dc:], _bf_coords(cfg, f, tok), cfg.bands, cfg.theta)
                 row = [_round_scalar(v, cfg.dtype) for v in row]
-                if cfg.cache_fmt == "int4":
+                if cfg.cache_fmt in ("int4", "int2"):
                     c = []
                     for gi in range(0, dc, 32):
-                        c += _bf_int4(row[gi:gi + 32])
-                    row = c + _bf_int4(row[dc:])
+                        c += _bf_lowbit(row[gi:gi + 32], 4 if cfg.cache_fmt == "int4" else 2)
+                    row = c + _bf_lowbit(row[dc:], 4)
                 rows.append(row)
                 rows_out[(b, f, tok)] = row
             ring.append((f, rows))
@@ -441,6 +444,48 @@ def check_int4():
     return float(bad)
 
 
+# ---------------------------------------------------------------------------
+# INT2 content quantiser (the rotary key stays INT4)
+# ---------------------------------------------------------------------------
+def check_int2():
+    import torch
+    bad = 0
+    allb = np.arange(256, dtype=np.uint8)
+    bad += int(np.any(oi.pack_crumbs(oi.unpack_crumbs(allb[None]))[0] != allb))
+    codes = oi.unpack_crumbs(allb[None])[0]
+    for k in range(4):   # element 4j + k is bits 2k .. 2k + 1, two's complement
+        want = (((allb >> (2 * k)) & 3).astype(np.int16) ^ 2) - 2
+        bad += int(np.any(codes[k::4] != want))
+    rng = np.random.default_rng(11)
+    x = om.round_bf16(rng.standard_normal((400, 64)) * np.exp(rng.uniform(-8, 8, (400, 1))))
+    q, s = oi.quantize_groups(x, 32, 2)
+    xh = oi.dequantize_groups(q, s, 32)
+    s64 = np.repeat(s.astype(np.float64), 32, axis=1)
+    bad += int(np.any(np.abs(x - xh) > s64 / 2 * (1 + 1e-12)))   # |x / s| <= 1: never clamped
+    bad += int(np.any((q < -1) | (q > 1)))
+    amax_pos = np.abs(x.reshape(400, 2, 32)).argmax(axis=2)
+    qa = np.take_along_axis(q.reshape(400, 2, 32), amax_pos[..., None], 2)[..., 0]
+    bad += int(np.any(np.abs(qa) != 1))
+    want_s = torch.from_numpy((np.abs(x.reshape(400, 2, 32)).max(axis=2) / 1.0).astype(np.float32)).half().numpy()
+    bad += int(np.any(want_s.view(np.uint16) != s.view(np.uint16)))
+    # ties go to even: scale 2 (amax 2), values +-1 and +-3 over 2 -> 0, +-2 over 2 -> +-1
+    t = np.array([[2.0, 1.0, -1.0, 0.5, -2.0, 1.5] + [0.0] * 26])
+    q3, s3 = oi.quantize_groups(t, 32, 2)
+    bad += int(float(s3[0, 0]) != 2.0 or list(q3[0, :6]) != [1, 0, 0, 0, -1, 1])
+    # zero group -> zero scale, zero codes
+    q4, s4 = oi.quantize_groups(np.zeros((1, 32)), 32, 2)
+    bad += int(np.any(q4 != 0) or float(s4[0, 0]) != 0.0)
+    # row storage round trip; bytes per token: d_c / 4 + d_r / 2 codes, fp16 scales
+    rows = om.round_bf16(rng.standard_normal((5, 3, 72)))
+    st = oi.quantize_cache_rows(rows, 64, 32, 2)
+    bad += int(np.any(oi.dequantize_cache_rows(st["codes"], st["cscale"], st["rscale"], 64, 32, 2) != st["values"]))
+    bad += int(st["codes"].shape[-1] != 64 // 4 + 8 // 2 or st["cscale"].shape[-1] != 2)
+    # the rotary part is the INT4 quantiser's
+    st4 = oi.quantize_cache_rows(rows, 64)
+    bad += int(np.any(st["codes"][..., 16:] != st4["codes"][..., 32:]) or np.any(st["rscale"] != st4["rscale"]))
+    return float(bad)
+
+
 CHECKS = {
     "bruteforce": (check_bruteforce, 1e-12),
     "absorption": (check_absorption, 1e-12),
@@ -452,6 +497,7 @@ CHECKS = {
     "library_attention": (check_library_attention, 1e-12),
     "bf16_rounding": (check_bf16_rounding, 0.0),
     "int4": (check_int4, 0.0),
+    "int2": (check_int2, 0.0),
 }
 
 

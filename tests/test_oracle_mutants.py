@@ -17,7 +17,7 @@ _orig = {
     "absorb_query": om.absorb_query, "round_bf16": om.round_bf16,
     "softmax_scale": om.softmax_scale, "query_coords": om.query_coords,
     "quantize_groups": oi.quantize_groups, "pack_nibbles": oi.pack_nibbles,
-    "unpack_nibbles": oi.unpack_nibbles,
+    "unpack_nibbles": oi.unpack_nibbles, "pack_crumbs": oi.pack_crumbs, "unpack_crumbs": oi.unpack_crumbs,
 }
 
 
@@ -106,28 +106,51 @@ def _query_coords_shift(cfg, q_first):
     return _orig["query_coords"](cfg, q_first + 1)
 
 
-def _int4_half_away(x, group):
+def _half_away(x, group, bits=4):
+    qmax, qmin = 2 ** (bits - 1) - 1, -2 ** (bits - 1)
     x = np.asarray(x, np.float32)
     n = x.shape[-1]
     g = x.reshape(x.shape[:-1] + (n // group, group))
-    s16 = (np.max(np.abs(g), axis=-1) / np.float32(7)).astype(np.float16)
+    s16 = (np.max(np.abs(g), axis=-1) / np.float32(qmax)).astype(np.float16)
     s = s16.astype(np.float32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.sign(g / s) * np.floor(np.abs(g / s) + np.float32(0.5))
     q = np.where(s == 0, 0, q)
-    return np.clip(q, -8, 7).astype(np.int8).reshape(x.shape), s16
+    return np.clip(q, qmin, qmax).astype(np.int8).reshape(x.shape), s16
 
 
-def _int4_scale_8(x, group):
+def _scale_one_more(x, group, bits=4):
+    # scale amax / (qmax + 1): 8 for INT4, 2 for INT2
+    qmax, qmin = 2 ** (bits - 1) - 1, -2 ** (bits - 1)
     x = np.asarray(x, np.float32)
     n = x.shape[-1]
     g = x.reshape(x.shape[:-1] + (n // group, group))
-    s16 = (np.max(np.abs(g), axis=-1) / np.float32(8)).astype(np.float16)
+    s16 = (np.max(np.abs(g), axis=-1) / np.float32(qmax + 1)).astype(np.float16)
     s = s16.astype(np.float32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint(g / s)
     q = np.where(s == 0, 0, q)
-    return np.clip(q, -8, 7).astype(np.int8).reshape(x.shape), s16
+    return np.clip(q, qmin, qmax).astype(np.int8).reshape(x.shape), s16
+
+
+def _only_int2(fn):
+    # a mistake in the INT2 path only (INT4 calls pass through)
+    def wrapped(x, group, bits=4):
+        return fn(x, group, bits) if bits == 2 else _orig["quantize_groups"](x, group)
+    return wrapped
+
+
+def _crumbs_reversed_pack(codes):
+    c = np.asarray(codes).astype(np.int16)
+    out = np.zeros(c.shape[:-1] + (c.shape[-1] // 4,), dtype=np.int16)
+    for k in range(4):
+        out |= (c[..., k::4] & 0x3) << (2 * (3 - k))
+    return out.astype(np.uint8)
+
+
+def _crumbs_reversed_unpack(packed):
+    out = _orig["unpack_crumbs"](packed)
+    return out.reshape(out.shape[:-1] + (-1, 4))[..., ::-1].reshape(out.shape)
 
 
 def _pack_swapped(codes):
@@ -157,8 +180,12 @@ MUTANTS = {
     "bf16_truncates": [(om, "round_bf16", _bf16_truncate)],
     "softmax_scale_nope_only": [(om, "softmax_scale", _scale_nope_only)],
     "query_rotated_at_next_frame": [(om, "query_coords", _query_coords_shift)],
-    "int4_ties_away_from_zero": [(oi, "quantize_groups", _int4_half_away)],
-    "int4_scale_amax_over_8": [(oi, "quantize_groups", _int4_scale_8)],
+    "int4_ties_away_from_zero": [(oi, "quantize_groups", _half_away)],
+    "int4_scale_amax_over_8": [(oi, "quantize_groups", _scale_one_more)],
+    "int2_ties_away_from_zero": [(oi, "quantize_groups", _only_int2(_half_away))],
+    "int2_scale_amax_over_2": [(oi, "quantize_groups", _only_int2(_scale_one_more))],
+    "int2_crumbs_reversed": [(oi, "pack_crumbs", _crumbs_reversed_pack),
+                             (oi, "unpack_crumbs", _crumbs_reversed_unpack)],
     "int4_nibbles_swapped": [(oi, "pack_nibbles", _pack_swapped), (oi, "unpack_nibbles", _unpack_swapped)],
 }
 
