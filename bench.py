@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: LLM decode)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload 1..6 (default 2: LLM decode; 5, 6: INT4 and INT2 content cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -74,7 +75,7 @@ def main():
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import head_latent_attention_cache_amd as mla
     from head_latent_attention_cache_amd import api
-    from mla_inputs import CONFIGS, make_workload
+    from mla_inputs import get_config, make_workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -82,7 +83,7 @@ def main():
     mla.load()                      # raises if the HIP library is not built
     torch.cuda.set_device(0)
     dev = "cuda"
-    cfg = CONFIGS[args.config]
+    cfg = get_config(args.config)
     B, H, P = cfg.batch, cfg.n_heads, cfg.tokens_per_frame
     dims, geom = api.dims_from_config(cfg), api.geom_from_config(cfg)
     dt = api.torch_dtype(dims)

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmla_amd.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
-MLA_CACHE_DENSE, MLA_CACHE_INT4 = 0, 1
+MLA_CACHE_DENSE, MLA_CACHE_INT4, MLA_CACHE_INT2 = 0, 1, 2
 
 
 class MlaDims(ctypes.Structure):

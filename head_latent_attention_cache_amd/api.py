@@ -11,7 +11,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT4, MLA_F32, MlaDims, MlaGeom,
+from ._lib import (MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT2, MLA_CACHE_INT4, MLA_F32, MlaDims, MlaGeom,
                    check, load)
 
 _TORCH_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
@@ -27,7 +27,7 @@ def make_dims(n_heads, d_model, d_nope, d_v, d_c, d_r, rope_dims, bands, theta=1
     d.rope_theta = theta
     d.softmax_scale = softmax_scale
     d.dtype = {"f32": MLA_F32, "bf16": MLA_BF16}[dtype] if isinstance(dtype, str) else dtype
-    d.cache_fmt = ({"dense": MLA_CACHE_DENSE, "int4": MLA_CACHE_INT4}[cache_fmt]
+    d.cache_fmt = ({"dense": MLA_CACHE_DENSE, "int4": MLA_CACHE_INT4, "int2": MLA_CACHE_INT2}[cache_fmt]
                    if isinstance(cache_fmt, str) else cache_fmt)
     return d
 
@@ -92,8 +92,9 @@ def new_cache(dims, geom, device="cuda", fill=None):
     nb, na = cache_nbytes(dims, geom)
     cap = geom.window * geom.grid_h * geom.grid_w
     dqk = dims.d_c + dims.d_r
-    if dims.cache_fmt == MLA_CACHE_INT4:
-        cache = torch.empty((geom.batch, cap, dqk // 2), dtype=torch.uint8, device=device)
+    if dims.cache_fmt in (MLA_CACHE_INT4, MLA_CACHE_INT2):
+        # low-bit: code bytes per row as the library sizes them; fp16 scales
+        cache = torch.empty((geom.batch, cap, nb // max(1, geom.batch * cap)), dtype=torch.uint8, device=device)
         aux = torch.empty(na // 2, dtype=torch.float16, device=device)
     else:
         cache = torch.empty((geom.batch, cap, dqk), dtype=torch_dtype(dims), device=device)
@@ -112,7 +113,7 @@ def new_cache(dims, geom, device="cuda", fill=None):
 
 def _check_cache(dims, geom, cache, cache_aux):
     nb, na = cache_nbytes(dims, geom)
-    if dims.cache_fmt == MLA_CACHE_INT4:
+    if dims.cache_fmt in (MLA_CACHE_INT4, MLA_CACHE_INT2):
         _need(cache, "cache", torch.uint8, nb)
         _need(cache_aux, "cache_aux", torch.float16, na // 2)
     else:

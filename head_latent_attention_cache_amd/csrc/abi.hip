@@ -70,11 +70,11 @@ mla_status check_dims(const mla_dims* dm, Dims* d) {
   if (!(dm->rope_theta > 0.f)) return fail(MLA_ERR_INVALID_ARG, "rope_theta must be positive");
   if (dm->dtype != MLA_F32 && dm->dtype != MLA_BF16)
     return fail(MLA_ERR_INVALID_ARG, "dtype must be MLA_F32 or MLA_BF16");
-  if (dm->cache_fmt != MLA_CACHE_DENSE && dm->cache_fmt != MLA_CACHE_INT4)
-    return fail(MLA_ERR_INVALID_ARG, "cache_fmt must be MLA_CACHE_DENSE or MLA_CACHE_INT4");
-  if (dm->cache_fmt == MLA_CACHE_INT4) {
-    if (dm->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "the INT4 cache requires MLA_BF16");
-    if (dm->d_c % 32) return fail(MLA_ERR_INVALID_ARG, "the INT4 cache requires d_c %% 32 == 0");
+  if (dm->cache_fmt != MLA_CACHE_DENSE && dm->cache_fmt != MLA_CACHE_INT4 && dm->cache_fmt != MLA_CACHE_INT2)
+    return fail(MLA_ERR_INVALID_ARG, "cache_fmt must be MLA_CACHE_DENSE, MLA_CACHE_INT4 or MLA_CACHE_INT2");
+  if (dm->cache_fmt != MLA_CACHE_DENSE) {
+    if (dm->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "a low-bit cache requires MLA_BF16");
+    if (dm->d_c % 32) return fail(MLA_ERR_INVALID_ARG, "a low-bit cache requires d_c %% 32 == 0");
   }
   const int dqk = dm->d_c + dm->d_r;
   if (dm->d_c > 1024 || dqk > 1536)
@@ -158,7 +158,7 @@ size_t mla_cache_bytes(const mla_dims* dims, const mla_geom* geom) {
   Geo g;
   if (check_dims(dims, &d) != MLA_OK || check_geom(geom, d, &g) != MLA_OK) return 0;
   const size_t rows = (size_t)geom->batch * g.capacity;
-  if (d.cache_fmt == MLA_CACHE_INT4) return rows * (d.d_qk / 2);
+  if (lowbit_cache(d)) return rows * code_row_bytes(d);
   return rows * d.d_qk * elem_size(d);
 }
 
@@ -166,7 +166,7 @@ size_t mla_cache_aux_bytes(const mla_dims* dims, const mla_geom* geom) {
   Dims d;
   Geo g;
   if (check_dims(dims, &d) != MLA_OK || check_geom(geom, d, &g) != MLA_OK) return 0;
-  if (d.cache_fmt != MLA_CACHE_INT4) return 0;
+  if (!lowbit_cache(d)) return 0;
   const size_t rows = (size_t)geom->batch * g.capacity;
   return rows * (d.d_c / 32 + 1) * sizeof(__half);
 }
@@ -204,7 +204,7 @@ mla_status mla_cache_append(const mla_dims* dims, const mla_geom* geom, void* st
   NEED_PTR(w_dkr);
   NEED_PTR(cache);
   NEED_PTR(workspace);
-  if (d.cache_fmt == MLA_CACHE_INT4) NEED_PTR(cache_aux);
+  if (lowbit_cache(d)) NEED_PTR(cache_aux);
   const size_t need = append_ws_bytes(d, B, n_tokens);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "append workspace needs %zu bytes, got %zu", need, workspace_bytes);
@@ -285,7 +285,7 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
   NEED_PTR(cache);
   NEED_PTR(o_lat);
   if (lse && ((uintptr_t)lse & 3u)) return fail(MLA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
-  if (d.cache_fmt == MLA_CACHE_INT4) NEED_PTR(cache_aux);
+  if (lowbit_cache(d)) NEED_PTR(cache_aux);
   AttnArgs a;
   a.d = d;
   a.g = g;
@@ -361,7 +361,7 @@ mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* s
   if (geom->batch == 0) return MLA_OK;
   NEED_PTR(cache);
   NEED_PTR(out);
-  if (d.cache_fmt == MLA_CACHE_INT4) NEED_PTR(cache_aux);
+  if (lowbit_cache(d)) NEED_PTR(cache_aux);
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_dequant(d, g, geom->batch, cache, cache_aux, out, st), st, "cache dequant");
 }

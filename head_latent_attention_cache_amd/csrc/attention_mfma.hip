@@ -56,17 +56,17 @@ constexpr int PREAD_AHEAD = 3;           // score steps between the probability 
 
 // LDS bytes of one packed INT4 tile (staging): codes [key][DQK / 2 B], then
 // the content scales [key][DC / 32] fp16, then the rotary scales [key] fp16
-template <int DC, int DR>
-constexpr int q4_stage_bytes() { return MF_BN * (DC + DR) / 2 + MF_BN * (DC / 32) * 2 + MF_BN * 2; }
+template <int DC, int DR, int CB>
+constexpr int q4_stage_bytes() { return MF_BN * (DC * CB / 8 + DR / 2) + MF_BN * (DC / 32) * 2 + MF_BN * 2; }
 
-template <int DC, int DR, bool Q4>
+template <int DC, int DR, bool Q4, int CB = 4>
 constexpr size_t attn_mfma_lds_bytes() {
   return (size_t)(Q4 ? 2 : MF_NBUF) * ((DC + DR) / 64) * MF_BN * 128 +
-         (Q4 ? 2 * (size_t)q4_stage_bytes<DC, DR>() : 0) + (size_t)MF_WAVES * MF_QLDS_STEPS * 1024 +
+         (Q4 ? 2 * (size_t)q4_stage_bytes<DC, DR, CB>() : 0) + (size_t)MF_WAVES * MF_QLDS_STEPS * 1024 +
          2 * MF_WAVES * 2 * 1024 + MF_ROWS * sizeof(float) + MF_MAX_TPS;
 }
 
-template <int DC, int DR, bool Q4>
+template <int DC, int DR, bool Q4, int CB = 4>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(MfmaArgs ma) {
   constexpr int DQK = DC + DR;
@@ -82,7 +82,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   static_assert(DQK % 64 == 0 && WDIMS % 32 == 0, "widths");
   static_assert(TILE_BYTES % (256 * 16) == 0, "tile");
 
-  constexpr int STG_BYTES = Q4 ? q4_stage_bytes<DC, DR>() : 0;
+  constexpr int STG_BYTES = Q4 ? q4_stage_bytes<DC, DR, CB>() : 0;
   static_assert(STG_BYTES % 16 == 0, "staging");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* stg = smem + NTB * TILE_BYTES;                   // INT4: [2] packed tiles
@@ -257,26 +257,36 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // ---- packed INT4 tiles: the packed bytes and scales of a tile are copied
   // into a staging buffer (global_load_lds), then dequantised into the bf16
   // tile layout.  Requires capacity % 8 == 0 (16-byte aligned scale rows).
-  constexpr int Q4_CODE_CH = MF_BN * DQK / 32;          // 16-byte chunks of codes
+  constexpr int CODE_ROW = DC * CB / 8 + DR / 2;        // code bytes per key (content, rotary)
+  constexpr int Q4_CODE_CH = MF_BN * CODE_ROW / 16;     // 16-byte chunks of codes
   constexpr int Q4_CS_CH = MF_BN * DC / 256;            // of content scales
   constexpr int Q4_RS_CH = MF_BN * 2 / 16;              // of rotary scales
   constexpr int Q4_CH = Q4_CODE_CH + Q4_CS_CH + Q4_RS_CH;
-  constexpr int Q4_CODE_BYTES = MF_BN * DQK / 2, Q4_CS_BYTES = MF_BN * DC / 16;
-  const uint8_t* q4_codes = (const uint8_t*)a.cache + (size_t)b * cap * (DQK / 2);
+  constexpr int Q4_CODE_BYTES = MF_BN * CODE_ROW, Q4_CS_BYTES = MF_BN * DC / 16;
+  static_assert(CB == 4 || CB == 2, "content code bits");
+  const uint8_t* q4_codes = (const uint8_t*)a.cache + (size_t)b * cap * CODE_ROW;
   const uint8_t* q4_cs = (const uint8_t*)a.aux + (size_t)b * cap * (DC / 16);
   const uint8_t* q4_rs = (const uint8_t*)a.aux + (size_t)a.batch * cap * (DC / 16) + (size_t)b * cap * 2;
-  static_assert(Q4_CODE_CH == 576 && Q4_CS_CH == 64 && Q4_RS_CH == 4, "staging chunk counts");
+  static_assert(Q4_CODE_CH % 64 == 0 && Q4_CS_CH == 64 && Q4_RS_CH == 4, "staging chunk counts");
+  constexpr int CODE_BLK = Q4_CODE_CH / 64;             // 1 KB blocks of codes
   auto stage_dma = [&](int t, int sidx) {
     const int k0 = (t_begin + t) * MF_BN;
     const uint32_t lds_stage = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
     if (k0 + MF_BN <= cap) {
-      // whole tile: each plane is one contiguous run; chunk j lands at 16 j
-      const uint8_t* cb = q4_codes + (size_t)k0 * (DQK / 2);
-      dma16_sv(cb, (uint32_t)tid * 16, lds_stage + wave * 1024);                  // chunks 0 .. 255
-      dma16_sv(cb, 4096u + (uint32_t)tid * 16, lds_stage + 4096 + wave * 1024);   // 256 .. 511
-      if (wave == 0) dma16_sv(cb, 8192u + (uint32_t)lane * 16, lds_stage + 8192);  // codes 512 .. 575
-      if (wave == 1) dma16_sv(q4_cs + (size_t)k0 * (DC / 16), (uint32_t)lane * 16, lds_stage + 576 * 16);
-      if (wave == 2 && lane < Q4_RS_CH) dma16_sv(q4_rs + (size_t)k0 * 2, (uint32_t)lane * 16, lds_stage + 640 * 16);
+      // whole tile: each plane is one contiguous run; chunk j lands at 16 j;
+      // 1 KB block n goes to wave n % 4 (codes, then the content scales, then
+      // the rotary scales)
+      const uint8_t* cb = q4_codes + (size_t)k0 * CODE_ROW;
+#pragma unroll
+      for (int i = 0; i < (CODE_BLK + 2 + 3) / 4; ++i) {
+        const int blk = wave + 4 * i;   // wave-uniform
+        if (blk < CODE_BLK)
+          dma16_sv(cb, (uint32_t)(blk * 64 + lane) * 16, lds_stage + blk * 1024);
+        else if (blk == CODE_BLK)
+          dma16_sv(q4_cs + (size_t)k0 * (DC / 16), (uint32_t)lane * 16, lds_stage + CODE_BLK * 1024);
+        else if (blk == CODE_BLK + 1 && lane < Q4_RS_CH)
+          dma16_sv(q4_rs + (size_t)k0 * 2, (uint32_t)lane * 16, lds_stage + (CODE_BLK + 1) * 1024);
+      }
       return;
     }
 #pragma unroll
@@ -285,8 +295,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
       const int j = r * 256 + wave * 64 + lane;
       const uint8_t* src;
       if (j < Q4_CODE_CH) {
-        const int key = j / (DQK / 32), off = j % (DQK / 32);
-        src = q4_codes + (size_t)min(k0 + key, cap - 1) * (DQK / 2) + off * 16;
+        const int key = j / (CODE_ROW / 16), off = j % (CODE_ROW / 16);
+        src = q4_codes + (size_t)min(k0 + key, cap - 1) * CODE_ROW + off * 16;
       } else if (j < Q4_CODE_CH + Q4_CS_CH) {
         const int jj = j - Q4_CODE_CH, key = jj / (DC / 256);
         src = q4_cs + (size_t)min(k0 + key, cap - 1) * (DC / 16) + (jj % (DC / 256)) * 16;
@@ -307,11 +317,12 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // split of a tile's dequantisation: DQ_QK groups during the score chain
   // (one every DQ_GAP steps), the others one every DQ_PV_GAP output MFMAs
   constexpr int DQ_QK = 5, DQ_GAP = 5, DQ_PV_GAP = 6;
-  struct DqPlan { const LDS_AS uint8_t *sp, *cp, *scp; LDS_AS uint8_t* tp; float keep; };
+  struct DqPlan { const LDS_AS uint8_t *sp, *cp, *rp, *scp; LDS_AS uint8_t* tp; float keep; };
   auto dequant_plan = [&](int t, int sidx, int tbuf) -> DqPlan {
     DqPlan d;
     d.sp = (const LDS_AS uint8_t*)(stg + sidx * STG_BYTES);
-    d.cp = d.sp + dq_key * (DQK / 2) + dq_cb * 4;                        // + 32 i
+    d.cp = d.sp + dq_key * CODE_ROW + dq_cb * CB;                        // + 8 CB i (content)
+    d.rp = d.sp + dq_key * CODE_ROW + DC * CB / 8 + dq_cb * 4;            // rotary codes
     d.scp = d.sp + Q4_CODE_BYTES + dq_key * (DC / 16) + (dq_cb >> 2) * 2;  // + 4 i
     d.tp = (LDS_AS uint8_t*)(smem + tbuf * TILE_BYTES) + dq_key * 128 +
            ((dq_cb ^ key_swizzle(dq_key)) << 4);                             // + 4096 i
@@ -325,17 +336,21 @@ void attn_mfma_kernel(MfmaArgs ma) {
   };
   // 64-dim group i of this thread's key
   auto dequant_chunk = [&](const DqPlan& d, int i) {
-    const uint32_t codes = *(const LDS_AS uint32_t*)(d.cp + 32 * i);
+    const bool content = i < DC / 64;
+    const int cbits = content ? CB : 4;
+    const uint32_t codes = !content ? *(const LDS_AS uint32_t*)d.rp
+                           : CB == 4 ? *(const LDS_AS uint32_t*)(d.cp + 8 * CB * i)
+                                     : (uint32_t)*(const LDS_AS uint16_t*)(d.cp + 8 * CB * i);
     const uint16_t sbits = i < DC / 64 ? *(const LDS_AS uint16_t*)(d.scp + 4 * i)
                                        : *(const LDS_AS uint16_t*)(d.sp + Q4_CODE_BYTES + Q4_CS_BYTES + dq_key * 2);
     const float sc = d.keep != 0.f ? __half2float(__ushort_as_half(sbits)) : 0.f;
     bf16x8_t v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // element e = nibble e of the little-endian word (low nibble first),
+      // element e = field e of the little-endian word (lowest bits first),
       // sign-extended; q * s is exact in fp32 (4 x 11 significant bits) and
       // rounds once to bf16 (nearest even, v_cvt_pk_bf16_f32)
-      const int q = __builtin_amdgcn_sbfe((int)codes, 4 * e, 4);
+      const int q = __builtin_amdgcn_sbfe((int)codes, cbits * e, cbits);
       v[e] = (__bf16)((float)q * sc);
     }
     *(LDS_AS bf16x8_t*)(d.tp + i * MF_BN * 128) = v;
@@ -713,8 +728,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaArgs ma) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Shapes with an MFMA kernel: bf16, d_c = 512, d_r = 64; the packed INT4
-// cache also needs capacity % 8 == 0 (16-byte aligned scale rows).
+// Shapes with an MFMA kernel: bf16, d_c = 512, d_r = 64; the packed INT4 and
+// INT2 caches also need capacity % 8 == 0 (16-byte aligned scale rows).
 bool attn_mfma_supported(const Dims& d, const Geo& g) {
   // MLA_ATTN_KERNEL=generic or =dsplit routes these shapes to another kernel (testing)
   static const bool other = [] {
@@ -722,7 +737,7 @@ bool attn_mfma_supported(const Dims& d, const Geo& g) {
     return e && (strcmp(e, "generic") == 0 || strcmp(e, "dsplit") == 0);
   }();
   if (other || d.dtype != MLA_BF16 || d.d_c != 512 || d.d_r != 64) return false;
-  return d.cache_fmt == MLA_CACHE_DENSE || (d.cache_fmt == MLA_CACHE_INT4 && g.capacity % 8 == 0);
+  return d.cache_fmt == MLA_CACHE_DENSE || (lowbit_cache(d) && g.capacity % 8 == 0);
 }
 
 // cost model of a plan (seconds): the busiest CU's queue under greedy
@@ -881,9 +896,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStr
   if (ws_bytes < attn_plan_workspace(ma)) return hipErrorInvalidValue;
   attn_plan_bind(&ma, ws);
   constexpr int DC = 512, DR = 64;
-  const bool q4 = a.d.cache_fmt == MLA_CACHE_INT4;
-  const size_t shm = q4 ? attn_mfma_lds_bytes<DC, DR, true>() : attn_mfma_lds_bytes<DC, DR, false>();
-  auto kern = q4 ? attn_mfma_kernel<DC, DR, true> : attn_mfma_kernel<DC, DR, false>;
+  const int fmt = a.d.cache_fmt;
+  const size_t shm = fmt == MLA_CACHE_INT4   ? attn_mfma_lds_bytes<DC, DR, true, 4>()
+                     : fmt == MLA_CACHE_INT2 ? attn_mfma_lds_bytes<DC, DR, true, 2>()
+                                             : attn_mfma_lds_bytes<DC, DR, false>();
+  auto kern = fmt == MLA_CACHE_INT4   ? attn_mfma_kernel<DC, DR, true, 4>
+              : fmt == MLA_CACHE_INT2 ? attn_mfma_kernel<DC, DR, true, 2>
+                                      : attn_mfma_kernel<DC, DR, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   kern<<<blocks, 256, shm, st>>>(ma);

@@ -1,4 +1,4 @@
-// Latent attention, generic SIMT kernel (any width, fp32 / bf16 / INT4 cache).
+// Latent attention, generic SIMT kernel (any width, fp32 / bf16 / INT4 / INT2 cache).
 //
 // "Multi-Head Latent Attention" concept page, Low-rank joint compression:
 // with W^UK absorbed into the query every head scores the shared cache row
@@ -19,7 +19,7 @@ constexpr int SIMT_RB = 8;        // rows per block
 constexpr int SIMT_MAXU = 32;     // d_c <= 32 * 32
 
 
-template <typename T, bool INT4>
+template <typename T, bool LOWBIT>
 __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a, int KT) {
   extern __shared__ float smem[];
   const Dims& d = a.d;
@@ -69,12 +69,10 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a, int KT) {
       float v = 0.f;
       if (s < a.g.capacity && ring_frame(s / a.g.P, newest, nm, a.g.window) >= 0) {
         const size_t srow = (size_t)b * a.g.capacity + s;
-        if (!INT4) {
+        if (!LOWBIT) {
           v = Elem<T>::load((const T*)a.cache, srow * dqk + j);
         } else {
-          const uint8_t byte = ((const uint8_t*)a.cache)[srow * (dqk / 2) + j / 2];
-          int qv = (j & 1) ? (byte >> 4) : (byte & 0xF);
-          qv = (qv ^ 8) - 8;
+          const int qv = lowbit_code((const uint8_t*)a.cache + srow * code_row_bytes(d), d, j);
           const float sc16 = j < d.d_c ? __half2float(a.aux[srow * ng + j / 32])
                                        : __half2float(a.aux[(size_t)a.batch * a.g.capacity * ng + srow]);
           v = (float)qv * sc16;
@@ -160,12 +158,12 @@ hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t st) {
   const int KT = simt_key_tile(a.d.d_qk);
   const size_t shm = simt_lds_bytes(a.d.d_qk, KT);
   dim3 grid((a.n_rows + SIMT_RB - 1) / SIMT_RB, a.batch);
-  const void* fn = a.d.cache_fmt == MLA_CACHE_INT4 ? (const void*)attn_simt_kernel<bf16_t, true>
+  const void* fn = lowbit_cache(a.d) ? (const void*)attn_simt_kernel<bf16_t, true>
                    : a.d.dtype == MLA_BF16         ? (const void*)attn_simt_kernel<bf16_t, false>
                                                    : (const void*)attn_simt_kernel<float, false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  if (a.d.cache_fmt == MLA_CACHE_INT4)
+  if (lowbit_cache(a.d))
     attn_simt_kernel<bf16_t, true><<<grid, 256, shm, st>>>(a, KT);
   else if (a.d.dtype == MLA_BF16)
     attn_simt_kernel<bf16_t, false><<<grid, 256, shm, st>>>(a, KT);

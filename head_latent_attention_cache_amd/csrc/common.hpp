@@ -94,4 +94,25 @@ struct Dims {
   int dtype, cache_fmt;
 };
 
+// low-bit caches (INT4, INT2): bits per content code, code bytes per cache
+// row (content codes, then the INT4 rotary codes)
+__host__ __device__ __forceinline__ bool lowbit_cache(const Dims& d) { return d.cache_fmt != MLA_CACHE_DENSE; }
+__host__ __device__ __forceinline__ int content_bits(const Dims& d) { return d.cache_fmt == MLA_CACHE_INT2 ? 2 : 4; }
+__host__ __device__ __forceinline__ int code_row_bytes(const Dims& d) { return d.d_c * content_bits(d) / 8 + d.d_r / 2; }
+
+// integer code of element j of a low-bit cache row (two's complement, the
+// lowest bits first: INT4 element 2i in the low nibble of byte i, INT2
+// element 4i + k in bits 2k .. 2k+1; the rotary part is INT4 after the content)
+__device__ __forceinline__ int lowbit_code(const uint8_t* row, const Dims& d, int j) {
+  if (j < d.d_c && d.cache_fmt == MLA_CACHE_INT2) {
+    const int q = (row[j >> 2] >> (2 * (j & 3))) & 3;
+    return (q ^ 2) - 2;
+  }
+  const int off = j < d.d_c ? 0 : d.d_c * content_bits(d) / 8;
+  const int jj = j < d.d_c ? j : j - d.d_c;
+  const uint8_t byte = row[off + (jj >> 1)];
+  const int q = (jj & 1) ? (byte >> 4) : (byte & 0xF);
+  return (q ^ 8) - 8;
+}
+
 }  // namespace mla

@@ -1,4 +1,4 @@
-// Rotary embedding, cache-row storage (dense or INT4) and the absorbed query's
+// Rotary embedding, cache-row storage (dense, INT4 or INT2) and the absorbed query's
 // rotary half.
 //
 // Rotary embedding: "Multi-Head Latent Attention" concept page, The RoPE
@@ -7,10 +7,11 @@
 // over time, height and width).  Pair i of a band of width b at coordinate p
 // rotates by p * theta^(-2i/b); bands are ordered (t, h, w).
 //
-// INT4 storage: "Multi-Head Latent Attention" topic page, QuantMLA abstract
-// (both cache paths in INT4, dequantised inside attention).  scale =
-// fp16(amax / 7), code = round-half-even(x / scale) clamped to [-8, 7] in IEEE
-// fp32, element 2j in the low nibble.
+// Low-bit storage: "Multi-Head Latent Attention" topic page, QuantMLA abstract
+// (both cache paths in INT4, dequantised inside attention; a deeper variant
+// with the content latent in INT2 and the rotary key in INT4).  For b bits:
+// scale = fp16(amax / (2^(b-1) - 1)), code = round-half-even(x / scale)
+// clamped to [-2^(b-1), 2^(b-1) - 1] in IEEE fp32, the lowest bits first.
 #include "launch.hpp"
 
 namespace mla {
@@ -43,20 +44,23 @@ __device__ void rope_table(const Dims& d, const double* coord, float* cosv, floa
   for (int i = threadIdx.x; i < d.d_r / 2; i += blockDim.x) rope_pair(d, coord, i, &cosv[i], &sinv[i]);
 }
 
-// quantise n values (n even) of an LDS row to INT4 codes + one fp16 scale
-__device__ __forceinline__ void quant_int4(const float* v, int n, uint8_t* codes, __half* scale) {
+// quantise n values (n a multiple of 8 / bits) of an LDS row to `bits`-bit
+// codes (4 or 2) + one fp16 scale
+__device__ __forceinline__ void quant_lowbit(const float* v, int n, int bits, uint8_t* codes, __half* scale) {
+  const int qmax = (1 << (bits - 1)) - 1, per_byte = 8 / bits, mask = (1 << bits) - 1;
   float amax = 0.f;
   for (int j = 0; j < n; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  __half s16 = __float2half_rn(amax / 7.0f);
+  __half s16 = __float2half_rn(amax / (float)qmax);
   float s = __half2float(s16);
   *scale = s16;
-  for (int j = 0; j < n; j += 2) {
-    int q0 = 0, q1 = 0;
-    if (s != 0.f) {
-      q0 = (int)fminf(fmaxf(rintf(v[j] / s), -8.f), 7.f);
-      q1 = (int)fminf(fmaxf(rintf(v[j + 1] / s), -8.f), 7.f);
+  for (int j = 0; j < n; j += per_byte) {
+    int byte = 0;
+    for (int k = 0; k < per_byte; ++k) {
+      int q = 0;
+      if (s != 0.f) q = (int)fminf(fmaxf(rintf(v[j + k] / s), (float)(-qmax - 1)), (float)qmax);
+      byte |= (q & mask) << (bits * k);
     }
-    codes[j / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+    codes[j / per_byte] = (uint8_t)byte;
   }
 }
 
@@ -69,11 +73,11 @@ __device__ __forceinline__ void quant_int4(const float* v, int n, uint8_t* codes
 // before the sum (fixed split order), so the work-group waits for one round
 // of loads.
 // ---------------------------------------------------------------------------
-template <typename T, bool INT4>
+template <typename T, bool LOWBIT>
 __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, int n_tokens,
                                     const int* __restrict__ frame, void* __restrict__ cache,
                                     __half* __restrict__ aux, int batch, int nsplit) {
-  extern __shared__ float row[];           // d_qk (INT4: the rounded row, quantised at the end)
+  extern __shared__ float row[];           // d_qk (low-bit: the rounded row, quantised at the end)
   constexpr int PG = 16;                   // partials loaded together
   const int i = blockIdx.x, b = blockIdx.y;
   const int f = frame[b] + i / g.P, tok = i % g.P;
@@ -99,7 +103,7 @@ __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, 
   for (int it = threadIdx.x; it < n_items; it += blockDim.x) {
     if (it < d.d_c) {
       const float v = round_to<T>(proj(it));
-      if (INT4) row[it] = v;
+      if (LOWBIT) row[it] = v;
       else Elem<T>::store(out, it, v);
     } else {
       const int p = it - d.d_c;
@@ -109,7 +113,7 @@ __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, 
       float c, s;
       rope_pair(d, coord, p, &c, &s);
       const float r0 = round_to<T>(x0 * c - x1 * s), r1 = round_to<T>(x0 * s + x1 * c);
-      if (INT4) {
+      if (LOWBIT) {
         row[d.d_c + 2 * p] = r0;
         row[d.d_c + 2 * p + 1] = r1;
       } else {
@@ -118,15 +122,16 @@ __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, 
       }
     }
   }
-  if (INT4) {
+  if (LOWBIT) {
     __syncthreads();
-    uint8_t* codes = (uint8_t*)cache + srow * (d.d_qk / 2);
+    const int cb = content_bits(d);
+    uint8_t* codes = (uint8_t*)cache + srow * code_row_bytes(d);
     const int ng = d.d_c / 32;
     __half* cscale = aux + srow * ng;
     __half* rscale = aux + (size_t)batch * g.capacity * ng + srow;
     for (int grp = threadIdx.x; grp <= ng; grp += blockDim.x) {
-      if (grp < ng) quant_int4(row + grp * 32, 32, codes + grp * 16, cscale + grp);
-      else quant_int4(row + d.d_c, d.d_r, codes + d.d_c / 2, rscale);
+      if (grp < ng) quant_lowbit(row + grp * 32, 32, cb, codes + grp * 32 * cb / 8, cscale + grp);
+      else quant_lowbit(row + d.d_c, d.d_r, 4, codes + d.d_c * cb / 8, rscale);
     }
   }
 }
@@ -164,7 +169,7 @@ __global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n
 // ---------------------------------------------------------------------------
 // cache rows as float (inspection utility)
 // ---------------------------------------------------------------------------
-template <typename T, bool INT4>
+template <typename T, bool LOWBIT>
 __global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict__ cache,
                                const __half* __restrict__ aux, float* __restrict__ out) {
   const size_t total = (size_t)batch * g.capacity * d.d_qk;
@@ -174,12 +179,10 @@ __global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict_
     const size_t srow = e / d.d_qk;
     const int j = (int)(e % d.d_qk);
     float v;
-    if (!INT4) {
+    if (!LOWBIT) {
       v = Elem<T>::load((const T*)cache, e);
     } else {
-      const uint8_t byte = ((const uint8_t*)cache)[srow * (d.d_qk / 2) + j / 2];
-      int q = (j & 1) ? (byte >> 4) : (byte & 0xF);
-      q = (q ^ 8) - 8;
+      const int q = lowbit_code((const uint8_t*)cache + srow * code_row_bytes(d), d, j);
       const float s = j < d.d_c ? __half2float(aux[srow * ng + j / 32])
                                 : __half2float(aux[(size_t)batch * g.capacity * ng + srow]);
       v = (float)q * s;
@@ -194,11 +197,11 @@ __global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict_
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
                                const int* frame, void* cache, void* aux, int nsplit, hipStream_t st) {
   dim3 grid(n_tokens, batch);
-  const size_t shm = d.cache_fmt == MLA_CACHE_INT4 ? (size_t)d.d_qk * sizeof(float) : 0;
+  const size_t shm = lowbit_cache(d) ? (size_t)d.d_qk * sizeof(float) : 0;
   // one thread per work item (content element or rotary pair), at most 1024
   const int items = d.d_c + d.d_r / 2;
   const int threads = min(1024, (items + 63) / 64 * 64);
-  if (d.cache_fmt == MLA_CACHE_INT4)
+  if (lowbit_cache(d))
     append_store_kernel<bf16_t, true><<<grid, threads, shm, st>>>(d, g, y, n_tokens, frame, cache, (__half*)aux, batch, nsplit);
   else if (d.dtype == MLA_BF16)
     append_store_kernel<bf16_t, false><<<grid, threads, shm, st>>>(d, g, y, n_tokens, frame, cache, nullptr, batch, nsplit);
@@ -223,7 +226,7 @@ hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* ca
   const size_t total = (size_t)batch * g.capacity * d.d_qk;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 65536) blocks = 65536;
-  if (d.cache_fmt == MLA_CACHE_INT4)
+  if (lowbit_cache(d))
     dequant_kernel<bf16_t, true><<<blocks, 256, 0, st>>>(d, g, batch, cache, (const __half*)aux, out);
   else if (d.dtype == MLA_BF16)
     dequant_kernel<bf16_t, false><<<blocks, 256, 0, st>>>(d, g, batch, cache, nullptr, out);

@@ -84,7 +84,7 @@ typedef enum {
 } mla_status;
 
 enum { MLA_F32 = 0, MLA_BF16 = 1 };
-enum { MLA_CACHE_DENSE = 0, MLA_CACHE_INT4 = 1 };
+enum { MLA_CACHE_DENSE = 0, MLA_CACHE_INT4 = 1, MLA_CACHE_INT2 = 2 };
 
 /* Model dimensions, identical for every call on one cache. */
 typedef struct {
@@ -92,14 +92,14 @@ typedef struct {
   int32_t d_model;     /* hidden width */
   int32_t d_nope;      /* per-head content query/key width */
   int32_t d_v;         /* per-head value width */
-  int32_t d_c;         /* shared content latent width (multiple of 32 for INT4) */
+  int32_t d_c;         /* shared content latent width (multiple of 32 for INT4 / INT2) */
   int32_t d_r;         /* shared rotary key width (even) */
   int32_t rope_dims;   /* 1 or 3 */
   int32_t band[3];     /* rotary band widths; 3D: (t, h, w), each even, sum d_r; 1D: band[0] = d_r */
   float rope_theta;    /* frequency base, e.g. 10000 */
   float softmax_scale; /* <= 0 selects 1/sqrt(d_nope + d_r) */
   int32_t dtype;       /* MLA_F32 or MLA_BF16 */
-  int32_t cache_fmt;   /* MLA_CACHE_DENSE, or MLA_CACHE_INT4 (requires MLA_BF16) */
+  int32_t cache_fmt;   /* MLA_CACHE_DENSE, MLA_CACHE_INT4 or MLA_CACHE_INT2 (low-bit: MLA_BF16 only) */
 } mla_dims;
 
 /* Cache geometry shared by every sequence of a batch. */
@@ -122,6 +122,14 @@ typedef struct {
  *                 group, followed by [B, capacity] per-token rotary scales.
  *     value = code * scale; scale = fp16(amax / 7), code = round-half-even of
  *     x / scale clamped to [-8, 7] (IEEE fp32), a zero scale gives zero codes.
+ *   INT2 (the same abstract's deeper variant: the content latent in INT2, the
+ *   rotary key in INT4):
+ *     cache     = [B, capacity, d_c / 4 + d_r / 2] bytes; content codes (element
+ *                 4j + k in bits 2k .. 2k+1 of byte j, two's complement in
+ *                 [-2, 1]) then the rotary codes as for INT4;
+ *     cache_aux = as for INT4.  Content: scale = fp16(amax / 1), code =
+ *     round-half-even of x / scale clamped to [-2, 1] (so -1, 0 or 1);
+ *     rotary key as for INT4.
  * Both functions return 0 when the arguments are invalid.
  */
 size_t mla_cache_bytes(const mla_dims* dims, const mla_geom* geom);

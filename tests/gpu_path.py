@@ -78,7 +78,7 @@ def run_gpu(cfg, inp, fill=None, keep_device=False):
     torch.cuda.synchronize()
     out = {"q_abs": to_host(q_abs), "o_lat": to_host(o_lat), "lse": to_host(lse),
            "o_heads": to_host(o_heads).reshape(B, cfg.n_q, H, cfg.d_v), "y": to_host(y)}
-    if cfg.cache_fmt == "int4":
+    if cfg.cache_fmt in ("int4", "int2"):
         out["codes"] = cache.cpu().numpy()
         na = aux.numel()
         ng = cfg.d_c // 32

@@ -9,7 +9,7 @@ import pytest
 
 import head_latent_attention_cache_amd as mla
 from head_latent_attention_cache_amd import _lib
-from mla_inputs import CONFIGS, SMALL_CONFIGS
+from mla_inputs import CONFIGS, SMALL_CONFIGS, get_config
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla.h")
@@ -55,9 +55,9 @@ def _geom(cfg, **kw):
     return g
 
 
-@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5, 6])
 def test_cache_sizes(lib, key):
-    cfg = CONFIGS[key]
+    cfg = get_config(key)
     d, g = _dims(cfg), _geom(cfg)
     nb = lib.mla_cache_bytes(ctypes.byref(d), ctypes.byref(g))
     na = lib.mla_cache_aux_bytes(ctypes.byref(d), ctypes.byref(g))
@@ -66,6 +66,11 @@ def test_cache_sizes(lib, key):
         assert nb == rows * cfg.d_qk // 2
         assert na == rows * (cfg.d_c // 32 + 1) * 2
         assert (nb + na) // rows == 322
+    elif cfg.cache_fmt == "int2":
+        # 2-bit content codes, 4-bit rotary codes, fp16 group and token scales
+        assert nb == rows * (cfg.d_c // 4 + cfg.d_r // 2)
+        assert na == rows * (cfg.d_c // 32 + 1) * 2
+        assert (nb + na) // rows == 194
     else:
         assert nb == rows * cfg.d_qk * (2 if cfg.dtype == "bf16" else 4)
         assert na == 0
@@ -79,6 +84,8 @@ BAD_DIMS = [
     ("theta zero", dict(rope_theta=0.0)),
     ("dtype", dict(dtype=7)),
     ("int4 with fp32", dict(cache_fmt=1)),
+    ("int2 with fp32", dict(cache_fmt=2)),
+    ("unknown cache format", dict(cache_fmt=3)),
 ]
 
 
@@ -91,6 +98,17 @@ def test_invalid_dims_rejected_before_launch(lib, name, kw):
                            fake, None, None, 0)
     assert st == _lib.MLA_ERR_INVALID_ARG, (name, st)
     assert lib.mla_last_error()
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_lowbit_cache_needs_whole_groups(lib, fmt):
+    cfg = SMALL_CONFIGS[5]              # bf16; a latent of 40 dims leaves a partial group of 32
+    d, g = _dims(cfg, d_c=40, cache_fmt=fmt), _geom(cfg)
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 16, fake, fake, fake, fake, fake,
+                           fake, None, None, 0)
+    assert st == _lib.MLA_ERR_INVALID_ARG
+    assert b"32" in lib.mla_last_error()
 
 
 def test_invalid_geometry_and_pointers(lib):

@@ -5,14 +5,14 @@ import os
 import numpy as np
 
 import oracle.mla as om
-from mla_inputs import CONFIGS
+from mla_inputs import CONFIGS, EXTRA_CONFIGS
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "cache_widths.json")))
 
 
 def _row_bytes(cfg):
     st = om.new_cache(cfg.replace(batch=1, window=1, grid_h=1, grid_w=1, n_frames=1, q_first=0, q_frames=1))
-    if cfg.cache_fmt == "int4":
+    if cfg.cache_fmt in ("int4", "int2"):
         return st["codes"].shape[-1] + 2 * st["cscale"].shape[-1] + 2
     return st["values"].shape[-1] * (2 if cfg.dtype == "bf16" else 4)
 
@@ -43,3 +43,11 @@ def test_int4_row_bytes_and_ratio():
     ratio = _row_bytes(CONFIGS[3]) / _row_bytes(cfg)
     assert abs(ratio - GOLD["quantmla_compression"]["ratio"]) / GOLD["quantmla_compression"]["ratio"] < 0.01
     assert np.isclose(ratio, 1152 / 322)
+
+
+def test_int2_row_bytes():
+    # 2-bit content codes (128 B) + 4-bit rotary codes (32 B) + 16 fp16 group
+    # scales + one fp16 token scale; the pages print no INT2 ratio to pin
+    cfg = EXTRA_CONFIGS[6]
+    assert _row_bytes(cfg) == 128 + 32 + 32 + 2 == 194
+    assert np.isclose(_row_bytes(CONFIGS[3]) / _row_bytes(cfg), 1152 / 194)

@@ -7,7 +7,7 @@ import pytest
 
 import gpu_path as gp
 import oracle.mla as om
-from mla_inputs import CONFIGS, make_workload
+from mla_inputs import CONFIGS, get_config, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -36,18 +36,19 @@ def test_fullsize_llm_decode(gpu_lib):
         gp.compare("y", got["y"][b], ref["y"].reshape(cfg.n_q, cfg.d_model), cfg.dtype)
 
 
-@pytest.mark.parametrize("key", [3, 5])
+@pytest.mark.parametrize("key", [3, 5, 6])
 def test_fullsize_video_chunk(gpu_lib, key):
-    """1560 query tokens x 32 heads over 18,720 keys (dense and INT4 cache):
-    the whole cache, every absorbed query, and five query tokens end to end."""
-    cfg = CONFIGS[key]
+    """1560 query tokens x 32 heads over 18,720 keys (dense, INT4 and INT2
+    content cache): the whole cache, every absorbed query, and five query
+    tokens end to end."""
+    cfg = get_config(key)
     _case(cfg.name)
     inp = make_workload(cfg, seed=0)
     got = gp.run_gpu(cfg, inp)
     st = om.build_cache(cfg, inp)
-    if cfg.cache_fmt == "int4":
+    if cfg.cache_fmt in ("int4", "int2"):
         same = np.mean(got["codes"] == st["codes"])
-        assert same > 0.99, f"only {same:.4f} of INT4 code bytes agree"
+        assert same > 0.99, f"only {same:.4f} of low-bit code bytes agree"
     else:
         gp.compare("cache", got["cache"], st["values"], cfg.dtype)
     toks = [(0, t) for t in (0, 51, 777, 1200, cfg.n_q - 1)]

@@ -20,7 +20,7 @@ def _bits(t):
     return t
 
 
-@pytest.mark.parametrize("key", [2, 3, 5])
+@pytest.mark.parametrize("key", [2, 3, 5, 6])
 def test_graph_replay_matches_direct_calls(gpu_lib, key):
     import torch
     from head_latent_attention_cache_amd import api

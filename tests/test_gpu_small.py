@@ -1,5 +1,5 @@
 """HIP path vs the CPU oracle on reduced workloads (whole outputs), plus the
-bit-exact checks of cache indexing, masking and INT4 storage.
+bit-exact checks of cache indexing, masking and low-bit (INT4, INT2) storage.
 
 Every call goes through the C-ABI (via the ctypes binding)."""
 import numpy as np
@@ -20,7 +20,7 @@ def _case(msg):
 def _check_all(cfg, got, ref, report=None):
     st = ref["cache"]
     written = om.slot_frames(cfg, st["newest"]) >= 0
-    if cfg.cache_fmt == "int4":
+    if cfg.cache_fmt in ("int4", "int2"):
         # codes may differ by one step where the two paths' bf16 cache values differ
         import torch
         from head_latent_attention_cache_amd import api
@@ -29,7 +29,7 @@ def _check_all(cfg, got, ref, report=None):
         api.cache_dequant(dev["dims"], dev["geom"], dev["cache"], dev["aux"], out)
         gp.compare("cache", gp.to_host(out)[:, written], st["values"][:, written], cfg.dtype, report)
         same = np.mean(got["codes"][:, written] == st["codes"][:, written])
-        assert same > 0.99, f"only {same:.4f} of INT4 code bytes agree"
+        assert same > 0.99, f"only {same:.4f} of low-bit code bytes agree"
     else:
         gp.compare("cache", got["cache"][:, written], st["values"][:, written], cfg.dtype, report)
     B, n_q, H = cfg.batch, cfg.n_q, cfg.n_heads
@@ -40,7 +40,7 @@ def _check_all(cfg, got, ref, report=None):
     gp.compare("y", got["y"], ref["y"].reshape(B, n_q, cfg.d_model), cfg.dtype, report)
 
 
-@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5, 6])
 def test_small_workload_end_to_end(gpu_lib, key):
     cfg = SMALL_CONFIGS[key]
     _case(cfg.name)
@@ -61,9 +61,10 @@ def test_partially_filled_ring_with_poisoned_slots(gpu_lib):
     _check_all(cfg, got, om.run(cfg, inp))
 
 
-def test_int4_partially_filled_ring_with_poisoned_slots(gpu_lib):
+@pytest.mark.parametrize("key", [5, 6])
+def test_lowbit_partially_filled_ring_with_poisoned_slots(gpu_lib, key):
     # packed codes and scales of the unwritten slots are 0xFF bytes (NaN scales)
-    cfg = SMALL_CONFIGS[5].replace(name="int4_ring_partial", n_frames=2, q_first=1)
+    cfg = SMALL_CONFIGS[key].replace(name=f"{SMALL_CONFIGS[key].cache_fmt}_ring_partial", n_frames=2, q_first=1)
     _case(cfg.name)
     inp = make_workload(cfg, seed=12)
     got = gp.run_gpu(cfg, inp, fill=0xFF, keep_device=True)
@@ -71,9 +72,10 @@ def test_int4_partially_filled_ring_with_poisoned_slots(gpu_lib):
     _check_all(cfg, got, ref)
 
 
-def test_int4_capacity_not_multiple_of_8(gpu_lib):
-    # 35-token frames: capacity 140 takes the generic kernel's INT4 path
-    cfg = SMALL_CONFIGS[5].replace(name="int4_cap140", grid_h=5, grid_w=7)
+@pytest.mark.parametrize("key", [5, 6])
+def test_lowbit_capacity_not_multiple_of_8(gpu_lib, key):
+    # 35-token frames: capacity 140 takes the generic kernel's low-bit path
+    cfg = SMALL_CONFIGS[key].replace(name=f"{SMALL_CONFIGS[key].cache_fmt}_cap140", grid_h=5, grid_w=7)
     _case(cfg.name)
     inp = make_workload(cfg, seed=13)
     got = gp.run_gpu(cfg, inp, keep_device=True)
@@ -115,13 +117,14 @@ def test_slot_indexing_bitexact(gpu_lib, key):
     assert np.array_equal(got["cache"][:, written, :cfg.d_c], st["values"][:, written, :cfg.d_c])
 
 
-def test_int4_quantiser_bitexact(gpu_lib):
-    cfg = SMALL_CONFIGS[5].replace(name="int4_nowrap", n_frames=4, q_first=3)
+@pytest.mark.parametrize("key", [5, 6])
+def test_lowbit_quantiser_bitexact(gpu_lib, key):
+    cfg = SMALL_CONFIGS[key].replace(name=f"{SMALL_CONFIGS[key].cache_fmt}_nowrap", n_frames=4, q_first=3)
     _case(cfg.name)
     inp = _one_hot_inputs(cfg)
     got = gp.run_gpu(cfg, inp)
     st = om.build_cache(cfg, inp)
-    ncb = cfg.d_c // 2
+    ncb = cfg.d_c * om.content_bits(cfg) // 8          # content code bytes per row
     assert np.array_equal(got["codes"][..., :ncb], st["codes"][..., :ncb])
     assert np.array_equal(got["cscale"].view(np.uint16), st["cscale"].view(np.uint16))
     # rotary part at coordinate (0, 0, 0): rotation by zero is exact on both sides
@@ -131,12 +134,13 @@ def test_int4_quantiser_bitexact(gpu_lib):
     assert np.mean(got["codes"][..., ncb:] == st["codes"][..., ncb:]) > 0.99
 
 
-def test_int4_unpack_bitexact_and_attention_on_oracle_cache(gpu_lib):
+@pytest.mark.parametrize("key", [5, 6])
+def test_lowbit_unpack_bitexact_and_attention_on_oracle_cache(gpu_lib, key):
     # the oracle writes the packed cache; the GPU reads it
     import torch
     from head_latent_attention_cache_amd import api
-    cfg = SMALL_CONFIGS[5]
-    _case("int4 unpack")
+    cfg = SMALL_CONFIGS[key]
+    _case(f"{cfg.cache_fmt} unpack")
     inp = make_workload(cfg, seed=5)
     st = om.build_cache(cfg, inp)
     dims, geom = api.dims_from_config(cfg), api.geom_from_config(cfg)
@@ -165,7 +169,7 @@ def gp_bf16(a):
     return bf16_bits_from_f32(np.asarray(a, np.float32))
 
 
-@pytest.mark.parametrize("key,q_shift", [(2, 0), (3, 0), (4, 0), (3, 1), (4, -2), (3, 4), (5, 0), (5, 1)])
+@pytest.mark.parametrize("key,q_shift", [(2, 0), (3, 0), (4, 0), (3, 1), (4, -2), (3, 4), (5, 0), (5, 1), (6, 0)])
 def test_mask_counts_bitexact(gpu_lib, key, q_shift):
     """q_abs = 0 makes every visible score 0, so exp(lse) is the number of
     visible keys exactly (and rows with none give lse = -inf)."""
@@ -213,7 +217,7 @@ def test_fully_masked_rows(gpu_lib):
     assert torch.all(torch.isneginf(lse)).item()
 
 
-@pytest.mark.parametrize("key", [2, 3, 5])
+@pytest.mark.parametrize("key", [2, 3, 5, 6])
 def test_attention_is_deterministic(gpu_lib, key):
     import torch
     from head_latent_attention_cache_amd import api

@@ -38,14 +38,14 @@ def _run(key, env_extra, out, tmp_path):
     return np.load(tmp_path / (out + ".npy"))
 
 
-@pytest.mark.parametrize("key", [2, 3, 4, 5])
+@pytest.mark.parametrize("key", [2, 3, 4, 5, 6])
 def test_split_count_invariance(gpu_lib, key, tmp_path):
     outs = [_run(key, {"MLA_ATTN_SPLITS": str(ns)}, f"s{ns}", tmp_path) for ns in (1, 2, 3)]
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) <= 2e-2
 
 
-@pytest.mark.parametrize("key", [2, 3, 4, 5])
+@pytest.mark.parametrize("key", [2, 3, 4, 5, 6])
 def test_mfma_matches_generic_kernel(gpu_lib, key, tmp_path):
     a = _run(key, {}, "mfma", tmp_path)
     g = _run(key, {"MLA_ATTN_KERNEL": "generic"}, "generic", tmp_path)
@@ -62,7 +62,7 @@ def test_split_row_kernel_on_narrow_rows(gpu_lib, key, tmp_path):
 
 
 
-@pytest.mark.parametrize("key,plan", [(3, "1:2:3"), (3, "0:1:3"), (5, "1:1:4"), (4, "2:2:3"), (2, "0:3:5")])
+@pytest.mark.parametrize("key,plan", [(3, "1:2:3"), (3, "0:1:3"), (5, "1:1:4"), (6, "1:2:3"), (4, "2:2:3"), (2, "0:3:5")])
 def test_two_group_split_plan(gpu_lib, key, plan, tmp_path):
     # row blocks [0, n_a) of every sequence with ns_a splits, the rest with
     # ns_b (the work-group order and the merge both follow the plan); the
