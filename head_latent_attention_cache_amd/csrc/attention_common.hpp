@@ -86,6 +86,14 @@ __device__ __forceinline__ u32x2_t pack4_bf16(float x0, float x1, float x2, floa
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// two floats to two bf16 in one word (round to nearest even, one
+// v_cvt_pk_bf16_f32): lo in bits 0..15, hi in bits 16..31
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 // 16-byte chunk swizzle of a key row: chunk c of key k sits at position
 // c ^ key_swizzle(k) of the row's 128 bytes.  gfx950 LDS has a 128-byte bank
 // period, so

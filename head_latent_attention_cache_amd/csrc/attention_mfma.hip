@@ -316,7 +316,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
   const int dq_key = tid >> 3, dq_cb = tid & 7;
   // split of a tile's dequantisation: DQ_QK groups during the score chain
   // (one every DQ_GAP steps), the others one every DQ_PV_GAP output MFMAs
-  constexpr int DQ_QK = 5, DQ_GAP = 5, DQ_PV_GAP = 6;
+  constexpr int DQ_QK = 5, DQ_GAP = 5, DQ_PV_GAP = 6, DQ_LEAD = 2;
+  static_assert(DQ_LEAD <= 3 && DQ_LEAD < DQ_GAP, "reads of a group's packed word run ahead of its conversion");
   struct DqPlan { const LDS_AS uint8_t *sp, *cp, *rp, *scp; LDS_AS uint8_t* tp; float keep; };
   auto dequant_plan = [&](int t, int sidx, int tbuf) -> DqPlan {
     DqPlan d;
@@ -334,27 +335,57 @@ void attn_mfma_kernel(MfmaArgs ma) {
     }
     return d;
   };
-  // 64-dim group i of this thread's key
-  auto dequant_chunk = [&](const DqPlan& d, int i) {
+  // 64-dim group i of this thread's key: the packed word and the scale are
+  // read from the staging buffer (dq_load) apart from the conversion
+  // (dq_store), so the reads can be issued a few MFMAs before their use
+  struct DqRaw { uint32_t codes, sbits; };
+  auto dq_load = [&](const DqPlan& d, int i) -> DqRaw {
     const bool content = i < DC / 64;
-    const int cbits = content ? CB : 4;
-    const uint32_t codes = !content ? *(const LDS_AS uint32_t*)d.rp
-                           : CB == 4 ? *(const LDS_AS uint32_t*)(d.cp + 8 * CB * i)
-                                     : (uint32_t)*(const LDS_AS uint16_t*)(d.cp + 8 * CB * i);
-    const uint16_t sbits = i < DC / 64 ? *(const LDS_AS uint16_t*)(d.scp + 4 * i)
-                                       : *(const LDS_AS uint16_t*)(d.sp + Q4_CODE_BYTES + Q4_CS_BYTES + dq_key * 2);
-    const float sc = d.keep != 0.f ? __half2float(__ushort_as_half(sbits)) : 0.f;
-    bf16x8_t v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // element e = field e of the little-endian word (lowest bits first),
-      // sign-extended; q * s is exact in fp32 (4 x 11 significant bits) and
-      // rounds once to bf16 (nearest even, v_cvt_pk_bf16_f32)
-      const int q = __builtin_amdgcn_sbfe((int)codes, cbits * e, cbits);
-      v[e] = (__bf16)((float)q * sc);
-    }
-    *(LDS_AS bf16x8_t*)(d.tp + i * MF_BN * 128) = v;
+    DqRaw r;
+    r.codes = !content ? *(const LDS_AS uint32_t*)d.rp
+              : CB == 4 ? *(const LDS_AS uint32_t*)(d.cp + 8 * CB * i)
+                        : (uint32_t)*(const LDS_AS uint16_t*)(d.cp + 8 * CB * i);
+    r.sbits = content ? *(const LDS_AS uint16_t*)(d.scp + 4 * i)
+                      : *(const LDS_AS uint16_t*)(d.sp + Q4_CODE_BYTES + Q4_CS_BYTES + dq_key * 2);
+    return r;
   };
+  // Every value is bf16(q * s) rounded once to nearest even from the exact
+  // product (q * s is exact in fp32: at most 4 x 11 significant bits), the
+  // same bits as converting q, multiplying and rounding.
+  auto dq_store = [&](const DqPlan& d, int i, DqRaw r) {
+    const bool content = i < DC / 64;
+    // the conversion starts here, not next to the reads (no early wait for them)
+    asm volatile("" : "+v"(r.codes), "+v"(r.sbits));
+    // a zero scale for never-written slots (their bytes are arbitrary)
+    const float s16 = __half2float(__ushort_as_half((unsigned short)r.sbits));
+    const float sc = d.keep != 0.f ? s16 : 0.f;
+    u32x4_t out;
+    if (content && CB == 2) {
+      // 2-bit codes: the four values bf16(q s), q = 0, 1, -2, -1 (code
+      // 0 .. 3, two's complement), form an 8-byte table that v_perm_b32
+      // indexes; element 4j + k is bits 2k .. 2k + 1 of byte j
+      const uint32_t lut_lo = pack2_bf16(0.f, sc), lut_hi = pack2_bf16(-2.f * sc, -sc);
+      const uint32_t w = r.codes | (r.codes << 14);   // code 2p + 1 copied to bit 4p + 16
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // codes 2p, 2p + 1 at bits 0 and 16, then byte selectors (2c, 2c + 1) per half
+        const uint32_t t = (w >> (4 * p)) & 0x00030003u;
+        out[p] = __builtin_amdgcn_perm(lut_hi, lut_lo, t * 0x202u + 0x01000100u);
+      }
+    } else {
+      // 4-bit codes: offset binary (code ^ 8 = q + 8) in single bytes, byte
+      // to float conversion, then q s = (q + 8) s - 8 s in one exact FMA
+      const uint32_t ev = (r.codes & 0x0F0F0F0Fu) ^ 0x08080808u;          // elements 0, 2, 4, 6
+      const uint32_t od = ((r.codes >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1, 3, 5, 7
+      const float off = -8.f * sc;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        out[p] = pack2_bf16(fmaf((float)((ev >> (8 * p)) & 0xFFu), sc, off),
+                            fmaf((float)((od >> (8 * p)) & 0xFFu), sc, off));
+    }
+    *(LDS_AS u32x4_t*)(d.tp + i * MF_BN * 128) = out;
+  };
+  auto dequant_chunk = [&](const DqPlan& d, int i) { dq_store(d, i, dq_load(d, i)); };
   auto dequant = [&](int t, int sidx, int tbuf) {
     const DqPlan d = dequant_plan(t, sidx, tbuf);
 #pragma unroll 3
@@ -386,6 +417,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     };
     constexpr int KPF = 4;
     bf16x8_t kb[KPF], qb[KPF];
+    DqRaw raw[DQ_QK];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
     // scheduling barriers keep every read KPF MFMAs ahead of its use
@@ -411,9 +443,12 @@ void attn_mfma_kernel(MfmaArgs ma) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             lds_barrier();
           }
-          // groups 0 .. DQ_QK - 1 here, one every DQ_GAP steps; the rest with the output MFMAs
+          // groups 0 .. DQ_QK - 1 here, one every DQ_GAP steps (its packed
+          // word read DQ_LEAD steps earlier); the rest with the output MFMAs
+          const int rel = ks + DQ_LEAD - 2 * NDB - 1;
+          if (rel >= 0 && rel % DQ_GAP == 0 && rel / DQ_GAP < DQ_QK) raw[rel / DQ_GAP] = dq_load(dqp, rel / DQ_GAP);
           if (ks > 2 * NDB && (ks - 2 * NDB - 1) % DQ_GAP == 0 && (ks - 2 * NDB - 1) / DQ_GAP < DQ_QK)
-            dequant_chunk(dqp, (ks - 2 * NDB - 1) / DQ_GAP);
+            dq_store(dqp, (ks - 2 * NDB - 1) / DQ_GAP, raw[(ks - 2 * NDB - 1) / DQ_GAP]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -479,6 +514,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     // runs while the matrix core is busy (scheduling barriers pin the order)
     float p[16];
     float lsum = 0.f;
+    DqRaw praw{0u, 0u};
 #pragma unroll
     for (int i = 0; i < 2 * NDB * MF_WAVES; ++i) {
       const int j = i / (NDB * MF_WAVES), d = (i / MF_WAVES) % NDB, r = i % MF_WAVES;
@@ -489,7 +525,9 @@ void attn_mfma_kernel(MfmaArgs ma) {
       o[d * MF_WAVES + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, f.pfr[j][r], o[d * MF_WAVES + r], 0, 0, 0);
       if constexpr (Q4) {
         static_assert(DQ_PV_GAP * (NCG - DQ_QK) <= 2 * NDB * MF_WAVES, "dequantisation steps");
-        if (do_dq && i % DQ_PV_GAP == 3 && DQ_QK + i / DQ_PV_GAP < NCG) dequant_chunk(dqp, DQ_QK + i / DQ_PV_GAP);
+        if (do_dq && i % DQ_PV_GAP == 3 - DQ_LEAD && DQ_QK + i / DQ_PV_GAP < NCG)
+          praw = dq_load(dqp, DQ_QK + i / DQ_PV_GAP);
+        if (do_dq && i % DQ_PV_GAP == 3 && DQ_QK + i / DQ_PV_GAP < NCG) dq_store(dqp, DQ_QK + i / DQ_PV_GAP, praw);
       }
       if ((i & 1) == 0 && i / 2 < 16) {
         const int e = i / 2;
