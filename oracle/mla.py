@@ -197,6 +197,39 @@ def given_cache(st, cfg, cache_c, cache_r):
 
 
 # ---------------------------------------------------------------------------
+# re-rotation of cached rotary keys: [MLA topics, Irminsul abstract] (an MLA
+# row is a position-free content latent plus a small rotary key that a change
+# of position corrects in closed form) and [MLA topics, the RedKnot
+# head-aware reuse abstract] (relocating content computed at another
+# position).  Rotations by angles
+# proportional to the coordinate compose: R(p + d) = R(d) R(p), so a key
+# stored at coordinates p is moved to p + d by rotating it with R(d).
+# ---------------------------------------------------------------------------
+def rope_shift(st, cfg, delta, slot_begin: int, n_slots: int):
+    """Rotate the stored rotary keys of slots [slot_begin, slot_begin + n_slots)
+    of every sequence b by the coordinate shift ``delta[b]`` ((t, h, w) for
+    3D; 1D uses ``delta[b][0]``, a position shift), as if each of those
+    tokens had been appended that much further along.  The rotated key is
+    rounded to the cache format (low-bit: rounded to bf16, then re-quantised
+    to INT4 with a new per-token scale); the content latent is untouched and a
+    zero shift leaves the rows unchanged."""
+    delta = np.asarray(delta, dtype=np.int64).reshape(cfg.batch, 3)
+    sl = slice(slot_begin, slot_begin + n_slots)
+    for b in range(cfg.batch):
+        if not np.any(delta[b]):
+            continue
+        d = delta[b, :cfg.rope_dims].astype(np.float64)
+        k = rope_rotate(st["values"][b, sl, cfg.d_c:], d, cfg)
+        k = round_to_storage(k, cfg.dtype)
+        if cfg.cache_fmt in ("int4", "int2"):
+            codes, scale = int4.quantize_groups(k, cfg.d_r)
+            st["codes"][b, sl, cfg.d_c * content_bits(cfg) // 8:] = int4.pack_nibbles(codes)
+            st["rscale"][b, sl] = scale[..., 0]
+            k = int4.dequantize_groups(codes, scale, cfg.d_r)
+        st["values"][b, sl, cfg.d_c:] = k
+
+
+# ---------------------------------------------------------------------------
 # absorbed query: [MLA concept, Low-rank joint compression] (q.(W^UK c) =
 # ((W^UK)^T q).c, so W^UK folds into the query side)
 # ---------------------------------------------------------------------------

@@ -486,6 +486,97 @@ def check_int2():
     return float(bad)
 
 
+def check_rope_shift():
+    """Re-rotation of cached rotary keys, against properties fixed by the
+    composition of rotations: rows appended at p and shifted by d equal rows
+    appended at p + d (up to the storage rounding); attention is unchanged when
+    every key and the query move by the same d; a zero shift, the content
+    latent and the slots outside the range are untouched bit for bit; d then
+    -d returns the keys; low-bit rows re-quantise within half a step."""
+    errs = []
+    rng = np.random.default_rng(17)
+    for cfg in (_tiny_video(), TINIER_BLOCK, TINY_DECODE.replace(name="tiny_dec_f32", dtype="f32")):
+        inp = make_workload(cfg, seed=4)
+        st = om.build_cache(cfg, inp)
+        ref = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in st.items()}
+        delta = rng.integers(-9, 10, (cfg.batch, 3))
+        delta[0, 1:] = 0
+        if cfg.batch > 1:
+            delta[1] = 0                     # a sequence with a zero shift
+        om.rope_shift(st, cfg, delta, 0, cfg.capacity)
+        # unchanged: content, zero-shift sequences
+        errs.append(float(np.any(st["values"][..., :cfg.d_c] != ref["values"][..., :cfg.d_c])))
+        if cfg.batch > 1:
+            errs.append(float(np.any(st["values"][1] != ref["values"][1])))
+        # appended at p, shifted by d == appended at p + d: the stored key
+        # rotated by d against the unrotated projection rotated at p + d
+        frames = om.slot_frames(cfg, ref["newest"])
+        P = cfg.tokens_per_frame
+        y = None
+        if not cfg.cache_given:
+            x = om.as_f64(inp["x"])
+            w = om.as_f64(inp["w_dkr"])
+            for s_ in range(cfg.capacity):
+                f = frames[s_]
+                if f < 0:
+                    continue
+                yr = x[:, f, s_ % P] @ w[cfg.d_c:].T
+                coords = om.token_coords(cfg, f, s_ % P) + delta[:, :cfg.rope_dims]
+                want = om.rope_rotate(yr, coords, cfg)
+                got = st["values"][:, s_, cfg.d_c:]
+                errs.append(np.max(np.abs(got - want)) / max(1.0, np.max(np.abs(want))) / 1e-5)
+        # shift back: the original keys up to the storage rounding
+        st2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in st.items()}
+        om.rope_shift(st2, cfg, -delta, 0, cfg.capacity)
+        errs.append(np.max(np.abs(st2["values"] - ref["values"])) / 1e-5)
+        # attention with every key and the query moved by the same shift
+        if cfg.batch > 1:
+            continue
+        w_uk, w_uv = om.as_f64(inp["w_uk"]), om.as_f64(inp["w_uv"])
+        q_nope, q_rope = om.as_f64(inp["q_nope"]), om.as_f64(inp["q_rope"])
+        i = np.arange(cfg.n_q)
+        c0 = om.token_coords(cfg, cfg.q_first + i // P, i % P)[None, :, None, :]
+        q0 = om.rope_rotate(q_rope, c0, cfg)
+        q1 = om.rope_rotate(q_rope, c0 + delta[0, :cfg.rope_dims], cfg)
+        _, o0, l0 = om.attend(cfg, ref, q_nope, q0, w_uk, w_uv, cfg.q_first)
+        _, o1, l1 = om.attend(cfg, st, q_nope, q1, w_uk, w_uv, cfg.q_first)
+        errs.append(np.max(np.abs(o1 - o0)) / 1e-5)
+        errs.append(np.max(np.abs(l1 - l0)) / 1e-5)
+    # slot range: only [3, 3 + 5) moves
+    cfg = _tiny_video()
+    st = om.build_cache(cfg, make_workload(cfg, seed=5))
+    ref = st["values"].copy()
+    om.rope_shift(st, cfg, np.array([[2, 1, -1]]), 3, 5)
+    out = np.ones(cfg.capacity, bool)
+    out[3:8] = False
+    errs.append(float(np.any(st["values"][:, out] != ref[:, out])))
+    errs.append(float(not np.any(st["values"][:, 3:8, cfg.d_c:] != ref[:, 3:8, cfg.d_c:])))
+    # low-bit: content codes and scales untouched; the re-quantised rotary key
+    # is within half a step (plus the bf16 rounding) of the rotated key; amax -> +-7
+    for lcfg in (TINY_INT4, TINY_INT2):
+        st = om.build_cache(lcfg, make_workload(lcfg, seed=6))
+        ref = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in st.items()}
+        d = np.array([[3, -1, 2]])
+        om.rope_shift(st, lcfg, d, 0, lcfg.capacity)
+        nb = lcfg.d_c * om.content_bits(lcfg) // 8
+        errs.append(float(np.any(st["codes"][..., :nb] != ref["codes"][..., :nb])))
+        errs.append(float(np.any(st["cscale"] != ref["cscale"])))
+        want = om.rope_rotate(ref["values"][..., lcfg.d_c:], d[0].astype(np.float64), lcfg)
+        s_new = st["rscale"].astype(np.float64)[..., None]
+        bound = s_new / 2 + np.abs(want) * 2.0 ** -8 + 1e-12
+        errs.append(float(np.any(np.abs(st["values"][..., lcfg.d_c:] - want) > bound)))
+        stored = oi.dequantize_cache_rows(st["codes"], st["cscale"], st["rscale"], lcfg.d_c, 32,
+                                          om.content_bits(lcfg))
+        errs.append(float(np.any(stored != st["values"])))
+        codes = oi.unpack_nibbles(st["codes"][..., nb:])
+        errs.append(float(np.any(np.max(np.abs(codes), axis=-1)[st["rscale"] > 0] != 7)))
+        # a zero shift leaves every byte
+        st3 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in ref.items()}
+        om.rope_shift(st3, lcfg, np.zeros((1, 3), int), 0, lcfg.capacity)
+        errs.append(float(any(np.any(st3[k] != ref[k]) for k in ("codes", "cscale", "rscale", "values"))))
+    return float(max(errs))
+
+
 CHECKS = {
     "bruteforce": (check_bruteforce, 1e-12),
     "absorption": (check_absorption, 1e-12),
@@ -498,6 +589,7 @@ CHECKS = {
     "bf16_rounding": (check_bf16_rounding, 0.0),
     "int4": (check_int4, 0.0),
     "int2": (check_int2, 0.0),
+    "rope_shift": (check_rope_shift, 0.5),
 }
 
 

@@ -18,7 +18,26 @@ _orig = {
     "softmax_scale": om.softmax_scale, "query_coords": om.query_coords,
     "quantize_groups": oi.quantize_groups, "pack_nibbles": oi.pack_nibbles,
     "unpack_nibbles": oi.unpack_nibbles, "pack_crumbs": oi.pack_crumbs, "unpack_crumbs": oi.unpack_crumbs,
+    "rope_shift": om.rope_shift,
 }
+
+
+def _shift_backwards(st, cfg, delta, slot_begin, n_slots):
+    _orig["rope_shift"](st, cfg, -np.asarray(delta), slot_begin, n_slots)
+
+
+def _shift_axes_reversed(st, cfg, delta, slot_begin, n_slots):
+    _orig["rope_shift"](st, cfg, np.asarray(delta).reshape(-1, 3)[:, ::-1], slot_begin, n_slots)
+
+
+def _shift_one_slot_late(st, cfg, delta, slot_begin, n_slots):
+    _orig["rope_shift"](st, cfg, delta, slot_begin + 1, n_slots)
+
+
+def _shift_codes_kept(st, cfg, delta, slot_begin, n_slots):
+    keep = {k: st[k].copy() for k in ("codes", "rscale") if k in st}
+    _orig["rope_shift"](st, cfg, delta, slot_begin, n_slots)
+    st.update(keep)
 
 
 def _rope_sign(u, coords, cfg):
@@ -187,6 +206,10 @@ MUTANTS = {
     "int2_crumbs_reversed": [(oi, "pack_crumbs", _crumbs_reversed_pack),
                              (oi, "unpack_crumbs", _crumbs_reversed_unpack)],
     "int4_nibbles_swapped": [(oi, "pack_nibbles", _pack_swapped), (oi, "unpack_nibbles", _unpack_swapped)],
+    "rope_shift_backwards": [(om, "rope_shift", _shift_backwards)],
+    "rope_shift_axes_reversed": [(om, "rope_shift", _shift_axes_reversed)],
+    "rope_shift_slot_range_off_by_one": [(om, "rope_shift", _shift_one_slot_late)],
+    "rope_shift_low_bit_codes_kept": [(om, "rope_shift", _shift_codes_kept)],
 }
 
 
