@@ -210,6 +210,16 @@ def cache_dequant(dims, geom, cache, cache_aux, out):
     check(lib.mla_cache_dequant(_rd(dims), _rd(geom), _stream(), _ptr(cache), _ptr(cache_aux), _ptr(out)))
 
 
+def cache_rope_shift(dims, geom, delta, slot_begin, n_slots, cache, cache_aux):
+    """Rotate the rotary keys of slots [slot_begin, slot_begin + n_slots) of
+    every sequence by the coordinate shift delta [B, 3] int32 (device)."""
+    lib = load()
+    _check_cache(dims, geom, cache, cache_aux)
+    _need(delta, "delta", torch.int32, geom.batch * 3)
+    check(lib.mla_cache_rope_shift(_rd(dims), _rd(geom), _stream(), _ptr(delta), int(slot_begin), int(n_slots),
+                                   _ptr(cache), _ptr(cache_aux)))
+
+
 def raw_lib():
     """The loaded ctypes library (for callers passing their own pointers)."""
     return _lib.load()

@@ -366,4 +366,22 @@ mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* s
   return hip_status(launch_dequant(d, g, geom->batch, cache, cache_aux, out, st), st, "cache dequant");
 }
 
+mla_status mla_cache_rope_shift(const mla_dims* dims, const mla_geom* geom, void* stream, const int32_t* delta,
+                                int32_t slot_begin, int32_t n_slots, void* cache, void* cache_aux) {
+  Dims d;
+  Geo g;
+  CHECK(check_dims(dims, &d));
+  CHECK(check_geom(geom, d, &g));
+  if (slot_begin < 0 || n_slots < 0 || (int64_t)slot_begin + n_slots > g.capacity)
+    return fail(MLA_ERR_INVALID_ARG, "slots [%d, %d + %d) must lie inside [0, capacity = %d)", slot_begin,
+                slot_begin, n_slots, g.capacity);
+  if (geom->batch == 0 || n_slots == 0) return MLA_OK;
+  NEED_PTR(delta);
+  NEED_PTR(cache);
+  if (lowbit_cache(d)) NEED_PTR(cache_aux);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_rope_shift(d, g, geom->batch, delta, slot_begin, n_slots, cache, cache_aux, st), st,
+                    "rotary key shift");
+}
+
 }  // extern "C"

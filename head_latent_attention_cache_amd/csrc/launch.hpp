@@ -41,6 +41,8 @@ hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_r
                          const int* q_first, void* q_abs, hipStream_t st);
 hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* cache, const void* aux,
                           float* out, hipStream_t st);
+hipError_t launch_rope_shift(const Dims& d, const Geo& g, int batch, const int* delta, int slot_begin,
+                             int n_slots, void* cache, void* aux, hipStream_t st);
 hipError_t launch_attn_simt(const AttnArgs& a, hipStream_t st);
 bool attn_mfma_supported(const Dims& d, const Geo& g);
 size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows);

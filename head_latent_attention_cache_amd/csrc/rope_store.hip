@@ -192,6 +192,73 @@ __global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// re-rotation of stored rotary keys by a coordinate shift ("Multi-Head Latent
+// Attention" topic page, Irminsul abstract: the rotary part of a row is
+// corrected in closed form when its token moves, the content latent is
+// position-free).  Rotations by angles proportional to the coordinate
+// compose, R(p + delta) = R(delta) R(p), so every row of a sequence turns by
+// the same table.  grid (ceil(n_slots / SHIFT_ROWS), B): one rotary pair per
+// thread and row; low-bit rows are dequantised, rotated, rounded to bf16 and
+// re-quantised (new per-token scale) once the work-group holds them.  A
+// shift that is zero in the coordinates the embedding uses returns at once.
+// ---------------------------------------------------------------------------
+constexpr int SHIFT_ROWS = 16;
+
+template <typename T, bool LOWBIT>
+__global__ void rope_shift_kernel(Dims d, Geo g, int batch, const int* __restrict__ delta, int slot_begin,
+                                  int n_slots, void* __restrict__ cache, __half* __restrict__ aux) {
+  extern __shared__ float smem[];
+  float* cosv = smem;                 // [d_r / 2]
+  float* sinv = smem + d.d_r / 2;     // [d_r / 2]
+  float* rows = smem + d.d_r;         // low-bit: [SHIFT_ROWS][d_r] rotated keys
+  const int b = blockIdx.y;
+  const int dt = delta[3 * b], dh = delta[3 * b + 1], dw = delta[3 * b + 2];
+  if (dt == 0 && (d.rope_dims == 1 || (dh == 0 && dw == 0))) return;
+  const double coord[3] = {(double)dt, (double)dh, (double)dw};
+  rope_table(d, coord, cosv, sinv);
+  __syncthreads();
+  const int s0 = slot_begin + blockIdx.x * SHIFT_ROWS;
+  const int nrow = min(SHIFT_ROWS, slot_begin + n_slots - s0);
+  const int npair = d.d_r / 2;
+  const size_t rs_base = (size_t)batch * g.capacity * (d.d_c / 32);   // per-token rotary scales
+  for (int e = threadIdx.x; e < nrow * npair; e += blockDim.x) {
+    const int r = e / npair, p = e % npair;
+    const size_t srow = (size_t)b * g.capacity + s0 + r;
+    float x0, x1;
+    if (!LOWBIT) {
+      const T* k = (const T*)cache + srow * d.d_qk + d.d_c;
+      x0 = Elem<T>::load(k, 2 * p);
+      x1 = Elem<T>::load(k, 2 * p + 1);
+    } else {
+      // INT4 rotary codes: element 2p in the low nibble of byte p
+      const uint8_t* codes = (const uint8_t*)cache + srow * code_row_bytes(d) + d.d_c * content_bits(d) / 8;
+      const int byte = codes[p];
+      const float s = __half2float(aux[rs_base + srow]);
+      x0 = (float)(((byte & 15) ^ 8) - 8) * s;
+      x1 = (float)(((byte >> 4) ^ 8) - 8) * s;
+    }
+    const float c = cosv[p], sn = sinv[p];
+    const float r0 = round_to<T>(x0 * c - x1 * sn), r1 = round_to<T>(x0 * sn + x1 * c);
+    if (!LOWBIT) {
+      T* k = (T*)cache + srow * d.d_qk + d.d_c;
+      Elem<T>::store(k, 2 * p, r0);
+      Elem<T>::store(k, 2 * p + 1, r1);
+    } else {
+      rows[r * d.d_r + 2 * p] = r0;
+      rows[r * d.d_r + 2 * p + 1] = r1;
+    }
+  }
+  if (LOWBIT) {
+    __syncthreads();   // every code of these rows is read before any is rewritten
+    for (int r = threadIdx.x; r < nrow; r += blockDim.x) {
+      const size_t srow = (size_t)b * g.capacity + s0 + r;
+      uint8_t* codes = (uint8_t*)cache + srow * code_row_bytes(d) + d.d_c * content_bits(d) / 8;
+      quant_lowbit(rows + r * d.d_r, d.d_r, 4, codes, aux + rs_base + srow);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
@@ -232,6 +299,19 @@ hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* ca
     dequant_kernel<bf16_t, false><<<blocks, 256, 0, st>>>(d, g, batch, cache, nullptr, out);
   else
     dequant_kernel<float, false><<<blocks, 256, 0, st>>>(d, g, batch, cache, nullptr, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_shift(const Dims& d, const Geo& g, int batch, const int* delta, int slot_begin,
+                             int n_slots, void* cache, void* aux, hipStream_t st) {
+  dim3 grid((n_slots + SHIFT_ROWS - 1) / SHIFT_ROWS, batch);
+  const size_t shm = (size_t)d.d_r * sizeof(float) * (lowbit_cache(d) ? 1 + SHIFT_ROWS : 1);
+  if (lowbit_cache(d))
+    rope_shift_kernel<bf16_t, true><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, cache, (__half*)aux);
+  else if (d.dtype == MLA_BF16)
+    rope_shift_kernel<bf16_t, false><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, cache, nullptr);
+  else
+    rope_shift_kernel<float, false><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, cache, nullptr);
   return hipGetLastError();
 }
 

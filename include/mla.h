@@ -205,6 +205,33 @@ mla_status mla_unabsorb_out(const mla_dims* dims, const mla_geom* geom, void* st
                             const void* o_lat, const void* w_uv, const void* w_o,
                             void* o_heads, void* y);
 
+/*
+ * mla_cache_rope_shift: [MLA topics, Irminsul abstract] (the rotary key of a
+ * cached row is corrected in closed form when its token moves; the content
+ * latent carries no position) and [MLA topics, the RedKnot head-aware reuse
+ * abstract] (content computed at one position is relocated to another).
+ * Rotations by angles proportional to the coordinate compose,
+ * R(p + delta) = R(delta) R(p), so for every sequence b and slot s in
+ * [slot_begin, slot_begin + n_slots):
+ *     cache_row[b, s, d_c : d_c + d_r]  <-  R(delta[b]) cache_row[b, s, d_c : d_c + d_r]
+ * i.e. the key as if the token had been appended delta[b] further along
+ * (pair i of a band of width w turns by delta_axis * theta^(-2i/w)).
+ *   delta  [B, 3] int32 (device): the shift of (t, h, w); rope_dims = 1 uses
+ *          delta[b, 0] (a position shift) and ignores the rest
+ *   cache, cache_aux: see "Cache storage"; the content latent and every other
+ *          slot are left untouched.  Dense: rotated in fp32, rounded to
+ *          dims->dtype.  Low-bit: the INT4 rotary codes are dequantised,
+ *          rotated, rounded to bf16 and re-quantised with a new per-token
+ *          scale.  A shift that is zero in the coordinates used leaves the
+ *          rows unchanged bit for bit.
+ * Errors: the slot range must lie inside [0, capacity) (MLA_ERR_INVALID_ARG).
+ * The caller owns the positions: queries that should see the moved keys at
+ * their new offsets are absorbed at positions shifted by the same delta.
+ */
+mla_status mla_cache_rope_shift(const mla_dims* dims, const mla_geom* geom, void* stream,
+                                const int32_t* delta, int32_t slot_begin, int32_t n_slots,
+                                void* cache, void* cache_aux);
+
 /* Inspection utility (not on the hot path): cache rows as float [B, capacity, d_c + d_r]. */
 mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* stream,
                              const void* cache, const void* cache_aux, float* out);

@@ -212,13 +212,14 @@ def rope_shift(st, cfg, delta, slot_begin: int, n_slots: int):
     tokens had been appended that much further along.  The rotated key is
     rounded to the cache format (low-bit: rounded to bf16, then re-quantised
     to INT4 with a new per-token scale); the content latent is untouched and a
-    zero shift leaves the rows unchanged."""
+    shift that is zero in the coordinates the embedding uses (1D: the first)
+    leaves the rows unchanged."""
     delta = np.asarray(delta, dtype=np.int64).reshape(cfg.batch, 3)
     sl = slice(slot_begin, slot_begin + n_slots)
     for b in range(cfg.batch):
-        if not np.any(delta[b]):
-            continue
         d = delta[b, :cfg.rope_dims].astype(np.float64)
+        if not np.any(d):
+            continue
         k = rope_rotate(st["values"][b, sl, cfg.d_c:], d, cfg)
         k = round_to_storage(k, cfg.dtype)
         if cfg.cache_fmt in ("int4", "int2"):

@@ -164,3 +164,21 @@ def test_unsupported_widths(lib):
     fake = ctypes.c_void_p(0x1000)
     assert lib.mla_attention(ctypes.byref(d), ctypes.byref(g), None, 1, fake, fake, fake, fake, None,
                              fake, None, None, 0) == _lib.MLA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("begin,count", [(-1, 4), (0, -1), (0, 10 ** 6), (5, 10 ** 6)])
+def test_rope_shift_slot_range_rejected(lib, begin, count):
+    cfg = SMALL_CONFIGS[3]
+    d, g = _dims(cfg), _geom(cfg)
+    fake = ctypes.c_void_p(0x1000)       # never dereferenced: validation fails first
+    st = lib.mla_cache_rope_shift(ctypes.byref(d), ctypes.byref(g), None, fake, begin, count, fake, None)
+    assert st == _lib.MLA_ERR_INVALID_ARG
+    assert b"slots" in lib.mla_last_error()
+
+
+def test_rope_shift_needs_aux_for_lowbit(lib):
+    cfg = SMALL_CONFIGS[5]
+    d, g = _dims(cfg), _geom(cfg)
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.mla_cache_rope_shift(ctypes.byref(d), ctypes.byref(g), None, fake, 0, 4, fake, None)
+    assert st == _lib.MLA_ERR_INVALID_ARG
