@@ -40,6 +40,7 @@ class MLAConfig:
     cache_fmt: str = "dense"   # "dense", "int4", or "int2" (INT2 content latent, INT4 rotary key)
     cache_given: bool = False  # decode: earlier positions' rows are given; only the
                                # newest frame is appended
+    d_cq: int = 1536     # low-rank query latent width (load-time fold of W^UQ and W^UK)
 
     # ---- derived -------------------------------------------------------
     @property
@@ -81,7 +82,7 @@ TINY_VIDEO = MLAConfig(
     name="tiny_video_f32", batch=1, n_heads=4, d_model=128, d_nope=32, d_v=32,
     d_c=64, d_r=16, rope_dims=3, bands=(4, 6, 6), theta=10000.0,
     grid_h=4, grid_w=4, window=3, frames_per_block=1,
-    n_frames=3, q_first=2, q_frames=1, dtype="f32")
+    n_frames=3, q_first=2, q_frames=1, dtype="f32", d_cq=40)
 
 LLM_DECODE = MLAConfig(
     name="llm_decode_bf16", batch=32, n_heads=128, d_model=16384, d_nope=128,
@@ -116,10 +117,10 @@ SMALL_CONFIGS = {
     1: TINY_VIDEO,
     # 300 written of 320 slots: poisoned unwritten tail, ragged key tiles
     2: LLM_DECODE.replace(name="llm_decode_small", batch=3, d_model=256,
-                          window=320, n_frames=300, q_first=299),
+                          window=320, n_frames=300, q_first=299, d_cq=200),
     # 35-token frames, ring of 4 frames wrapped once (frames 0..5 appended)
     3: VIDEO_CHUNK.replace(name="video_chunk_small", d_model=512, grid_h=5,
-                           grid_w=7, window=4, n_frames=6, q_first=5),
+                           grid_w=7, window=4, n_frames=6, q_first=5, d_cq=264),
     # frame-causal 3-frame chunk over a wrapped 6-frame ring, d_r = 512
     4: LONG_VIDEO.replace(name="long_video_small", n_heads=8, d_model=512,
                           grid_h=3, grid_w=5, window=6, n_frames=9, q_first=6),

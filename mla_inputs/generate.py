@@ -28,9 +28,15 @@ x_new      [B, 1, P, d_model]       hidden state of the newest   1
                                     frame, appended by the step
 q_nope     [B, n_q, H, d_nope]      content queries              1
 q_rope     [B, n_q, H, d_r]         rotary queries (unrotated)   1
+c_q        [B, n_q, d_cq]           low-rank query latents       1
+                                    (optional part)
+w_uq       [H * d_nope, d_cq]       query up-projection,         1/sqrt(d_cq)
+                                    output-feature major
+                                    (optional part)
 =========  =======================  ===========================  =============
 
 ``x`` is only drawn for workloads that build their cache by appending frames.
+Optional parts (``c_q``, ``w_uq``) are drawn only when asked for by name.
 Decode workloads are given the cache of every earlier position
 (``cache_c``/``cache_r``) and append only the newest token from ``x_new``.
 """
@@ -43,7 +49,9 @@ from .configs import MLAConfig
 _PART_IDS = {
     "w_dkr": 1, "w_uk": 2, "w_uv": 3, "w_o": 4, "x": 5,
     "cache_c": 6, "cache_r": 7, "q_nope": 8, "q_rope": 9, "x_new": 10,
+    "c_q": 11, "w_uq": 12,
 }
+OPTIONAL_PARTS = ("c_q", "w_uq")
 
 
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
@@ -68,6 +76,8 @@ def part_shapes(cfg: MLAConfig) -> dict:
         "q_rope": ((B, cfg.n_q, H, cfg.d_r), 1.0),
     }
     shapes["w_dkr"] = ((cfg.d_c + cfg.d_r, cfg.d_model), 1.0 / np.sqrt(cfg.d_model))
+    shapes["c_q"] = ((B, cfg.n_q, cfg.d_cq), 1.0)
+    shapes["w_uq"] = ((H * cfg.d_nope, cfg.d_cq), 1.0 / np.sqrt(cfg.d_cq))
     if cfg.cache_given:
         L = (cfg.n_frames - 1) * P
         shapes["cache_c"] = ((B, L, cfg.d_c), 1.0)
@@ -91,5 +101,5 @@ def make_part(cfg: MLAConfig, name: str, seed: int = 0) -> np.ndarray:
 
 def make_workload(cfg: MLAConfig, seed: int = 0, parts=None) -> dict:
     """Return {part name: array}; float32 arrays or bf16 bit patterns (uint16)."""
-    names = list(part_shapes(cfg)) if parts is None else list(parts)
+    names = [n for n in part_shapes(cfg) if n not in OPTIONAL_PARTS] if parts is None else list(parts)
     return {n: make_part(cfg, n, seed) for n in names}

@@ -249,6 +249,36 @@ def absorb_query(cfg, q_nope, q_rope, w_uk, q_first: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# low-rank query with the key up-projection folded in at load time:
+# [MLA concept, Low-rank joint compression]: with a query latent c^Q and its
+# up-projection W^UQ, q_t . k_s = (W^UQ c^Q_t) . (W^UK c^KV_s)
+# = c^Q_t^T (W^UQ^T W^UK) c^KV_s, so the product of the two up-projections
+# can be formed once when the weights are loaded.
+# ---------------------------------------------------------------------------
+def query_up(cfg, c_q, w_uq) -> np.ndarray:
+    """Per-head content queries q_nope [..., H, d_nope] of query latents
+    c_q [..., d_cq]: q_nope[.., h, i] = sum_j w_uq[h d_nope + i, j] c_q[.., j]."""
+    q = np.asarray(c_q, np.float64) @ np.asarray(w_uq, np.float64).T
+    return q.reshape(q.shape[:-1] + (cfg.n_heads, cfg.d_nope))
+
+
+def fold_query_weights(cfg, w_uq, w_uk) -> np.ndarray:
+    """w_fold [H, d_c, d_cq], w_fold[h] = w_uk[h] . W^UQ_h with W^UQ_h the
+    rows h d_nope .. (h + 1) d_nope - 1 of w_uq (so that w_fold[h] . c_q is
+    (W^UK_h)^T W^UQ_h c_q, the absorbed content query of head h)."""
+    wq = np.asarray(w_uq, np.float64).reshape(cfg.n_heads, cfg.d_nope, -1)
+    return np.matmul(np.asarray(w_uk, np.float64), wq)
+
+
+def absorb_query_folded(cfg, c_q, q_rope, w_fold, q_first: int) -> np.ndarray:
+    """q_abs[b,t,h] = [ w_fold[h] . c_q[b,t] ; RoPE(q_rope) ] -> [B, n_q, H, d_c + d_r]."""
+    q_lat = np.einsum("btj,hcj->bthc", np.asarray(c_q, np.float64), np.asarray(w_fold, np.float64))
+    coords = query_coords(cfg, q_first)[None, :, None, :]
+    q_rot = rope_rotate(q_rope, coords, cfg)
+    return np.concatenate([q_lat, q_rot], axis=-1)
+
+
+# ---------------------------------------------------------------------------
 # attention with materialised per-head keys/values (the plain definition):
 # [MLA concept, The RoPE problem, and the decoupled fix] each head's query and
 # key join a content part and the rotary part shared by all heads;

@@ -577,6 +577,45 @@ def check_rope_shift():
     return float(max(errs))
 
 
+def check_query_fold():
+    """Load-time fold of the query and key up-projections: scalar loops on a
+    tiny shape for the fold and the query up-projection, then the
+    associativity (W^UK_h)^T (W^UQ_h c) = ((W^UK_h)^T W^UQ_h) c on workloads:
+    the folded absorbed query equals the absorbed up-projected query."""
+    errs = []
+    rng = np.random.default_rng(19)
+    cfg = TINIER.replace(name="fold", d_cq=5)
+    H, dn, dc, dq = cfg.n_heads, cfg.d_nope, cfg.d_c, cfg.d_cq
+    w_uq = rng.standard_normal((H * dn, dq))
+    w_uk = rng.standard_normal((H, dc, dn))
+    c_q = rng.standard_normal((2, 3, dq))
+    fold = om.fold_query_weights(cfg, w_uq, w_uk)
+    for h in range(H):
+        for a in range(dc):
+            for j in range(dq):
+                v = 0.0
+                for i in range(dn):
+                    v += float(w_uk[h, a, i]) * float(w_uq[h * dn + i, j])
+                errs.append(abs(fold[h, a, j] - v))
+    up = om.query_up(cfg, c_q, w_uq)
+    for b in range(2):
+        for t in range(3):
+            for h in range(H):
+                for i in range(dn):
+                    v = sum(float(c_q[b, t, j]) * float(w_uq[h * dn + i, j]) for j in range(dq))
+                    errs.append(abs(up[b, t, h, i] - v))
+    for key in (1, 2, 3):
+        from mla_inputs import SMALL_CONFIGS
+        c = SMALL_CONFIGS[key]
+        inp = make_workload(c, seed=3, parts=("c_q", "w_uq", "w_uk", "q_rope"))
+        cq, wq, wk = om.as_f64(inp["c_q"]), om.as_f64(inp["w_uq"]), om.as_f64(inp["w_uk"])
+        qr = om.as_f64(inp["q_rope"])
+        a = om.absorb_query_folded(c, cq, qr, om.fold_query_weights(c, wq, wk), c.q_first)
+        b_ = om.absorb_query(c, om.query_up(c, cq, wq), qr, wk, c.q_first)
+        errs.append(np.max(np.abs(a - b_)) / np.max(np.abs(b_)))
+    return float(max(errs))
+
+
 CHECKS = {
     "bruteforce": (check_bruteforce, 1e-12),
     "absorption": (check_absorption, 1e-12),
@@ -590,6 +629,7 @@ CHECKS = {
     "int4": (check_int4, 0.0),
     "int2": (check_int2, 0.0),
     "rope_shift": (check_rope_shift, 0.5),
+    "query_fold": (check_query_fold, 1e-12),
 }
 
 

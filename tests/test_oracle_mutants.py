@@ -18,8 +18,24 @@ _orig = {
     "softmax_scale": om.softmax_scale, "query_coords": om.query_coords,
     "quantize_groups": oi.quantize_groups, "pack_nibbles": oi.pack_nibbles,
     "unpack_nibbles": oi.unpack_nibbles, "pack_crumbs": oi.pack_crumbs, "unpack_crumbs": oi.unpack_crumbs,
-    "rope_shift": om.rope_shift,
+    "rope_shift": om.rope_shift, "fold_query_weights": om.fold_query_weights, "query_up": om.query_up,
 }
+
+
+def _fold_heads_interleaved(cfg, w_uq, w_uk):
+    wq = np.asarray(w_uq, np.float64).reshape(cfg.d_nope, cfg.n_heads, -1).transpose(1, 0, 2)
+    return np.matmul(np.asarray(w_uk, np.float64), wq)
+
+
+def _fold_uk_transposed_inner(cfg, w_uq, w_uk):
+    wk = np.asarray(w_uk, np.float64)
+    wq = np.asarray(w_uq, np.float64).reshape(cfg.n_heads, cfg.d_nope, -1)
+    return np.matmul(wk[..., ::-1], wq)
+
+
+def _query_up_heads_interleaved(cfg, c_q, w_uq):
+    q = np.asarray(c_q, np.float64) @ np.asarray(w_uq, np.float64).T
+    return q.reshape(q.shape[:-1] + (cfg.d_nope, cfg.n_heads)).swapaxes(-1, -2)
 
 
 def _shift_backwards(st, cfg, delta, slot_begin, n_slots):
@@ -210,6 +226,9 @@ MUTANTS = {
     "rope_shift_axes_reversed": [(om, "rope_shift", _shift_axes_reversed)],
     "rope_shift_slot_range_off_by_one": [(om, "rope_shift", _shift_one_slot_late)],
     "rope_shift_low_bit_codes_kept": [(om, "rope_shift", _shift_codes_kept)],
+    "fold_heads_interleaved": [(om, "fold_query_weights", _fold_heads_interleaved)],
+    "fold_inner_index_reversed": [(om, "fold_query_weights", _fold_uk_transposed_inner)],
+    "query_up_heads_interleaved": [(om, "query_up", _query_up_heads_interleaved)],
 }
 
 
