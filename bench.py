@@ -216,6 +216,63 @@ def main():
     torch.cuda.synchronize()
     attn_call_ms = start.elapsed_time(end) / args.steps
 
+    # ---- operations beside the step (not part of `value`) ----
+    adjacent = {}
+    # rotary-key shift of every slot of every sequence (alternating +1 / -1
+    # frames so the cache returns to its state); bytes: the rotary part of
+    # each row read and written (low-bit: codes and the per-token scale)
+    c0, a0 = caches[0]
+    deltas = [torch.tensor([s_, 0, 0] * B, dtype=torch.int32, device=dev) for s_ in (1, -1)]
+    for i in range(2):
+        api.cache_rope_shift(dims, geom, deltas[i], 0, cfg.capacity, c0, a0)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        api.cache_rope_shift(dims, geom, deltas[i % 2], 0, cfg.capacity, c0, a0)
+    end.record(stream)
+    torch.cuda.synchronize()
+    shift_ms = start.elapsed_time(end) / args.steps
+    rot_bytes = (cfg.d_r // 2 + 2) if cfg.cache_fmt in ("int4", "int2") else cfg.d_r * (2 if cfg.dtype == "bf16" else 4)
+    shift_bytes = 2.0 * B * cfg.capacity * rot_bytes
+    adjacent["cache_rope_shift"] = {"ms": round(shift_ms, 5), "slots": B * cfg.capacity,
+                                    "bytes": shift_bytes, "gbs": round(shift_bytes / shift_ms / 1e6, 1),
+                                    "hbm_frac": round(shift_bytes / shift_ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+    # the absorbed query from a low-rank query latent: the fold of W^UQ and
+    # W^UK formed once (load time), then one product per step over d_cq,
+    # against the per-head absorb of given q_nope (the step's call; the query
+    # up-projection that would produce q_nope is outside this library)
+    fin = make_workload(cfg, seed=0, parts=("c_q", "w_uq"))
+    c_q_t, w_uq_t = dev_t(fin["c_q"]), dev_t(fin["w_uq"])
+    del fin
+    w_fold = torch.empty((H, cfg.d_c, cfg.d_cq), dtype=dt, device=dev)
+    qa_f = torch.empty_like(q_abs[0])
+    api.fold_query_weights(dims, w_uq_t, w_uk, w_fold)
+    torch.cuda.synchronize()
+    start.record(stream)
+    api.fold_query_weights(dims, w_uq_t, w_uk, w_fold)
+    end.record(stream)
+    torch.cuda.synchronize()
+    fold_ms = start.elapsed_time(end)
+    timed = {}
+    for name, call in (("absorb_q_folded", lambda: api.absorb_q_folded(dims, geom, c_q_t, q_rope, q_first, w_fold, qa_f)),
+                       ("absorb_q", lambda: api.absorb_q(dims, geom, q_nope, q_rope, q_first, w_uk, qa_f))):
+        call()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        timed[name] = start.elapsed_time(end) / args.steps
+    adjacent["query_fold"] = {"d_cq": cfg.d_cq, "fold_ms": round(fold_ms, 4),
+                              "absorb_q_folded_ms": round(timed["absorb_q_folded"], 5),
+                              "absorb_q_ms": round(timed["absorb_q"], 5),
+                              "w_fold_bytes": w_fold.numel() * w_fold.element_size(),
+                              "w_uk_bytes": w_uk.numel() * w_uk.element_size(),
+                              "w_uq_bytes": w_uq_t.numel() * w_uq_t.element_size()}
+    del w_fold, w_uq_t, c_q_t, qa_f
+
     # ---- algorithmic work of the attention call ----
     qf = np.arange(cfg.n_q) // P + cfg.q_first
     mask_keys = 0
@@ -276,6 +333,7 @@ def main():
         "breakdown_ms": {k: round(v, 5) for k, v in call_ms.items()},
         "timing": {"step": timing, "direct_calls_ms_per_step": round(eager_ms_per_step, 5)},
         "roofline": roof,
+        "adjacent_ops": adjacent,
     }
 
     if args.copy_calibration:

@@ -46,6 +46,9 @@ SIGNATURES = {
                                  c_void_p, c_void_p, c_void_p, c_size_t]),
     "mla_absorb_q": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p]),
+    "mla_fold_query_weights": (c_int, [_D, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    "mla_absorb_q_folded": (c_int, [_D, _G, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p]),
     "mla_attention_workspace_size": (c_size_t, [_D, _G, c_int32]),
     "mla_attention": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t]),

@@ -160,6 +160,33 @@ def absorb_q(dims, geom, q_nope, q_rope, q_first, w_uk, q_abs):
                            _ptr(q_first), _ptr(w_uk), _ptr(q_abs)))
 
 
+def fold_query_weights(dims, w_uq, w_uk, w_fold):
+    """w_uq [H * d_nope, d_cq], w_uk [H, d_c, d_nope] -> w_fold [H, d_c, d_cq] (load time)."""
+    lib = load()
+    dt = torch_dtype(dims)
+    H = dims.n_heads
+    d_cq = w_uq.shape[-1]
+    _need(w_uq, "w_uq", dt, H * dims.d_nope * d_cq)
+    _need(w_uk, "w_uk", dt, H * dims.d_c * dims.d_nope)
+    _need(w_fold, "w_fold", dt, H * dims.d_c * d_cq)
+    check(lib.mla_fold_query_weights(_rd(dims), _stream(), d_cq, _ptr(w_uq), _ptr(w_uk), _ptr(w_fold)))
+
+
+def absorb_q_folded(dims, geom, c_q, q_rope, q_first, w_fold, q_abs):
+    """c_q [B, n_q, d_cq]; q_rope [B, n_q, H, d_r] -> q_abs [B, n_q, H, d_c + d_r]."""
+    lib = load()
+    dt = torch_dtype(dims)
+    B, H = geom.batch, dims.n_heads
+    n_q, d_cq = c_q.shape[1], c_q.shape[2]
+    _need(c_q, "c_q", dt, B * n_q * d_cq)
+    _need(q_rope, "q_rope", dt, B * n_q * H * dims.d_r)
+    _need(q_first, "q_first", torch.int32, B)
+    _need(w_fold, "w_fold", dt, H * dims.d_c * d_cq)
+    _need(q_abs, "q_abs", dt, B * n_q * H * (dims.d_c + dims.d_r))
+    check(lib.mla_absorb_q_folded(_rd(dims), _rd(geom), _stream(), n_q, d_cq, _ptr(c_q), _ptr(q_rope),
+                                  _ptr(q_first), _ptr(w_fold), _ptr(q_abs)))
+
+
 def attention_workspace_bytes(dims, geom, n_q):
     return int(load().mla_attention_workspace_size(_rd(dims), _rd(geom), n_q))
 

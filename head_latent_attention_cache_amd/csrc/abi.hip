@@ -258,6 +258,58 @@ mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream
   return hip_status(e, st, "query rotary");
 }
 
+static mla_status check_d_cq(const Dims& d, int32_t d_cq) {
+  if (d_cq <= 0) return fail(MLA_ERR_INVALID_ARG, "d_cq must be positive, got %d", d_cq);
+  if (d.dtype == MLA_BF16 && d_cq % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 kernels need d_cq divisible by 8, got %d", d_cq);
+  return MLA_OK;
+}
+
+mla_status mla_fold_query_weights(const mla_dims* dims, void* stream, int32_t d_cq, const void* w_uq,
+                                  const void* w_uk, void* w_fold) {
+  Dims d;
+  CHECK(check_dims(dims, &d));
+  CHECK(check_d_cq(d, d_cq));
+  NEED_PTR(w_uq);
+  NEED_PTR(w_uk);
+  NEED_PTR(w_fold);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_fold_query(d, d_cq, w_uq, w_uk, w_fold, st), st, "query weight fold");
+}
+
+mla_status mla_absorb_q_folded(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                               int32_t d_cq, const void* c_q, const void* q_rope, const int32_t* q_first,
+                               const void* w_fold, void* q_abs) {
+  Dims d;
+  Geo g;
+  CHECK(check_dims(dims, &d));
+  CHECK(check_geom(geom, d, &g));
+  CHECK(check_d_cq(d, d_cq));
+  if (n_q < 0) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 0");
+  const int B = geom->batch;
+  if (B == 0 || n_q == 0) return MLA_OK;
+  NEED_PTR(c_q);
+  NEED_PTR(q_rope);
+  NEED_PTR(q_first);
+  NEED_PTR(w_fold);
+  NEED_PTR(q_abs);
+  hipStream_t st = (hipStream_t)stream;
+  // per head h: q_abs[:, h, 0:d_c] = c_q . w_fold[h]^T (every head reads the same query latents)
+  GemmArgs ga;
+  ga.M = B * n_q;
+  ga.N = d.d_c;
+  ga.K = d_cq;
+  ga.batch = d.H;
+  ga.A = c_q; ga.lda = d_cq; ga.sA = 0;
+  ga.B = w_fold; ga.ldb = d_cq; ga.sB = (long long)d.d_c * d_cq;
+  ga.C = q_abs; ga.ldc = (long long)d.H * d.d_qk; ga.sC = d.d_qk;
+  ga.out_f32 = 0;
+  hipError_t e = launch_gemm_nt(d.dtype, ga, st);
+  if (e != hipSuccess) return hip_status(e, st, "folded absorb projection");
+  e = launch_q_rope(d, g, B, q_rope, n_q, q_first, q_abs, st);
+  return hip_status(e, st, "query rotary");
+}
+
 size_t mla_attention_workspace_size(const mla_dims* dims, const mla_geom* geom, int32_t n_q) {
   Dims d;
   Geo g;

@@ -355,6 +355,52 @@ int gemm_skinny_ksplit(int dtype, int M, int N, int K, int batch) {
   return ks;
 }
 
+// ---------------------------------------------------------------------------
+// load-time fold of the query and key up-projections ("Multi-Head Latent
+// Attention" concept page, Low-rank joint compression: the product
+// W^UQ^T W^UK can be formed once):
+//   w_fold[h][a][j] = sum_i w_uk[h][a][i] * w_uq[h d_nope + i][j]
+// fp32 accumulation in the order i = 0 .. d_nope - 1, rounded once to the
+// storage type.  grid (ceil(d_cq / 256), ceil(d_c / FOLD_ROWS), H): a thread
+// owns one column j of FOLD_ROWS rows a; the w_uq row segment is read once
+// per work-group step (coalesced along j), the w_uk values are broadcasts.
+// ---------------------------------------------------------------------------
+constexpr int FOLD_ROWS = 8;
+
+template <typename T>
+__global__ __launch_bounds__(256) void fold_query_kernel(int d_nope, int d_c, int d_cq, const T* __restrict__ w_uq,
+                                                         const T* __restrict__ w_uk, T* __restrict__ w_fold) {
+  const int h = blockIdx.z, j = blockIdx.x * 256 + threadIdx.x, a0 = blockIdx.y * FOLD_ROWS;
+  if (j >= d_cq) return;
+  float acc[FOLD_ROWS];
+#pragma unroll
+  for (int r = 0; r < FOLD_ROWS; ++r) acc[r] = 0.f;
+  const T* uk = w_uk + (size_t)h * d_c * d_nope;
+  const T* uq = w_uq + (size_t)h * d_nope * d_cq + j;
+  for (int i = 0; i < d_nope; ++i) {
+    const float q = Elem<T>::load(uq, (size_t)i * d_cq);
+#pragma unroll
+    for (int r = 0; r < FOLD_ROWS; ++r)
+      if (a0 + r < d_c) acc[r] = fmaf(Elem<T>::load(uk, (size_t)(a0 + r) * d_nope + i), q, acc[r]);
+  }
+  T* out = w_fold + (size_t)h * d_c * d_cq + j;
+#pragma unroll
+  for (int r = 0; r < FOLD_ROWS; ++r)
+    if (a0 + r < d_c) Elem<T>::store(out, (size_t)(a0 + r) * d_cq, acc[r]);
+}
+
+hipError_t launch_fold_query(const Dims& d, int d_cq, const void* w_uq, const void* w_uk, void* w_fold,
+                             hipStream_t st) {
+  dim3 grid((d_cq + 255) / 256, (d.d_c + FOLD_ROWS - 1) / FOLD_ROWS, d.H);
+  if (d.dtype == MLA_BF16)
+    fold_query_kernel<bf16_t><<<grid, 256, 0, st>>>(d.d_nope, d.d_c, d_cq, (const bf16_t*)w_uq, (const bf16_t*)w_uk,
+                                                    (bf16_t*)w_fold);
+  else
+    fold_query_kernel<float><<<grid, 256, 0, st>>>(d.d_nope, d.d_c, d_cq, (const float*)w_uq, (const float*)w_uk,
+                                                   (float*)w_fold);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0 || a.batch == 0) return hipSuccess;
   if (dtype == MLA_F32) {

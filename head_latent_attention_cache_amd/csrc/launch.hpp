@@ -35,6 +35,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st);
+hipError_t launch_fold_query(const Dims& d, int d_cq, const void* w_uq, const void* w_uk, void* w_fold,
+                             hipStream_t st);
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
                                const int* frame, void* cache, void* aux, int nsplit, hipStream_t st);
 hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,

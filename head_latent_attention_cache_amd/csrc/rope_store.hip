@@ -197,30 +197,33 @@ __global__ void dequant_kernel(Dims d, Geo g, int batch, const void* __restrict_
 // corrected in closed form when its token moves, the content latent is
 // position-free).  Rotations by angles proportional to the coordinate
 // compose, R(p + delta) = R(delta) R(p), so every row of a sequence turns by
-// the same table.  grid (ceil(n_slots / SHIFT_ROWS), B): one rotary pair per
-// thread and row; low-bit rows are dequantised, rotated, rounded to bf16 and
-// re-quantised (new per-token scale) once the work-group holds them.  A
+// the same table.  grid (ceil(n_slots / rows_per_block), B): one rotary pair
+// per thread and row; low-bit rows are dequantised, rotated, rounded to bf16
+// and re-quantised (new per-token scale) once the work-group holds them.  A
 // shift that is zero in the coordinates the embedding uses returns at once.
 // ---------------------------------------------------------------------------
-constexpr int SHIFT_ROWS = 16;
-
 template <typename T, bool LOWBIT>
 __global__ void rope_shift_kernel(Dims d, Geo g, int batch, const int* __restrict__ delta, int slot_begin,
-                                  int n_slots, void* __restrict__ cache, __half* __restrict__ aux) {
+                                  int n_slots, int rows_per_block, void* __restrict__ cache,
+                                  __half* __restrict__ aux) {
   extern __shared__ float smem[];
   float* cosv = smem;                 // [d_r / 2]
   float* sinv = smem + d.d_r / 2;     // [d_r / 2]
-  float* rows = smem + d.d_r;         // low-bit: [SHIFT_ROWS][d_r] rotated keys
+  float* rows = smem + d.d_r;         // low-bit: [rows_per_block][d_r] rotated keys, then row maxima
+  int* amax = (int*)(rows + rows_per_block * d.d_r);
   const int b = blockIdx.y;
   const int dt = delta[3 * b], dh = delta[3 * b + 1], dw = delta[3 * b + 2];
   if (dt == 0 && (d.rope_dims == 1 || (dh == 0 && dw == 0))) return;
   const double coord[3] = {(double)dt, (double)dh, (double)dw};
   rope_table(d, coord, cosv, sinv);
+  const int s0 = slot_begin + blockIdx.x * rows_per_block;
+  const int nrow = min(rows_per_block, slot_begin + n_slots - s0);
+  if (LOWBIT)
+    for (int r = threadIdx.x; r < nrow; r += blockDim.x) amax[r] = 0;
   __syncthreads();
-  const int s0 = slot_begin + blockIdx.x * SHIFT_ROWS;
-  const int nrow = min(SHIFT_ROWS, slot_begin + n_slots - s0);
   const int npair = d.d_r / 2;
   const size_t rs_base = (size_t)batch * g.capacity * (d.d_c / 32);   // per-token rotary scales
+  const size_t rot_off = (size_t)d.d_c * content_bits(d) / 8;        // low-bit: rotary codes in a row
   for (int e = threadIdx.x; e < nrow * npair; e += blockDim.x) {
     const int r = e / npair, p = e % npair;
     const size_t srow = (size_t)b * g.capacity + s0 + r;
@@ -231,8 +234,7 @@ __global__ void rope_shift_kernel(Dims d, Geo g, int batch, const int* __restric
       x1 = Elem<T>::load(k, 2 * p + 1);
     } else {
       // INT4 rotary codes: element 2p in the low nibble of byte p
-      const uint8_t* codes = (const uint8_t*)cache + srow * code_row_bytes(d) + d.d_c * content_bits(d) / 8;
-      const int byte = codes[p];
+      const int byte = ((const uint8_t*)cache)[srow * code_row_bytes(d) + rot_off + p];
       const float s = __half2float(aux[rs_base + srow]);
       x0 = (float)(((byte & 15) ^ 8) - 8) * s;
       x1 = (float)(((byte >> 4) ^ 8) - 8) * s;
@@ -246,17 +248,33 @@ __global__ void rope_shift_kernel(Dims d, Geo g, int batch, const int* __restric
     } else {
       rows[r * d.d_r + 2 * p] = r0;
       rows[r * d.d_r + 2 * p + 1] = r1;
+      // row maximum of |x| (non-negative floats order as their bit patterns)
+      atomicMax(&amax[r], __float_as_int(fmaxf(fabsf(r0), fabsf(r1))));
     }
   }
   if (LOWBIT) {
-    __syncthreads();   // every code of these rows is read before any is rewritten
-    for (int r = threadIdx.x; r < nrow; r += blockDim.x) {
+    // every code of these rows is read before any is rewritten; then the
+    // quantiser of the append, one byte (two codes) per thread
+    __syncthreads();
+    for (int e = threadIdx.x; e < nrow * npair; e += blockDim.x) {
+      const int r = e / npair, p = e % npair;
       const size_t srow = (size_t)b * g.capacity + s0 + r;
-      uint8_t* codes = (uint8_t*)cache + srow * code_row_bytes(d) + d.d_c * content_bits(d) / 8;
-      quant_lowbit(rows + r * d.d_r, d.d_r, 4, codes, aux + rs_base + srow);
+      const __half s16 = __float2half_rn(__int_as_float(amax[r]) / 7.f);
+      const float s = __half2float(s16);
+      int byte = 0;
+      for (int k = 0; k < 2; ++k) {
+        int q = 0;
+        if (s != 0.f) q = (int)fminf(fmaxf(rintf(rows[r * d.d_r + 2 * p + k] / s), -8.f), 7.f);
+        byte |= (q & 15) << (4 * k);
+      }
+      ((uint8_t*)cache)[srow * code_row_bytes(d) + rot_off + p] = (uint8_t)byte;
+      if (p == 0) aux[rs_base + srow] = s16;
     }
   }
 }
+
+// rows per work-group of the shift: 64 dense; low-bit rows are held in LDS
+inline int rope_shift_rows(const Dims& d) { return lowbit_cache(d) ? max(1, min(64, 4096 / d.d_r)) : 64; }
 
 // ---------------------------------------------------------------------------
 // host launchers
@@ -304,14 +322,18 @@ hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* ca
 
 hipError_t launch_rope_shift(const Dims& d, const Geo& g, int batch, const int* delta, int slot_begin,
                              int n_slots, void* cache, void* aux, hipStream_t st) {
-  dim3 grid((n_slots + SHIFT_ROWS - 1) / SHIFT_ROWS, batch);
-  const size_t shm = (size_t)d.d_r * sizeof(float) * (lowbit_cache(d) ? 1 + SHIFT_ROWS : 1);
+  const int rpb = rope_shift_rows(d);
+  dim3 grid((n_slots + rpb - 1) / rpb, batch);
+  const size_t shm = (size_t)d.d_r * sizeof(float) + (lowbit_cache(d) ? (size_t)rpb * (d.d_r + 1) * sizeof(float) : 0);
   if (lowbit_cache(d))
-    rope_shift_kernel<bf16_t, true><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, cache, (__half*)aux);
+    rope_shift_kernel<bf16_t, true><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, rpb, cache,
+                                                             (__half*)aux);
   else if (d.dtype == MLA_BF16)
-    rope_shift_kernel<bf16_t, false><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, cache, nullptr);
+    rope_shift_kernel<bf16_t, false><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, rpb, cache,
+                                                              nullptr);
   else
-    rope_shift_kernel<float, false><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, cache, nullptr);
+    rope_shift_kernel<float, false><<<grid, 256, shm, st>>>(d, g, batch, delta, slot_begin, n_slots, rpb, cache,
+                                                             nullptr);
   return hipGetLastError();
 }
 

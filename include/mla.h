@@ -173,6 +173,31 @@ mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream
                         const void* w_uk, void* q_abs);
 
 /*
+ * Low-rank query with the key up-projection folded in when the weights are
+ * loaded: [MLA concept, Low-rank joint compression] (q . k = c^Q^T (W^UQ^T
+ * W^UK) c^KV, so the product of the two up-projections is formed once).
+ * mla_fold_query_weights (load time):
+ *     w_fold[h] = w_uk[h] . W^UQ_h        (fp32 accumulation, one rounding)
+ *   w_uq   [H * d_nope, d_cq]  the query up-projection, output-feature major:
+ *          q_nope[.., h, i] = sum_j w_uq[h * d_nope + i, j] c_q[.., j]
+ *   w_uk   [H, d_c, d_nope]    as for mla_absorb_q
+ *   w_fold [H, d_c, d_cq]
+ * mla_absorb_q_folded (instead of mla_absorb_q when the model has a query latent):
+ *     q_abs[b, t, h, 0 : d_c]        = w_fold[h] . c_q[b, t]
+ *     q_abs[b, t, h, d_c : d_c + d_r] = RoPE(q_rope[b, t, h], coordinates of the token)
+ *   c_q [B, n_q, d_cq]; q_rope, q_first, q_abs as for mla_absorb_q.
+ * d_cq must be positive (bf16: a multiple of 8, else MLA_ERR_UNSUPPORTED).
+ * The fold trades the per-head product over d_nope (plus the query
+ * up-projection, outside this library) for one product over d_cq with a
+ * weight d_c / d_nope times the size of W^UQ.
+ */
+mla_status mla_fold_query_weights(const mla_dims* dims, void* stream, int32_t d_cq, const void* w_uq,
+                                  const void* w_uk, void* w_fold);
+mla_status mla_absorb_q_folded(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                               int32_t d_cq, const void* c_q, const void* q_rope, const int32_t* q_first,
+                               const void* w_fold, void* q_abs);
+
+/*
  * mla_attention: [MLA concept, Low-rank joint compression] (with both
  * up-projections absorbed, decode-time attention runs on the latents
  * themselves) and [The RoPE problem, and the decoupled fix] (score = content

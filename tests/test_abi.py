@@ -182,3 +182,15 @@ def test_rope_shift_needs_aux_for_lowbit(lib):
     fake = ctypes.c_void_p(0x1000)
     st = lib.mla_cache_rope_shift(ctypes.byref(d), ctypes.byref(g), None, fake, 0, 4, fake, None)
     assert st == _lib.MLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d_cq,status", [(0, _lib.MLA_ERR_INVALID_ARG), (-8, _lib.MLA_ERR_INVALID_ARG),
+                                         (12, _lib.MLA_ERR_UNSUPPORTED)])
+def test_query_fold_width_checked(lib, d_cq, status):
+    cfg = SMALL_CONFIGS[3]                # bf16
+    d, g = _dims(cfg), _geom(cfg)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.mla_fold_query_weights(ctypes.byref(d), None, d_cq, fake, fake, fake) == status
+    assert lib.mla_absorb_q_folded(ctypes.byref(d), ctypes.byref(g), None, 4, d_cq, fake, fake, fake, fake,
+                                   fake) == status
+    assert lib.mla_last_error()
