@@ -350,6 +350,58 @@ def attend(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, q_first: int, tokens=None, h
 
 
 # ---------------------------------------------------------------------------
+# QK normalisation: [MLA topics, QK-Norm abstract]: RMSNorm of the projected
+# query and key splits into a static per-dimension weight and one dynamic RMS
+# statistic; in MLA every head's key comes from the one cached latent, so the
+# key statistic is one scalar per token (one KV group).
+# Reading: the norm covers the content part of the projected query, and of
+# the projected key, of all heads together (H * d_nope values per token),
+# with eps inside the root; the decoupled rotary parts are not normalised;
+# the key is projected from the stored latent (what attention reads).
+# ---------------------------------------------------------------------------
+def rms_normalise(v, g, eps: float):
+    """g * v / sqrt(mean(v^2) + eps) over the last two axes [.., H, d_nope]."""
+    v = np.asarray(v, np.float64)
+    d = np.sqrt(np.mean(v * v, axis=(-2, -1), keepdims=True) + eps)
+    return np.asarray(g, np.float64) * v / np.where(d > 0, d, 1.0)   # (an all-zero v stays zero)
+
+
+def attend_qk_norm(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, g_q, g_k, eps: float, q_first: int,
+                   tokens=None):
+    """Per-head attention with explicit post-projection QK RMSNorm: every
+    head's content key k_h = W^UK_h c and content query are normalised as
+    above (weights g_q, g_k [H, d_nope]), joined with the unnormalised rotary
+    parts, and attend with the textbook softmax.  Same outputs as ``attend``."""
+    B, H = cfg.batch, cfg.n_heads
+    w_uk = np.asarray(w_uk, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    if tokens is None:
+        tokens = [(b, t) for b in range(B) for t in range(cfg.n_q)]
+    tokens = list(tokens)
+    mask_all = mask_matrix(cfg, q_first, st["newest"])
+    o_heads = np.zeros((len(tokens), H, cfg.d_v))
+    o_lat = np.zeros((len(tokens), H, cfg.d_c))
+    lse = np.zeros((len(tokens), H))
+    for b in sorted({b for b, _ in tokens}):
+        idx = [i for i, (bb, _) in enumerate(tokens) if bb == b]
+        ts = np.array([tokens[i][1] for i in idx])
+        C = st["values"][b, :, :cfg.d_c]
+        KR = st["values"][b, :, cfg.d_c:]
+        k_all = rms_normalise(np.einsum("sc,hci->shi", C, w_uk), g_k, eps)     # [S, H, d_nope]
+        q_all = rms_normalise(np.asarray(q_nope, np.float64)[b, ts], g_q, eps)  # [T, H, d_nope]
+        mask = mask_all[ts]
+        for h in range(H):
+            K = np.concatenate([k_all[:, h], KR], axis=-1)
+            V = C @ w_uv[h].T
+            Q = np.concatenate([q_all[:, h], q_rope_rot[b, ts, h]], axis=-1)
+            o, P, l = attention_core(Q, K, V, mask, softmax_scale(cfg))
+            o_heads[idx, h] = o
+            o_lat[idx, h] = P @ C
+            lse[idx, h] = l
+    return o_heads, o_lat, lse
+
+
+# ---------------------------------------------------------------------------
 # output: [MLA concept, Low-rank joint compression] (W^UV folds into the output
 # projection) and [MLA explainer, On-the-Fly Reconstruction]
 # ---------------------------------------------------------------------------

@@ -616,6 +616,101 @@ def check_query_fold():
     return float(max(errs))
 
 
+def _qkn_inputs(cfg, seed):
+    rng = np.random.default_rng(seed)
+    inp = make_workload(cfg, seed=seed)
+    st = om.build_cache(cfg, inp)
+    g_q = rng.uniform(0.5, 1.5, (cfg.n_heads, cfg.d_nope))
+    g_k = rng.uniform(0.5, 1.5, (cfg.n_heads, cfg.d_nope))
+    return inp, st, g_q, g_k
+
+
+def check_qk_norm():
+    """Explicit post-projection QK RMSNorm: scalar loops on a tiny workload;
+    the absorbed form (static weights folded into the key up-projection,
+    one inverse RMS per key token and per query token, applied to the content
+    score) equals it; with unit-RMS keys and queries and unit weights it is
+    plain attention; a common scale of every latent or of the query leaves the
+    probabilities."""
+    errs = []
+    eps = 1e-6
+    cfg = TINIER_BLOCK
+    inp, st, g_q, g_k = _qkn_inputs(cfg, 7)
+    w_uk, w_uv = om.as_f64(inp["w_uk"]), om.as_f64(inp["w_uv"])
+    q_nope, q_rope = om.as_f64(inp["q_nope"]), om.as_f64(inp["q_rope"])
+    q_rot = om.absorb_query(cfg, q_nope, q_rope, w_uk, cfg.q_first)[..., cfg.d_c:]
+    _, o_lat, lse = om.attend_qk_norm(cfg, st, q_nope, q_rot, w_uk, w_uv, g_q, g_k, eps, cfg.q_first)
+    H, dn, dc = cfg.n_heads, cfg.d_nope, cfg.d_c
+    mask = om.mask_matrix(cfg, cfg.q_first, st["newest"])
+    scale = 1.0 / math.sqrt(dn + cfg.d_r)
+    # (1) scalar loops
+    n = 0
+    for b in range(cfg.batch):
+        vals = st["values"][b]
+        keys = []
+        for s_ in range(cfg.capacity):
+            k = [[sum(vals[s_, a] * w_uk[h, a, i] for a in range(dc)) for i in range(dn)] for h in range(H)]
+            ms = sum(k[h][i] ** 2 for h in range(H) for i in range(dn)) / (H * dn)
+            keys.append([[g_k[h][i] * k[h][i] / math.sqrt(ms + eps) for i in range(dn)] for h in range(H)])
+        for t in range(cfg.n_q):
+            q = q_nope[b, t]
+            ms = sum(q[h][i] ** 2 for h in range(H) for i in range(dn)) / (H * dn)
+            for h in range(H):
+                qh = [g_q[h][i] * q[h][i] / math.sqrt(ms + eps) for i in range(dn)]
+                sc = []
+                for s_ in range(cfg.capacity):
+                    if not mask[t, s_]:
+                        continue
+                    v = sum(qh[i] * keys[s_][h][i] for i in range(dn))
+                    v += sum(q_rot[b, t, h, j] * vals[s_, dc + j] for j in range(cfg.d_r))
+                    sc.append((v * scale, s_))
+                m = max(v for v, _ in sc)
+                tot = sum(math.exp(v - m) for v, _ in sc)
+                o = [sum(math.exp(v - m) / tot * vals[s_, a] for v, s_ in sc) for a in range(dc)]
+                errs.append(abs(lse[n + t, h] - (m + math.log(tot))))
+                errs.append(max(abs(o_lat[n + t, h, a] - o[a]) for a in range(dc)))
+        n += cfg.n_q
+    # (2) absorbed form: score_h = inv_q inv_k (w_uk[h] (g_q g_k q_h)) . c + q_r . k_r
+    gram = np.einsum("hai,hbi->ab", w_uk, w_uk)
+    for b in range(cfg.batch):
+        C = st["values"][b, :, :dc]
+        inv_k = 1.0 / np.sqrt(np.einsum("sa,ab,sb->s", C, gram, C) / (H * dn) + eps)
+        qn = q_nope[b]
+        inv_q = 1.0 / np.sqrt(np.mean(qn * qn, axis=(1, 2)) + eps)
+        q_lat = np.einsum("hai,thi->tha", w_uk, qn * (g_q * g_k)) * inv_q[:, None, None]
+        s_abs = (np.einsum("tha,sa->ths", q_lat, C) * inv_k[None, None, :]
+                 + np.einsum("thj,sj->ths", q_rot[b], st["values"][b, :, dc:]))
+        k_all = om.rms_normalise(np.einsum("sc,hci->shi", C, w_uk), g_k, eps)
+        q_all = om.rms_normalise(qn, g_q, eps)
+        s_mat = (np.einsum("thi,shi->ths", q_all, k_all)
+                 + np.einsum("thj,sj->ths", q_rot[b], st["values"][b, :, dc:]))
+        errs.append(np.max(np.abs(s_abs - s_mat)))
+    # (3) unit RMS, unit weights, eps 0: plain attention
+    for c2 in (TINIER_BLOCK, TINY_DECODE.replace(name="td32", dtype="f32")):
+        inp2, st2, _, _ = _qkn_inputs(c2, 8)
+        wk2, wv2 = om.as_f64(inp2["w_uk"]), om.as_f64(inp2["w_uv"])
+        for b in range(c2.batch):
+            C = st2["values"][b, :, :c2.d_c]
+            k = np.einsum("sc,hci->shi", C, wk2)
+            r = np.sqrt(np.mean(k * k, axis=(1, 2)))
+            st2["values"][b, :, :c2.d_c] = C / np.where(r > 0, r, 1.0)[:, None]
+        qn2 = om.as_f64(inp2["q_nope"])
+        qn2 = qn2 / np.sqrt(np.mean(qn2 * qn2, axis=(-2, -1), keepdims=True))
+        qr2 = om.absorb_query(c2, qn2, om.as_f64(inp2["q_rope"]), wk2, c2.q_first)[..., c2.d_c:]
+        ones = np.ones((c2.n_heads, c2.d_nope))
+        a = om.attend_qk_norm(c2, st2, qn2, qr2, wk2, wv2, ones, ones, 0.0, c2.q_first)
+        p = om.attend(c2, st2, qn2, qr2, wk2, wv2, c2.q_first)
+        errs.append(max(np.max(np.abs(x - y)) for x, y in zip(a, p)))
+    # (4) scale invariance of the probabilities
+    st3 = {"values": st["values"].copy(), "newest": st["newest"]}
+    st3["values"][..., :dc] *= 3.0
+    _, o3, l3 = om.attend_qk_norm(cfg, st3, 0.25 * q_nope, q_rot, w_uk, w_uv, g_q, g_k, 0.0, cfg.q_first)
+    _, o0, l0 = om.attend_qk_norm(cfg, st, q_nope, q_rot, w_uk, w_uv, g_q, g_k, 0.0, cfg.q_first)
+    errs.append(np.max(np.abs(l3 - l0)))
+    errs.append(np.max(np.abs(o3 - 3.0 * o0)))
+    return float(max(errs))
+
+
 CHECKS = {
     "bruteforce": (check_bruteforce, 1e-12),
     "absorption": (check_absorption, 1e-12),
@@ -630,6 +725,7 @@ CHECKS = {
     "int2": (check_int2, 0.0),
     "rope_shift": (check_rope_shift, 0.5),
     "query_fold": (check_query_fold, 1e-12),
+    "qk_norm": (check_qk_norm, 1e-9),
 }
 
 

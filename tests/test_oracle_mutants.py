@@ -19,7 +19,23 @@ _orig = {
     "quantize_groups": oi.quantize_groups, "pack_nibbles": oi.pack_nibbles,
     "unpack_nibbles": oi.unpack_nibbles, "pack_crumbs": oi.pack_crumbs, "unpack_crumbs": oi.unpack_crumbs,
     "rope_shift": om.rope_shift, "fold_query_weights": om.fold_query_weights, "query_up": om.query_up,
+    "rms_normalise": om.rms_normalise, "attend_qk_norm": om.attend_qk_norm,
 }
+
+
+def _rms_per_head(v, g, eps):
+    v = np.asarray(v, np.float64)
+    return np.asarray(g, np.float64) * v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+
+
+def _rms_eps_outside(v, g, eps):
+    v = np.asarray(v, np.float64)
+    return np.asarray(g, np.float64) * v / (np.sqrt(np.mean(v * v, axis=(-2, -1), keepdims=True)) + eps)
+
+
+def _qkn_key_weight_dropped(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, g_q, g_k, eps, q_first, tokens=None):
+    return _orig["attend_qk_norm"](cfg, st, q_nope, q_rope_rot, w_uk, w_uv, g_q, np.ones_like(g_k), eps,
+                                   q_first, tokens)
 
 
 def _fold_heads_interleaved(cfg, w_uq, w_uk):
@@ -229,6 +245,9 @@ MUTANTS = {
     "fold_heads_interleaved": [(om, "fold_query_weights", _fold_heads_interleaved)],
     "fold_inner_index_reversed": [(om, "fold_query_weights", _fold_uk_transposed_inner)],
     "query_up_heads_interleaved": [(om, "query_up", _query_up_heads_interleaved)],
+    "qk_norm_per_head_rms": [(om, "rms_normalise", _rms_per_head)],
+    "qk_norm_eps_outside_root": [(om, "rms_normalise", _rms_eps_outside)],
+    "qk_norm_key_weight_dropped": [(om, "attend_qk_norm", _qkn_key_weight_dropped)],
 }
 
 
