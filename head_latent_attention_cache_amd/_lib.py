@@ -22,7 +22,7 @@ class MlaDims(ctypes.Structure):
         ("n_heads", c_int32), ("d_model", c_int32), ("d_nope", c_int32), ("d_v", c_int32),
         ("d_c", c_int32), ("d_r", c_int32), ("rope_dims", c_int32), ("band", c_int32 * 3),
         ("rope_theta", c_float), ("softmax_scale", c_float), ("dtype", c_int32),
-        ("cache_fmt", c_int32),
+        ("cache_fmt", c_int32), ("qk_norm", c_int32), ("qk_norm_eps", c_float),
     ]
 
 
@@ -49,6 +49,8 @@ SIGNATURES = {
     "mla_fold_query_weights": (c_int, [_D, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "mla_absorb_q_folded": (c_int, [_D, _G, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
+    "mla_qk_norm_prepare": (c_int, [_D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "mla_cache_key_norm": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_attention_workspace_size": (c_size_t, [_D, _G, c_int32]),
     "mla_attention": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t]),

@@ -18,7 +18,7 @@ _TORCH_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
 
 
 def make_dims(n_heads, d_model, d_nope, d_v, d_c, d_r, rope_dims, bands, theta=10000.0,
-              softmax_scale=0.0, dtype="bf16", cache_fmt="dense") -> MlaDims:
+              softmax_scale=0.0, dtype="bf16", cache_fmt="dense", qk_norm=False, qk_norm_eps=1e-6) -> MlaDims:
     d = MlaDims()
     d.n_heads, d.d_model, d.d_nope, d.d_v, d.d_c, d.d_r = n_heads, d_model, d_nope, d_v, d_c, d_r
     d.rope_dims = rope_dims
@@ -29,6 +29,8 @@ def make_dims(n_heads, d_model, d_nope, d_v, d_c, d_r, rope_dims, bands, theta=1
     d.dtype = {"f32": MLA_F32, "bf16": MLA_BF16}[dtype] if isinstance(dtype, str) else dtype
     d.cache_fmt = ({"dense": MLA_CACHE_DENSE, "int4": MLA_CACHE_INT4, "int2": MLA_CACHE_INT2}[cache_fmt]
                    if isinstance(cache_fmt, str) else cache_fmt)
+    d.qk_norm = int(bool(qk_norm))
+    d.qk_norm_eps = qk_norm_eps
     return d
 
 
@@ -41,7 +43,8 @@ def make_geom(batch, grid_h, grid_w, window, frames_per_block=1) -> MlaGeom:
 def dims_from_config(cfg) -> MlaDims:
     """Dimensions from any object with the workload attribute names."""
     return make_dims(cfg.n_heads, cfg.d_model, cfg.d_nope, cfg.d_v, cfg.d_c, cfg.d_r, cfg.rope_dims,
-                     cfg.bands, cfg.theta, 0.0, cfg.dtype, cfg.cache_fmt)
+                     cfg.bands, cfg.theta, 0.0, cfg.dtype, cfg.cache_fmt, getattr(cfg, "qk_norm", False),
+                     getattr(cfg, "qk_eps", 1e-6))
 
 
 def geom_from_config(cfg, batch=None) -> MlaGeom:
@@ -95,10 +98,10 @@ def new_cache(dims, geom, device="cuda", fill=None):
     if dims.cache_fmt in (MLA_CACHE_INT4, MLA_CACHE_INT2):
         # low-bit: code bytes per row as the library sizes them; fp16 scales
         cache = torch.empty((geom.batch, cap, nb // max(1, geom.batch * cap)), dtype=torch.uint8, device=device)
-        aux = torch.empty(na // 2, dtype=torch.float16, device=device)
     else:
         cache = torch.empty((geom.batch, cap, dqk), dtype=torch_dtype(dims), device=device)
-        aux = None
+    # fp16 scales (low-bit) and / or the per-slot key inverse RMS (QK normalisation)
+    aux = torch.empty(na // 2, dtype=torch.float16, device=device) if na else None
     assert cache.numel() * cache.element_size() == nb
     if fill is not None:
         cache.view(torch.uint8).fill_(fill)
@@ -115,9 +118,20 @@ def _check_cache(dims, geom, cache, cache_aux):
     nb, na = cache_nbytes(dims, geom)
     if dims.cache_fmt in (MLA_CACHE_INT4, MLA_CACHE_INT2):
         _need(cache, "cache", torch.uint8, nb)
-        _need(cache_aux, "cache_aux", torch.float16, na // 2)
     else:
         _need(cache, "cache", torch_dtype(dims), nb // (2 if dims.dtype == MLA_BF16 else 4))
+    if na:
+        _need(cache_aux, "cache_aux", torch.float16, na // 2)
+
+
+def key_scales(dims, geom, cache_aux):
+    """Float32 view [B, capacity] of the per-slot key inverse RMS held in
+    cache_aux (QK normalisation)."""
+    cap = geom.window * geom.grid_h * geom.grid_w
+    rows = geom.batch * cap
+    nb, na = cache_nbytes(dims, geom)
+    off = na - 4 * rows
+    return cache_aux.view(torch.uint8)[off:na].view(torch.float32).view(geom.batch, cap)
 
 
 # ---------------------------------------------------------------------------
@@ -185,6 +199,32 @@ def absorb_q_folded(dims, geom, c_q, q_rope, q_first, w_fold, q_abs):
     _need(q_abs, "q_abs", dt, B * n_q * H * (dims.d_c + dims.d_r))
     check(lib.mla_absorb_q_folded(_rd(dims), _rd(geom), _stream(), n_q, d_cq, _ptr(c_q), _ptr(q_rope),
                                   _ptr(q_first), _ptr(w_fold), _ptr(q_abs)))
+
+
+def qk_norm_prepare(dims, w_uk, g_q, g_k, w_uk_folded, gram):
+    """Load time: w_uk_folded = w_uk * g_q * g_k (per head and content dim),
+    gram [d_c, d_c] float = sum_h w_uk[h] w_uk[h]^T."""
+    lib = load()
+    dt = torch_dtype(dims)
+    H = dims.n_heads
+    _need(w_uk, "w_uk", dt, H * dims.d_c * dims.d_nope)
+    _need(g_q, "g_q", dt, H * dims.d_nope)
+    _need(g_k, "g_k", dt, H * dims.d_nope)
+    _need(w_uk_folded, "w_uk_folded", dt, H * dims.d_c * dims.d_nope)
+    _need(gram, "gram", torch.float32, dims.d_c * dims.d_c)
+    check(lib.mla_qk_norm_prepare(_rd(dims), _stream(), _ptr(w_uk), _ptr(g_q), _ptr(g_k), _ptr(w_uk_folded),
+                                  _ptr(gram)))
+
+
+def cache_key_norm(dims, geom, n_tokens, frame, gram, cache, cache_aux):
+    """Key inverse RMS of the rows of n_tokens tokens written at frame[b]
+    onwards (the arguments of the matching mla_cache_append)."""
+    lib = load()
+    _check_cache(dims, geom, cache, cache_aux)
+    _need(frame, "frame", torch.int32, geom.batch)
+    _need(gram, "gram", torch.float32, dims.d_c * dims.d_c)
+    check(lib.mla_cache_key_norm(_rd(dims), _rd(geom), _stream(), int(n_tokens), _ptr(frame), _ptr(gram),
+                                 _ptr(cache), _ptr(cache_aux)))
 
 
 def attention_workspace_bytes(dims, geom, n_q):

@@ -76,6 +76,9 @@ mla_status check_dims(const mla_dims* dm, Dims* d) {
     if (dm->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "a low-bit cache requires MLA_BF16");
     if (dm->d_c % 32) return fail(MLA_ERR_INVALID_ARG, "a low-bit cache requires d_c %% 32 == 0");
   }
+  if (dm->qk_norm != 0 && dm->qk_norm != 1) return fail(MLA_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
+  if (dm->qk_norm && !(dm->qk_norm_eps >= 0.f && dm->qk_norm_eps < 1e30f))
+    return fail(MLA_ERR_INVALID_ARG, "qk_norm_eps must be finite and >= 0");
   const int dqk = dm->d_c + dm->d_r;
   if (dm->d_c > 1024 || dqk > 1536)
     return fail(MLA_ERR_UNSUPPORTED, "d_c <= 1024 and d_c + d_r <= 1536 are supported");
@@ -99,6 +102,8 @@ mla_status check_dims(const mla_dims* dm, Dims* d) {
   d->scale = dm->softmax_scale > 0.f ? dm->softmax_scale : 1.0f / sqrtf((float)(dm->d_nope + dm->d_r));
   d->dtype = dm->dtype;
   d->cache_fmt = dm->cache_fmt;
+  d->qk_norm = dm->qk_norm;
+  d->qk_eps = dm->qk_norm ? dm->qk_norm_eps : 0.f;
   return MLA_OK;
 }
 
@@ -166,8 +171,9 @@ size_t mla_cache_aux_bytes(const mla_dims* dims, const mla_geom* geom) {
   Dims d;
   Geo g;
   if (check_dims(dims, &d) != MLA_OK || check_geom(geom, d, &g) != MLA_OK) return 0;
-  if (!lowbit_cache(d)) return 0;
   const size_t rows = (size_t)geom->batch * g.capacity;
+  if (d.qk_norm) return key_scale_offset(d, rows) + rows * sizeof(float);
+  if (!lowbit_cache(d)) return 0;
   return rows * (d.d_c / 32 + 1) * sizeof(__half);
 }
 
@@ -254,6 +260,10 @@ mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream
   ga.out_f32 = 0;
   hipError_t e = launch_gemm_nt(d.dtype, ga, st);
   if (e != hipSuccess) return hip_status(e, st, "absorb projection");
+  if (d.qk_norm) {
+    e = launch_q_norm(d, B, n_q, q_nope, q_abs, st);
+    if (e != hipSuccess) return hip_status(e, st, "query inverse RMS");
+  }
   e = launch_q_rope(d, g, B, q_rope, n_q, q_first, q_abs, st);
   return hip_status(e, st, "query rotary");
 }
@@ -285,6 +295,8 @@ mla_status mla_absorb_q_folded(const mla_dims* dims, const mla_geom* geom, void*
   CHECK(check_dims(dims, &d));
   CHECK(check_geom(geom, d, &g));
   CHECK(check_d_cq(d, d_cq));
+  if (d.qk_norm)
+    return fail(MLA_ERR_UNSUPPORTED, "QK normalisation needs the query's content values (use mla_absorb_q)");
   if (n_q < 0) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 0");
   const int B = geom->batch;
   if (B == 0 || n_q == 0) return MLA_OK;
@@ -337,7 +349,7 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
   NEED_PTR(cache);
   NEED_PTR(o_lat);
   if (lse && ((uintptr_t)lse & 3u)) return fail(MLA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
-  if (lowbit_cache(d)) NEED_PTR(cache_aux);
+  if (lowbit_cache(d) || d.qk_norm) NEED_PTR(cache_aux);
   AttnArgs a;
   a.d = d;
   a.g = g;
@@ -348,6 +360,8 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
   a.newest = newest;
   a.cache = cache;
   a.aux = (const __half*)cache_aux;
+  a.kscale = d.qk_norm ? (const float*)((const char*)cache_aux + key_scale_offset(d, (size_t)B * g.capacity))
+                       : nullptr;
   a.batch = B;
   a.o_lat = o_lat;
   a.lse = lse;
@@ -416,6 +430,40 @@ mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* s
   if (lowbit_cache(d)) NEED_PTR(cache_aux);
   hipStream_t st = (hipStream_t)stream;
   return hip_status(launch_dequant(d, g, geom->batch, cache, cache_aux, out, st), st, "cache dequant");
+}
+
+mla_status mla_qk_norm_prepare(const mla_dims* dims, void* stream, const void* w_uk, const void* g_q,
+                               const void* g_k, void* w_uk_folded, float* gram) {
+  Dims d;
+  CHECK(check_dims(dims, &d));
+  NEED_PTR(w_uk);
+  NEED_PTR(g_q);
+  NEED_PTR(g_k);
+  NEED_PTR(w_uk_folded);
+  NEED_PTR(gram);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_qkn_prepare(d, w_uk, g_q, g_k, w_uk_folded, gram, st), st, "QK-norm weight preparation");
+}
+
+mla_status mla_cache_key_norm(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_tokens,
+                              const int32_t* frame, const float* gram, const void* cache, void* cache_aux) {
+  Dims d;
+  Geo g;
+  CHECK(check_dims(dims, &d));
+  CHECK(check_geom(geom, d, &g));
+  if (!d.qk_norm) return fail(MLA_ERR_INVALID_ARG, "mla_cache_key_norm needs dims->qk_norm = 1");
+  if (n_tokens < 0) return fail(MLA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens % g.P) return fail(MLA_ERR_INVALID_ARG, "n_tokens (%d) must be a multiple of P (%d)", n_tokens, g.P);
+  if (n_tokens / g.P > g.window)
+    return fail(MLA_ERR_INVALID_ARG, "more frames (%d) than the window (%d)", n_tokens / g.P, g.window);
+  if (geom->batch == 0 || n_tokens == 0) return MLA_OK;
+  NEED_PTR(frame);
+  NEED_PTR(gram);
+  NEED_PTR(cache);
+  NEED_PTR(cache_aux);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(launch_key_norm(d, g, geom->batch, n_tokens, frame, gram, cache, cache_aux, st), st,
+                    "key inverse RMS");
 }
 
 mla_status mla_cache_rope_shift(const mla_dims* dims, const mla_geom* geom, void* stream, const int32_t* delta,

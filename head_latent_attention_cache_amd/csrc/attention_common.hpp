@@ -66,6 +66,12 @@ __device__ __forceinline__ void mfma_vgpr_settle(f32x16_t& acc) {
   asm volatile("s_nop 15\n\ts_nop 3" : "+v"(acc));
 }
 
+// wait states between a VALU write of the accumulator and an MFMA reading it
+// (as the accumulator operand of the chain's next step)
+__device__ __forceinline__ void mfma_vgpr_after_valu(f32x16_t& acc) {
+  asm volatile("s_nop 4" : "+v"(acc));
+}
+
 // max / sum of a value over the two 32-lane halves of a wave (lane l and
 // lane l ^ 32), with v_permlane32_swap (a VALU op; no LDS round trip): the
 // swap of x with itself yields, per lane, the pair {own, other} in some order

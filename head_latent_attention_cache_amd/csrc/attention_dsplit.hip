@@ -446,7 +446,8 @@ bool attn_dsplit_supported(const Dims& d) {
     const char* e = getenv("MLA_ATTN_KERNEL");
     return e && strcmp(e, "generic") == 0;
   }();
-  if (generic || d.dtype != MLA_BF16 || d.cache_fmt != MLA_CACHE_DENSE || d.d_c != 512) return false;
+  // (QK normalisation is served by the narrow and the generic kernels)
+  if (generic || d.dtype != MLA_BF16 || d.cache_fmt != MLA_CACHE_DENSE || d.d_c != 512 || d.qk_norm) return false;
   return d.d_r == 512 || (d.d_r == 64 && dsplit_forced());
 }
 

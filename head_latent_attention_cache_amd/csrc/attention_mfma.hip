@@ -59,14 +59,14 @@ constexpr int PREAD_AHEAD = 3;           // score steps between the probability 
 template <int DC, int DR, int CB>
 constexpr int q4_stage_bytes() { return MF_BN * (DC * CB / 8 + DR / 2) + MF_BN * (DC / 32) * 2 + MF_BN * 2; }
 
-template <int DC, int DR, bool Q4, int CB = 4>
+template <int DC, int DR, bool Q4, int CB = 4, bool QKN = false>
 constexpr size_t attn_mfma_lds_bytes() {
   return (size_t)(Q4 ? 2 : MF_NBUF) * ((DC + DR) / 64) * MF_BN * 128 +
          (Q4 ? 2 * (size_t)q4_stage_bytes<DC, DR, CB>() : 0) + (size_t)MF_WAVES * MF_QLDS_STEPS * 1024 +
-         2 * MF_WAVES * 2 * 1024 + MF_ROWS * sizeof(float) + MF_MAX_TPS;
+         2 * MF_WAVES * 2 * 1024 + MF_ROWS * sizeof(float) + (QKN ? 3 * MF_BN * sizeof(float) : 0) + MF_MAX_TPS;
 }
 
-template <int DC, int DR, bool Q4, int CB = 4>
+template <int DC, int DR, bool Q4, int CB = 4, bool QKN = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(MfmaArgs ma) {
   constexpr int DQK = DC + DR;
@@ -89,7 +89,8 @@ void attn_mfma_kernel(MfmaArgs ma) {
   uint8_t* qlds = stg + 2 * STG_BYTES;                      // [wave][NKS_LDS][64][16 B]
   uint8_t* plds = qlds + MF_WAVES * NKS_LDS * 1024;         // [2][wave][2 steps][64][16 B]
   float* lrow = (float*)(plds + 2 * MF_WAVES * 2 * 1024);   // [128] row sums
-  uint8_t* cls = (uint8_t*)(lrow + MF_ROWS);
+  float* ksl = lrow + MF_ROWS;                              // QK norm: [3][MF_BN] key inverse RMS per tile
+  uint8_t* cls = (uint8_t*)(ksl + (QKN ? 3 * MF_BN : 0));
   const AttnArgs& a = ma.a;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -152,10 +153,12 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // (zeroed later).  The pieces are issued between the score MFMAs of the
   // current tile: each LDS-DMA instruction takes the wave a while to issue,
   // and there it overlaps the matrix work.
-  struct DmaPlan { const uint8_t* tb; uint32_t voff, lds0; };
+  struct DmaPlan { const uint8_t* tb; uint32_t voff, lds0; int tile, kslot; };
   auto dma_plan = [&](int i, int buf) -> DmaPlan {
     const int k0 = (t_begin + i) * MF_BN;
     DmaPlan d;
+    d.tile = i;
+    d.kslot = buf;
     d.tb = (const uint8_t*)(cache_b + (size_t)k0 * DQK);
     d.lds0 = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * TILE_BYTES) + wave * 1024;
     d.voff = dma_off;
@@ -166,10 +169,24 @@ void attn_mfma_kernel(MfmaArgs ma) {
     return d;
   };
   auto dma_piece = [&](const DmaPlan& d, int q) { dma16_sv(d.tb + q * 128, d.voff, d.lds0 + q * 4096); };
+  // QK normalisation: the tile's 32 key inverse RMS values into LDS slot
+  // `slot` (one dword per lane of the first half-wave; past-the-end keys read
+  // the last slot)
+  const float* ksc_row = QKN ? a.kscale + (size_t)b * cap : nullptr;
+  auto ksl_dma = [&](int i, int slot) {
+    if constexpr (QKN) {
+      if (wave == 0 && lane < MF_BN) {
+        const float* src = ksc_row + min((t_begin + i) * MF_BN + lane, cap - 1);
+        const uint32_t dst = (uint32_t)(uintptr_t)(LDS_AS float*)(ksl + slot * MF_BN);
+        asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+      }
+    }
+  };
   auto issue_loads = [&](int i, int buf) {
     const DmaPlan d = dma_plan(i, buf);
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) dma_piece(d, q);
+    ksl_dma(i, buf);
   };
   // the first tile's copy is in flight while the queries load
   if (!Q4 && first < ntl) issue_loads(first, 0);
@@ -400,7 +417,12 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // INT4: with do_dq, the next tile is dequantised into buffer vprev during
   // the chain: once every wave holds its value fragments of vprev (a barrier
   // after their reads), one 64-dim group every third step.
-  auto qk_scores = [&](const uint8_t* tile, const DmaPlan& dp, bool dma, PVFrag& f, int vprev, int pprev,
+  // QK normalisation: the content part of a key's score (the first DC / 16
+  // steps of the chain) is multiplied by the key's inverse RMS (LDS slot
+  // kslot, read QKN_LEAD steps ahead) before the rotary steps accumulate
+  // onto it
+  constexpr int NKS_C = DC / 16, QKN_LEAD = 2;
+  auto qk_scores = [&](const uint8_t* tile, int kslot, const DmaPlan& dp, bool dma, PVFrag& f, int vprev, int pprev,
                        bool do_dq, const DqPlan& dqp) -> f32x16_t {
     // the score accumulator lives in VGPRs (mfma_vgpr): the 256 AGPRs hold
     // the output accumulators, and an AGPR score block would be swapped with
@@ -417,6 +439,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     };
     constexpr int KPF = 4;
     bf16x8_t kb[KPF], qb[KPF];
+    float ksc[QKN ? 16 : 1];
     DqRaw raw[DQ_QK];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
@@ -432,6 +455,24 @@ void attn_mfma_kernel(MfmaArgs ma) {
       }
       if (ks == 0) mfma_vgpr_zero(s, cur_k, cur_q);
       else mfma_vgpr(s, cur_k, cur_q);
+      if constexpr (QKN) {
+        if (dma && ks == 0) ksl_dma(dp.tile, dp.kslot);   // the next tile's values, with its copy
+        if (ks == NKS_C - 1 - QKN_LEAD) {
+          // score element e is key 8 (e / 4) + 4 g + e % 4 of the tile
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            typedef float f32x4_v __attribute__((ext_vector_type(4)));
+            const f32x4_v v = *(const LDS_AS f32x4_v*)(LDS_AS float*)(ksl + kslot * MF_BN + 8 * j + 4 * g);
+            ksc[4 * j] = v[0]; ksc[4 * j + 1] = v[1]; ksc[4 * j + 2] = v[2]; ksc[4 * j + 3] = v[3];
+          }
+        }
+        if (ks == NKS_C - 1) {
+          mfma_vgpr_settle(s);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] *= ksc[e];
+          mfma_vgpr_after_valu(s);
+        }
+      }
       // one piece of the next tile's copy every NKS / LOADS steps
       if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
       if (ks >= 1 && ks <= 2 * NDB) pv_read_v1(vprev, f, (ks - 1) / NDB, (ks - 1) % NDB);
@@ -502,10 +543,10 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // work: the VALU runs while the MFMAs execute).  Before the first tile of a
   // pass the "previous" probabilities are zeros (any finite tile serves as
   // values).
-  auto tile_step = [&](const uint8_t* tile, int k0, int cl, int pbuf, int vprev, int pprev, const DmaPlan& dp,
+  auto tile_step = [&](const uint8_t* tile, int k0, int kslot, int cl, int pbuf, int vprev, int pprev, const DmaPlan& dp,
                        bool dma, bool do_dq, const DqPlan& dqp) {
     PVFrag f;
-    f32x16_t s = qk_scores(tile, dp, dma, f, vprev, pprev, do_dq, dqp);
+    f32x16_t s = qk_scores(tile, kslot, dp, dma, f, vprev, pprev, do_dq, dqp);
     if (cl != TILE_FULL) mask_scores(s, k0);
     if constexpr (Q4) pv_read_p(pprev, f);
     const float neg_m = softmax_max(s);
@@ -597,7 +638,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
       // the previous tile's probabilities were published before this barrier
       // (the copy is issued every step: after the last tile it copies this
       // tile again into the free buffer, which costs less than a branch per piece)
-      tile_step(tile, k0, cl, pb, bprev >= 0 ? bprev : bcur, pb ^ 1, dp, true, false, DqPlan{});
+      tile_step(tile, k0, bcur, cl, pb, bprev >= 0 ? bprev : bcur, pb ^ 1, dp, true, false, DqPlan{});
       bprev = bcur;
       bcur = bnext;
       pb ^= 1;
@@ -615,12 +656,16 @@ void attn_mfma_kernel(MfmaArgs ma) {
     zero_p(1);
     if (cur < ntl) {
       stage_dma(cur, 0);
+      ksl_dma(cur, 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();
       dequant(cur, 0, 0);
     }
     int nxt = next_tile(cur + 1);
-    if (nxt < ntl) stage_dma(nxt, 1);
+    if (nxt < ntl) {
+      stage_dma(nxt, 1);
+      ksl_dma(nxt, 1);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     while (cur < ntl) {
       const int bc = it & 1;
@@ -629,10 +674,13 @@ void attn_mfma_kernel(MfmaArgs ma) {
       // the previous probabilities are published, staging it & 1 is free
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();
-      if (nn < ntl) stage_dma(nn, bc);
+      if (nn < ntl) {
+        stage_dma(nn, bc);
+        ksl_dma(nn, (it + 2) % 3);   // key inverse RMS slots follow the tile sequence mod 3
+      }
       const bool do_dq = nxt < ntl;
       const DqPlan dqp = do_dq ? dequant_plan(nxt, bc ^ 1, bc ^ 1) : DqPlan{};
-      tile_step(smem + bc * TILE_BYTES, (t_begin + cur) * MF_BN, cls[cur], pb, it > 0 ? (bc ^ 1) : bc, pb ^ 1,
+      tile_step(smem + bc * TILE_BYTES, (t_begin + cur) * MF_BN, it % 3, cls[cur], pb, it > 0 ? (bc ^ 1) : bc, pb ^ 1,
                 DmaPlan{nullptr, 0u, 0u}, false, do_dq, dqp);
       ++it;
       pb ^= 1;
@@ -935,12 +983,19 @@ hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStr
   attn_plan_bind(&ma, ws);
   constexpr int DC = 512, DR = 64;
   const int fmt = a.d.cache_fmt;
-  const size_t shm = fmt == MLA_CACHE_INT4   ? attn_mfma_lds_bytes<DC, DR, true, 4>()
-                     : fmt == MLA_CACHE_INT2 ? attn_mfma_lds_bytes<DC, DR, true, 2>()
-                                             : attn_mfma_lds_bytes<DC, DR, false>();
-  auto kern = fmt == MLA_CACHE_INT4   ? attn_mfma_kernel<DC, DR, true, 4>
-              : fmt == MLA_CACHE_INT2 ? attn_mfma_kernel<DC, DR, true, 2>
-                                      : attn_mfma_kernel<DC, DR, false>;
+  const bool qkn = a.kscale != nullptr;
+  const size_t shm = fmt == MLA_CACHE_INT4   ? (qkn ? attn_mfma_lds_bytes<DC, DR, true, 4, true>()
+                                                    : attn_mfma_lds_bytes<DC, DR, true, 4>())
+                     : fmt == MLA_CACHE_INT2 ? (qkn ? attn_mfma_lds_bytes<DC, DR, true, 2, true>()
+                                                    : attn_mfma_lds_bytes<DC, DR, true, 2>())
+                                             : (qkn ? attn_mfma_lds_bytes<DC, DR, false, 4, true>()
+                                                    : attn_mfma_lds_bytes<DC, DR, false>());
+  auto kern = qkn ? (fmt == MLA_CACHE_INT4   ? attn_mfma_kernel<DC, DR, true, 4, true>
+                         : fmt == MLA_CACHE_INT2 ? attn_mfma_kernel<DC, DR, true, 2, true>
+                                                 : attn_mfma_kernel<DC, DR, false, 4, true>)
+                       : (fmt == MLA_CACHE_INT4   ? attn_mfma_kernel<DC, DR, true, 4>
+                         : fmt == MLA_CACHE_INT2 ? attn_mfma_kernel<DC, DR, true, 2>
+                                                 : attn_mfma_kernel<DC, DR, false>);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   kern<<<blocks, 256, shm, st>>>(ma);

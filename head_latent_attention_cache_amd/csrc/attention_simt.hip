@@ -91,7 +91,14 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a, int KT) {
           float dot = 0.f;
           const float* qr = qs + r * dqk;
           const float* kr = ks + k * dqk;
-          for (int j = 0; j < dqk; ++j) dot = fmaf(qr[j], kr[j], dot);
+          if (!a.kscale) {
+            for (int j = 0; j < dqk; ++j) dot = fmaf(qr[j], kr[j], dot);
+          } else {
+            // QK normalisation: the content term times the key's inverse RMS
+            for (int j = 0; j < d.d_c; ++j) dot = fmaf(qr[j], kr[j], dot);
+            dot *= a.kscale[(size_t)b * a.g.capacity + s];
+            for (int j = d.d_c; j < dqk; ++j) dot = fmaf(qr[j], kr[j], dot);
+          }
           v = dot * scale_log2;
         }
       }

@@ -92,6 +92,8 @@ struct Dims {
   int rope_dims, band0, band1, band2;
   float theta, scale;
   int dtype, cache_fmt;
+  int qk_norm;    // 1: QK-normalised attention (per-slot key inverse RMS in the aux buffer)
+  float qk_eps;
 };
 
 // low-bit caches (INT4, INT2): bits per content code, code bytes per cache
@@ -99,6 +101,12 @@ struct Dims {
 __host__ __device__ __forceinline__ bool lowbit_cache(const Dims& d) { return d.cache_fmt != MLA_CACHE_DENSE; }
 __host__ __device__ __forceinline__ int content_bits(const Dims& d) { return d.cache_fmt == MLA_CACHE_INT2 ? 2 : 4; }
 __host__ __device__ __forceinline__ int code_row_bytes(const Dims& d) { return d.d_c * content_bits(d) / 8 + d.d_r / 2; }
+
+// byte offset of the per-slot key inverse RMS (QK normalisation) in the aux
+// buffer of `rows` slots: after the fp16 scales of a low-bit cache, 16-byte aligned
+__host__ __device__ __forceinline__ size_t key_scale_offset(const Dims& d, size_t rows) {
+  return lowbit_cache(d) ? (rows * (d.d_c / 32 + 1) * 2 + 15) / 16 * 16 : 0;
+}
 
 // integer code of element j of a low-bit cache row (two's complement, the
 // lowest bits first: INT4 element 2i in the low nibble of byte i, INT2

@@ -29,12 +29,18 @@ struct AttnArgs {
   const int* newest;
   const void* cache;
   const __half* aux;
+  const float* kscale = nullptr;   // QK normalisation: per-slot key inverse RMS [B, capacity], else null
   int batch;
   void* o_lat;
   float* lse;
 };
 
 hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st);
+hipError_t launch_qkn_prepare(const Dims& d, const void* w_uk, const void* g_q, const void* g_k, void* w_uk_folded,
+                              float* gram, hipStream_t st);
+hipError_t launch_key_norm(const Dims& d, const Geo& g, int batch, int n_tokens, const int* frame, const float* gram,
+                           const void* cache, void* aux, hipStream_t st);
+hipError_t launch_q_norm(const Dims& d, int batch, int n_q, const void* q_nope, void* q_abs, hipStream_t st);
 hipError_t launch_fold_query(const Dims& d, int d_cq, const void* w_uq, const void* w_uk, void* w_fold,
                              hipStream_t st);
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,

@@ -100,6 +100,8 @@ typedef struct {
   float softmax_scale; /* <= 0 selects 1/sqrt(d_nope + d_r) */
   int32_t dtype;       /* MLA_F32 or MLA_BF16 */
   int32_t cache_fmt;   /* MLA_CACHE_DENSE, MLA_CACHE_INT4 or MLA_CACHE_INT2 (low-bit: MLA_BF16 only) */
+  int32_t qk_norm;     /* 1: QK-normalised attention (see "QK normalisation"), 0: off */
+  float qk_norm_eps;   /* >= 0, added to the mean square inside the root (qk_norm = 1) */
 } mla_dims;
 
 /* Cache geometry shared by every sequence of a batch. */
@@ -130,6 +132,10 @@ typedef struct {
  *     cache_aux = as for INT4.  Content: scale = fp16(amax / 1), code =
  *     round-half-even of x / scale clamped to [-2, 1] (so -1, 0 or 1);
  *     rotary key as for INT4.
+ *   QK normalisation on (dims->qk_norm = 1), any format: cache_aux also holds
+ *     one float per slot, the key's inverse RMS [B, capacity], at byte offset
+ *     0 (DENSE) or after the fp16 scales rounded up to 16 bytes (INT4, INT2);
+ *     written by mla_cache_key_norm.
  * Both functions return 0 when the arguments are invalid.
  */
 size_t mla_cache_bytes(const mla_dims* dims, const mla_geom* geom);
@@ -167,10 +173,41 @@ mla_status mla_cache_append(const mla_dims* dims, const mla_geom* geom, void* st
  *   q_first [B] int32 (device)
  *   w_uk    [H, d_c, d_nope]   w_uk[h] = (W^UK_h)^T, W^UK_h mapping c to the head's content key
  *   q_abs   [B, n_q, H, d_c + d_r]
+ * With dims->qk_norm = 1 the content part is multiplied by inv_q of the token
+ * (see "QK normalisation"; w_uk is then the folded weight).
  */
 mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
                         const void* q_nope, const void* q_rope, const int32_t* q_first,
                         const void* w_uk, void* q_abs);
+
+/*
+ * QK normalisation ([MLA topics, QK-Norm abstract]: post-projection RMSNorm of
+ * query and key splits into a static per-dimension weight, which folds into
+ * the query side, and a dynamic RMS statistic, which for the key is one
+ * scalar per token because every head's key comes from the one cached latent).
+ * With g_q, g_k [H, d_nope] the norm weights and rms(v) = sqrt(mean(v^2) + eps)
+ * over the H * d_nope content values of one token (all heads together), the
+ * score of head h is
+ *     scale * ( (g_q . q_h / rms(q)) . (g_k . W^UK_h c / rms(W^UK c)) + q_rope . k_rope )
+ *   = scale * ( inv_q * inv_k * (w_uk'[h] q_h) . c + q_rope . k_rope )
+ * with w_uk'[h][a][i] = w_uk[h][a][i] g_q[h][i] g_k[h][i] (folded at load
+ * time), inv_q = 1 / rms(q_nope) (applied by mla_absorb_q) and
+ * inv_k = 1 / sqrt(c^T G c / (H d_nope) + eps), G = sum_h w_uk[h] w_uk[h]^T
+ * (stored per slot by mla_cache_key_norm, applied to the content score by
+ * mla_attention).  The rotary parts are not normalised.
+ * mla_qk_norm_prepare (load time):
+ *   w_uk [H, d_c, d_nope] (unweighted), g_q, g_k [H, d_nope] (dims->dtype)
+ *   -> w_uk_folded [H, d_c, d_nope] (dims->dtype; pass it to mla_absorb_q)
+ *      gram [d_c, d_c] float (pass it to mla_cache_key_norm)
+ * mla_cache_key_norm: after mla_cache_append with the same n_tokens and
+ *   frame (or after rows were written otherwise), stores inv_k of those rows,
+ *   computed from the stored latent (what attention reads).
+ * With qk_norm = 1, mla_absorb_q_folded returns MLA_ERR_UNSUPPORTED.
+ */
+mla_status mla_qk_norm_prepare(const mla_dims* dims, void* stream, const void* w_uk, const void* g_q,
+                               const void* g_k, void* w_uk_folded, float* gram);
+mla_status mla_cache_key_norm(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_tokens,
+                              const int32_t* frame, const float* gram, const void* cache, void* cache_aux);
 
 /*
  * Low-rank query with the key up-projection folded in when the weights are
@@ -207,6 +244,8 @@ mla_status mla_absorb_q_folded(const mla_dims* dims, const mla_geom* geom, void*
  *     o_lat[b, t, h] = sum_s softmax(a)_s * cache_row[b, s, 0 : d_c]
  *     lse[b, t, h]   = log sum_s exp(a_s)
  * A row with no visible key gives o_lat = 0 and lse = -inf.
+ * With dims->qk_norm = 1 the content part of a_s (the first d_c terms) is
+ * multiplied by the slot's stored inv_k (see "QK normalisation").
  *   q_abs   [B, n_q, H, d_c + d_r]; q_first [B], newest [B] int32 (device)
  *   o_lat   [B, n_q, H, d_c]; lse [B, n_q, H] float, or NULL
  *   workspace: >= mla_attention_workspace_size() bytes (split-key partials).

@@ -41,6 +41,8 @@ class MLAConfig:
     cache_given: bool = False  # decode: earlier positions' rows are given; only the
                                # newest frame is appended
     d_cq: int = 1536     # low-rank query latent width (load-time fold of W^UQ and W^UK)
+    qk_norm: bool = False  # QK-normalised attention (RMSNorm of all heads' content query / key)
+    qk_eps: float = 1e-6
 
     # ---- derived -------------------------------------------------------
     @property

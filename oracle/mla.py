@@ -387,7 +387,7 @@ def attend_qk_norm(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, g_q, g_k, eps: float
         ts = np.array([tokens[i][1] for i in idx])
         C = st["values"][b, :, :cfg.d_c]
         KR = st["values"][b, :, cfg.d_c:]
-        k_all = rms_normalise(np.einsum("sc,hci->shi", C, w_uk), g_k, eps)     # [S, H, d_nope]
+        k_all = rms_normalise(np.matmul(C, w_uk).transpose(1, 0, 2), g_k, eps)  # [S, H, d_nope]
         q_all = rms_normalise(np.asarray(q_nope, np.float64)[b, ts], g_q, eps)  # [T, H, d_nope]
         mask = mask_all[ts]
         for h in range(H):

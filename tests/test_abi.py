@@ -85,6 +85,8 @@ BAD_DIMS = [
     ("dtype", dict(dtype=7)),
     ("int4 with fp32", dict(cache_fmt=1)),
     ("int2 with fp32", dict(cache_fmt=2)),
+    ("qk_norm flag", dict(qk_norm=2)),
+    ("qk_norm eps negative", dict(qk_norm=1, qk_norm_eps=-1.0)),
     ("unknown cache format", dict(cache_fmt=3)),
 ]
 
@@ -194,3 +196,30 @@ def test_query_fold_width_checked(lib, d_cq, status):
     assert lib.mla_absorb_q_folded(ctypes.byref(d), ctypes.byref(g), None, 4, d_cq, fake, fake, fake, fake,
                                    fake) == status
     assert lib.mla_last_error()
+
+
+@pytest.mark.parametrize("key", [3, 5])
+def test_qk_norm_aux_bytes(lib, key):
+    cfg = CONFIGS[key]
+    d, g = _dims(cfg), _geom(cfg)
+    base = lib.mla_cache_aux_bytes(ctypes.byref(d), ctypes.byref(g))
+    d.qk_norm, d.qk_norm_eps = 1, 1e-6
+    na = lib.mla_cache_aux_bytes(ctypes.byref(d), ctypes.byref(g))
+    rows = cfg.batch * cfg.capacity
+    assert na == (base + 15) // 16 * 16 + 4 * rows
+
+
+def test_qk_norm_entry_checks(lib):
+    cfg = SMALL_CONFIGS[3]
+    d, g = _dims(cfg), _geom(cfg)
+    fake = ctypes.c_void_p(0x1000)
+    # key norm without qk_norm set
+    assert lib.mla_cache_key_norm(ctypes.byref(d), ctypes.byref(g), None, cfg.tokens_per_frame, fake, fake, fake,
+                                  fake) == _lib.MLA_ERR_INVALID_ARG
+    d.qk_norm, d.qk_norm_eps = 1, 1e-6
+    # a token count that is not a whole number of frames
+    assert lib.mla_cache_key_norm(ctypes.byref(d), ctypes.byref(g), None, cfg.tokens_per_frame + 1, fake, fake,
+                                  fake, fake) == _lib.MLA_ERR_INVALID_ARG
+    # the folded-query absorb has no query content values to normalise
+    assert lib.mla_absorb_q_folded(ctypes.byref(d), ctypes.byref(g), None, 4, 64, fake, fake, fake, fake,
+                                   fake) == _lib.MLA_ERR_UNSUPPORTED
