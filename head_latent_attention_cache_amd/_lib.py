@@ -50,7 +50,9 @@ SIGNATURES = {
     "mla_absorb_q_folded": (c_int, [_D, _G, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
     "mla_qk_norm_prepare": (c_int, [_D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
-    "mla_cache_key_norm": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "mla_key_norm_workspace_size": (c_size_t, [_D, _G, c_int32]),
+    "mla_cache_key_norm": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_size_t]),
     "mla_attention_workspace_size": (c_size_t, [_D, _G, c_int32]),
     "mla_attention": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t]),

@@ -216,15 +216,23 @@ def qk_norm_prepare(dims, w_uk, g_q, g_k, w_uk_folded, gram):
                                   _ptr(gram)))
 
 
-def cache_key_norm(dims, geom, n_tokens, frame, gram, cache, cache_aux):
+def key_norm_workspace_bytes(dims, geom, n_tokens):
+    return int(load().mla_key_norm_workspace_size(_rd(dims), _rd(geom), int(n_tokens)))
+
+
+def cache_key_norm(dims, geom, n_tokens, frame, gram, cache, cache_aux, workspace=None):
     """Key inverse RMS of the rows of n_tokens tokens written at frame[b]
     onwards (the arguments of the matching mla_cache_append)."""
     lib = load()
     _check_cache(dims, geom, cache, cache_aux)
     _need(frame, "frame", torch.int32, geom.batch)
     _need(gram, "gram", torch.float32, dims.d_c * dims.d_c)
+    need = key_norm_workspace_bytes(dims, geom, n_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=cache.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib.mla_cache_key_norm(_rd(dims), _rd(geom), _stream(), int(n_tokens), _ptr(frame), _ptr(gram),
-                                 _ptr(cache), _ptr(cache_aux)))
+                                 _ptr(cache), _ptr(cache_aux), _ptr(workspace), nbytes))
 
 
 def attention_workspace_bytes(dims, geom, n_q):

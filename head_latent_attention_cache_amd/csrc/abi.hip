@@ -79,6 +79,8 @@ mla_status check_dims(const mla_dims* dm, Dims* d) {
   if (dm->qk_norm != 0 && dm->qk_norm != 1) return fail(MLA_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
   if (dm->qk_norm && !(dm->qk_norm_eps >= 0.f && dm->qk_norm_eps < 1e30f))
     return fail(MLA_ERR_INVALID_ARG, "qk_norm_eps must be finite and >= 0");
+  if (dm->qk_norm && dm->d_c % 32)
+    return fail(MLA_ERR_UNSUPPORTED, "QK normalisation needs d_c divisible by 32, got %d", dm->d_c);
   const int dqk = dm->d_c + dm->d_r;
   if (dm->d_c > 1024 || dqk > 1536)
     return fail(MLA_ERR_UNSUPPORTED, "d_c <= 1024 and d_c + d_r <= 1536 are supported");
@@ -260,11 +262,7 @@ mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream
   ga.out_f32 = 0;
   hipError_t e = launch_gemm_nt(d.dtype, ga, st);
   if (e != hipSuccess) return hip_status(e, st, "absorb projection");
-  if (d.qk_norm) {
-    e = launch_q_norm(d, B, n_q, q_nope, q_abs, st);
-    if (e != hipSuccess) return hip_status(e, st, "query inverse RMS");
-  }
-  e = launch_q_rope(d, g, B, q_rope, n_q, q_first, q_abs, st);
+  e = launch_q_rope(d, g, B, q_rope, n_q, q_first, q_nope, q_abs, st);
   return hip_status(e, st, "query rotary");
 }
 
@@ -318,7 +316,7 @@ mla_status mla_absorb_q_folded(const mla_dims* dims, const mla_geom* geom, void*
   ga.out_f32 = 0;
   hipError_t e = launch_gemm_nt(d.dtype, ga, st);
   if (e != hipSuccess) return hip_status(e, st, "folded absorb projection");
-  e = launch_q_rope(d, g, B, q_rope, n_q, q_first, q_abs, st);
+  e = launch_q_rope(d, g, B, q_rope, n_q, q_first, nullptr, q_abs, st);
   return hip_status(e, st, "query rotary");
 }
 
@@ -445,8 +443,21 @@ mla_status mla_qk_norm_prepare(const mla_dims* dims, void* stream, const void* w
   return hip_status(launch_qkn_prepare(d, w_uk, g_q, g_k, w_uk_folded, gram, st), st, "QK-norm weight preparation");
 }
 
+static size_t key_norm_ws_bytes(const Dims& d, int batch, int n_tokens) {
+  const int z = key_norm_slices(d, batch, n_tokens);
+  return z > 1 ? (size_t)z * batch * n_tokens * sizeof(float) : 0;
+}
+
+size_t mla_key_norm_workspace_size(const mla_dims* dims, const mla_geom* geom, int32_t n_tokens) {
+  Dims d;
+  Geo g;
+  if (check_dims(dims, &d) != MLA_OK || check_geom(geom, d, &g) != MLA_OK || n_tokens < 0) return 0;
+  return key_norm_ws_bytes(d, geom->batch, n_tokens);
+}
+
 mla_status mla_cache_key_norm(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_tokens,
-                              const int32_t* frame, const float* gram, const void* cache, void* cache_aux) {
+                              const int32_t* frame, const float* gram, const void* cache, void* cache_aux,
+                              void* workspace, size_t workspace_bytes) {
   Dims d;
   Geo g;
   CHECK(check_dims(dims, &d));
@@ -461,9 +472,12 @@ mla_status mla_cache_key_norm(const mla_dims* dims, const mla_geom* geom, void* 
   NEED_PTR(gram);
   NEED_PTR(cache);
   NEED_PTR(cache_aux);
+  const size_t need = key_norm_ws_bytes(d, geom->batch, n_tokens);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "key norm workspace needs %zu bytes, got %zu", need, workspace_bytes);
   hipStream_t st = (hipStream_t)stream;
-  return hip_status(launch_key_norm(d, g, geom->batch, n_tokens, frame, gram, cache, cache_aux, st), st,
-                    "key inverse RMS");
+  return hip_status(launch_key_norm(d, g, geom->batch, n_tokens, frame, gram, cache, cache_aux, (float*)workspace, st),
+                    st, "key inverse RMS");
 }
 
 mla_status mla_cache_rope_shift(const mla_dims* dims, const mla_geom* geom, void* stream, const int32_t* delta,

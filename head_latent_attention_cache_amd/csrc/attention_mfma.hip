@@ -419,9 +419,10 @@ void attn_mfma_kernel(MfmaArgs ma) {
   // after their reads), one 64-dim group every third step.
   // QK normalisation: the content part of a key's score (the first DC / 16
   // steps of the chain) is multiplied by the key's inverse RMS (LDS slot
-  // kslot, read QKN_LEAD steps ahead) before the rotary steps accumulate
-  // onto it
-  constexpr int NKS_C = DC / 16, QKN_LEAD = 2;
+  // kslot) before the rotary steps accumulate onto it.  The values are read
+  // QKN_LEAD steps ahead: 0 measured best (registers held across steps cost
+  // spills that outweigh the exposed LDS latency)
+  constexpr int NKS_C = DC / 16, QKN_LEAD = 0;
   auto qk_scores = [&](const uint8_t* tile, int kslot, const DmaPlan& dp, bool dma, PVFrag& f, int vprev, int pprev,
                        bool do_dq, const DqPlan& dqp) -> f32x16_t {
     // the score accumulator lives in VGPRs (mfma_vgpr): the 256 AGPRs hold

@@ -38,15 +38,15 @@ struct AttnArgs {
 hipError_t launch_gemm_nt(int dtype, const GemmArgs& a, hipStream_t st);
 hipError_t launch_qkn_prepare(const Dims& d, const void* w_uk, const void* g_q, const void* g_k, void* w_uk_folded,
                               float* gram, hipStream_t st);
+int key_norm_slices(const Dims& d, int batch, int n_tokens);
 hipError_t launch_key_norm(const Dims& d, const Geo& g, int batch, int n_tokens, const int* frame, const float* gram,
-                           const void* cache, void* aux, hipStream_t st);
-hipError_t launch_q_norm(const Dims& d, int batch, int n_q, const void* q_nope, void* q_abs, hipStream_t st);
+                           const void* cache, void* aux, float* partial, hipStream_t st);
 hipError_t launch_fold_query(const Dims& d, int d_cq, const void* w_uq, const void* w_uk, void* w_fold,
                              hipStream_t st);
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
                                const int* frame, void* cache, void* aux, int nsplit, hipStream_t st);
 hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,
-                         const int* q_first, void* q_abs, hipStream_t st);
+                         const int* q_first, const void* q_nope, void* q_abs, hipStream_t st);
 hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* cache, const void* aux,
                           float* out, hipStream_t st);
 hipError_t launch_rope_shift(const Dims& d, const Geo& g, int batch, const int* delta, int slot_begin,

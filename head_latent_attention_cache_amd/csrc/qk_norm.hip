@@ -71,105 +71,97 @@ __global__ __launch_bounds__(256) void qkn_gram_kernel(Dims d, const T* __restri
 // ---------------------------------------------------------------------------
 // inv_k of the rows of appended tokens: token i of sequence b (frame
 // frame[b] + i / P, tok i % P) -> slot; c = the stored latent (low-bit:
-// dequantised); t = G c (G symmetric: column j read as row j, coalesced),
-// inv_k = 1 / sqrt(c . t / (H d_nope) + eps).  grid (ceil(n_tokens / tpb),
-// B), tpb <= KN_TOK tokens per work-group (their latents in LDS); thread
-// owns columns j = tid + 256 u.
+// dequantised); inv_k = 1 / sqrt(c^T G c / (H d_nope) + eps).  grid
+// (ceil(n_tokens / TPB), B, slices): the work-group's TPB latents sit in LDS
+// (read as broadcasts); it takes the rows [z rows_per_slice, ...) of G, thread
+// tid the rows k = tid + 256 u of those (16-byte loads along the row, each
+// used for all TPB tokens; G stays resident in L2), accumulates c_k (G_k . c)
+// per token, and the partial sums are added by a fixed tree.  With one slice
+// the work-group writes inv_k; with several (few tokens: the rows of G spread
+// over more work-groups) it writes its partial sum to `partial`
+// [slices][B][n_tokens] and key_norm_finish adds them in slice order.  The
+// result does not depend on scheduling.
 // ---------------------------------------------------------------------------
-constexpr int KN_TOK = 16;
-constexpr int KN_MAXU = 4;   // d_c <= 1024
-
-template <typename T, bool LOWBIT>
-__global__ __launch_bounds__(256) void key_norm_kernel(Dims d, Geo g, int batch, int n_tokens, int tpb,
+template <typename T, bool LOWBIT, int TPB>
+__global__ __launch_bounds__(256) void key_norm_kernel(Dims d, Geo g, int batch, int n_tokens, int rows_per_slice,
                                                        const int* __restrict__ frame, const float* __restrict__ gram,
                                                        const void* __restrict__ cache, const __half* __restrict__ aux,
-                                                       float* __restrict__ kscale) {
-  extern __shared__ float cs[];                 // [KN_TOK][d_c]
-  __shared__ float red[4][KN_TOK];
-  const int b = blockIdx.y, i0 = blockIdx.x * tpb;
-  const int nt = min(tpb, n_tokens - i0);
+                                                       float* __restrict__ kscale, float* __restrict__ partial) {
+  extern __shared__ __attribute__((aligned(16))) float cs[];   // [TPB][d_c]
+  __shared__ float red[4][TPB];
+  const int b = blockIdx.y, i0 = blockIdx.x * TPB;
+  const int nt = min(TPB, n_tokens - i0);
   const int ng = d.d_c / 32;
-  auto slot_of = [&](int i) { return ring_slot(g, frame[b] + i / g.P, i % g.P); };
-  for (int e = threadIdx.x; e < nt * d.d_c; e += blockDim.x) {
+  auto srow_of = [&](int t) {
+    return (size_t)b * g.capacity + ring_slot(g, frame[b] + (i0 + t) / g.P, (i0 + t) % g.P);
+  };
+  for (int e = threadIdx.x; e < TPB * d.d_c; e += blockDim.x) {
     const int t = e / d.d_c, j = e % d.d_c;
-    const size_t srow = (size_t)b * g.capacity + slot_of(i0 + t);
-    float v;
-    if (!LOWBIT) {
-      v = Elem<T>::load((const T*)cache, srow * d.d_qk + j);
-    } else {
-      const int q = lowbit_code((const uint8_t*)cache + srow * code_row_bytes(d), d, j);
-      v = (float)q * __half2float(aux[srow * ng + j / 32]);
+    float v = 0.f;
+    if (t < nt) {
+      const size_t srow = srow_of(t);
+      if (!LOWBIT) {
+        v = Elem<T>::load((const T*)cache, srow * d.d_qk + j);
+      } else {
+        const int q = lowbit_code((const uint8_t*)cache + srow * code_row_bytes(d), d, j);
+        v = (float)q * __half2float(aux[srow * ng + j / 32]);
+      }
     }
-    cs[t * d.d_c + j] = v;
+    cs[e] = v;
   }
   __syncthreads();
-  float acc[KN_TOK][KN_MAXU];
+  float p[TPB];
 #pragma unroll
-  for (int t = 0; t < KN_TOK; ++t)
+  for (int t = 0; t < TPB; ++t) p[t] = 0.f;
+  const int k_end = min(d.d_c, (int)(blockIdx.z + 1) * rows_per_slice);
+  for (int k = blockIdx.z * rows_per_slice + threadIdx.x; k < k_end; k += blockDim.x) {
+    const float4* gk = (const float4*)(gram + (size_t)k * d.d_c);
+    float dot[TPB];
 #pragma unroll
-    for (int u = 0; u < KN_MAXU; ++u) acc[t][u] = 0.f;
-  for (int k = 0; k < d.d_c; ++k) {
-    float gk[KN_MAXU];
+    for (int t = 0; t < TPB; ++t) dot[t] = 0.f;
+#pragma unroll 16
+    for (int j4 = 0; j4 < d.d_c / 4; ++j4) {
+      const float4 gv = gk[j4];
 #pragma unroll
-    for (int u = 0; u < KN_MAXU; ++u) {
-      const int j = threadIdx.x + 256 * u;
-      gk[u] = j < d.d_c ? gram[(size_t)k * d.d_c + j] : 0.f;
+      for (int t = 0; t < TPB; ++t) {
+        const float4 cv = *(const float4*)(cs + t * d.d_c + 4 * j4);
+        dot[t] = fmaf(gv.x, cv.x, dot[t]);
+        dot[t] = fmaf(gv.y, cv.y, dot[t]);
+        dot[t] = fmaf(gv.z, cv.z, dot[t]);
+        dot[t] = fmaf(gv.w, cv.w, dot[t]);
+      }
     }
 #pragma unroll
-    for (int t = 0; t < KN_TOK; ++t) {
-      const float c = t < nt ? cs[t * d.d_c + k] : 0.f;
-#pragma unroll
-      for (int u = 0; u < KN_MAXU; ++u) acc[t][u] = fmaf(gk[u], c, acc[t][u]);
-    }
+    for (int t = 0; t < TPB; ++t) p[t] = fmaf(cs[t * d.d_c + k], dot[t], p[t]);
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int t = 0; t < KN_TOK; ++t) {
-    float p = 0.f;
-#pragma unroll
-    for (int u = 0; u < KN_MAXU; ++u) {
-      const int j = threadIdx.x + 256 * u;
-      if (j < d.d_c && t < nt) p = fmaf(cs[t * d.d_c + j], acc[t][u], p);
-    }
-    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-    if (lane == 0) red[wave][t] = p;
+  for (int t = 0; t < TPB; ++t) {
+    float v = p[t];
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][t] = v;
   }
   __syncthreads();
   if (threadIdx.x < nt) {
     const int t = threadIdx.x;
-    const float q = red[0][t] + red[1][t] + red[2][t] + red[3][t];
-    const float ms = q / (float)(d.H * d.d_nope) + d.qk_eps;
-    kscale[(size_t)b * g.capacity + slot_of(i0 + t)] = ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
+    const float q = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    if (partial) {
+      partial[((size_t)blockIdx.z * batch + b) * n_tokens + i0 + t] = q;
+    } else {
+      const float ms = q / (float)(d.H * d.d_nope) + d.qk_eps;
+      kscale[srow_of(t)] = ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
+    }
   }
 }
 
-// ---------------------------------------------------------------------------
-// query side: q_abs[b, t, :, 0:d_c] *= inv_q, inv_q = 1 / sqrt(mean over all
-// heads of q_nope[b, t]^2 + eps).  grid (n_q, B).
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void q_norm_kernel(Dims d, int n_q, const T* __restrict__ q_nope,
-                                                     T* __restrict__ q_abs) {
-  __shared__ float red[4];
-  const int t = blockIdx.x, b = blockIdx.y;
-  const size_t tok = (size_t)b * n_q + t;
-  const int n = d.H * d.d_nope;
-  const T* q = q_nope + tok * n;
-  float p = 0.f;
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const float v = Elem<T>::load(q, e);
-    p = fmaf(v, v, p);
-  }
-  for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = p;
-  __syncthreads();
-  const float ms = (red[0] + red[1] + red[2] + red[3]) / (float)n + d.qk_eps;
-  const float inv = ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
-  T* out = q_abs + tok * d.H * d.d_qk;
-  for (int e = threadIdx.x; e < d.H * d.d_c; e += blockDim.x) {
-    const size_t off = (size_t)(e / d.d_c) * d.d_qk + e % d.d_c;
-    Elem<T>::store(out, off, Elem<T>::load(out, off) * inv);
-  }
+__global__ void key_norm_finish(Dims d, Geo g, int batch, int n_tokens, int slices, const int* __restrict__ frame,
+                                const float* __restrict__ partial, float* __restrict__ kscale) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= batch * n_tokens) return;
+  const int b = e / n_tokens, i = e % n_tokens;
+  float q = 0.f;
+  for (int z = 0; z < slices; ++z) q += partial[((size_t)z * batch + b) * n_tokens + i];
+  const float ms = q / (float)(d.H * d.d_nope) + d.qk_eps;
+  kscale[(size_t)b * g.capacity + ring_slot(g, frame[b] + i / g.P, i % g.P)] = ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -192,29 +184,43 @@ hipError_t launch_qkn_prepare(const Dims& d, const void* w_uk, const void* g_q, 
   return hipGetLastError();
 }
 
-hipError_t launch_key_norm(const Dims& d, const Geo& g, int batch, int n_tokens, const int* frame, const float* gram,
-                           const void* cache, void* aux, hipStream_t st) {
-  const int tpb = d.d_c <= 512 ? KN_TOK : KN_TOK / 2;   // latents staged in at most 32 KB
-  dim3 grid((n_tokens + tpb - 1) / tpb, batch);
-  const size_t shm = (size_t)tpb * d.d_c * sizeof(float);
-  float* kscale = (float*)((char*)aux + key_scale_offset(d, (size_t)batch * g.capacity));
-  if (lowbit_cache(d))
-    key_norm_kernel<bf16_t, true><<<grid, 256, shm, st>>>(d, g, batch, n_tokens, tpb, frame, gram, cache,
-                                                          (const __half*)aux, kscale);
-  else if (d.dtype == MLA_BF16)
-    key_norm_kernel<bf16_t, false><<<grid, 256, shm, st>>>(d, g, batch, n_tokens, tpb, frame, gram, cache, nullptr,
-                                                           kscale);
-  else
-    key_norm_kernel<float, false><<<grid, 256, shm, st>>>(d, g, batch, n_tokens, tpb, frame, gram, cache, nullptr, kscale);
-  return hipGetLastError();
+// row slices of G per token for a call: enough work-groups to spread the
+// reads of G when there are few tokens (decode)
+int key_norm_slices(const Dims& d, int batch, int n_tokens) {
+  const long long groups = (long long)batch * n_tokens;
+  if (groups >= 256) return 1;
+  int z = 1;
+  while (z < 8 && groups * z * 2 <= 512 && d.d_c / (z * 2) >= 64) z *= 2;
+  return z;
 }
 
-hipError_t launch_q_norm(const Dims& d, int batch, int n_q, const void* q_nope, void* q_abs, hipStream_t st) {
-  dim3 grid(n_q, batch);
-  if (d.dtype == MLA_BF16)
-    q_norm_kernel<bf16_t><<<grid, 256, 0, st>>>(d, n_q, (const bf16_t*)q_nope, (bf16_t*)q_abs);
-  else
-    q_norm_kernel<float><<<grid, 256, 0, st>>>(d, n_q, (const float*)q_nope, (float*)q_abs);
+hipError_t launch_key_norm(const Dims& d, const Geo& g, int batch, int n_tokens, const int* frame, const float* gram,
+                           const void* cache, void* aux, float* partial, hipStream_t st) {
+  // one token per work-group for short appends (decode: parallelism), eight
+  // when there are many (each row of G read once per eight tokens)
+  const bool many = n_tokens >= 64;
+  const int tpb = many ? 8 : 1;
+  const int slices = key_norm_slices(d, batch, n_tokens);
+  const int rps = (d.d_c + slices - 1) / slices;
+  if (slices == 1) partial = nullptr;
+  dim3 grid((n_tokens + tpb - 1) / tpb, batch, slices);
+  const size_t shm = (size_t)tpb * d.d_c * sizeof(float);
+  float* kscale = (float*)((char*)aux + key_scale_offset(d, (size_t)batch * g.capacity));
+#define KN_LAUNCH(T, LB, TPB)                                                                              \
+  key_norm_kernel<T, LB, TPB><<<grid, 256, shm, st>>>(d, g, batch, n_tokens, rps, frame, gram, cache,      \
+                                                      (const __half*)aux, kscale, partial)
+  if (lowbit_cache(d)) {
+    if (many) KN_LAUNCH(bf16_t, true, 8); else KN_LAUNCH(bf16_t, true, 1);
+  } else if (d.dtype == MLA_BF16) {
+    if (many) KN_LAUNCH(bf16_t, false, 8); else KN_LAUNCH(bf16_t, false, 1);
+  } else {
+    if (many) KN_LAUNCH(float, false, 8); else KN_LAUNCH(float, false, 1);
+  }
+#undef KN_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !partial) return e;
+  const int n = batch * n_tokens;
+  key_norm_finish<<<(n + 255) / 256, 256, 0, st>>>(d, g, batch, n_tokens, slices, frame, partial, kscale);
   return hipGetLastError();
 }
 

@@ -138,14 +138,19 @@ __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, 
 
 // ---------------------------------------------------------------------------
 // rotary half of the absorbed query: q_abs[b,t,h,d_c:] = RoPE(q_rope[b,t,h])
-// grid (n_q, B)
+// grid (n_q, B, ceil(H / 16)).  QK normalisation ("Multi-Head Latent
+// Attention" topic page, QK-Norm abstract): the work-group also scales its
+// heads' content part by inv_q = 1 / sqrt(mean(q_nope[b, t]^2) + eps), the
+// mean over every head of the token (each work-group of the token computes
+// the same sum in the same order).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n_q,
-                              const int* __restrict__ q_first, T* __restrict__ q_abs) {
+                              const int* __restrict__ q_first, const T* __restrict__ q_nope, T* __restrict__ q_abs) {
   extern __shared__ float smem[];
   float* cosv = smem;
   float* sinv = smem + d.d_r / 2;
+  __shared__ float red[4];
   const int t = blockIdx.x, b = blockIdx.y;
   const int f = q_first[b] + t / g.P, tok = t % g.P;
   double coord[3];
@@ -163,6 +168,54 @@ __global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n
     float c = cosv[p], s = sinv[p];
     Elem<T>::store(dst, 2 * p, x0 * c - x1 * s);
     Elem<T>::store(dst, 2 * p + 1, x0 * s + x1 * c);
+  }
+  if (d.qk_norm) {
+    const int n = d.H * d.d_nope;
+    const T* qn = q_nope + tok_index * n;
+    float acc = 0.f;
+    if constexpr (sizeof(T) == 2) {
+      // bf16: eight values per 16-byte load (n and d_c are multiples of 8)
+      for (int e = threadIdx.x * 8; e < n; e += blockDim.x * 8) {
+        const uint4 v = *(const uint4*)(qn + e);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __uint_as_float(w[k] << 16), hi = __uint_as_float(w[k] & 0xFFFF0000u);
+          acc = fmaf(lo, lo, acc);
+          acc = fmaf(hi, hi, acc);
+        }
+      }
+    } else {
+      for (int e = threadIdx.x; e < n; e += blockDim.x) {
+        const float v = Elem<T>::load(qn, e);
+        acc = fmaf(v, v, acc);
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    const float ms = (red[0] + red[1] + red[2] + red[3]) / (float)n + d.qk_eps;
+    const float inv = ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
+    if constexpr (sizeof(T) == 2) {
+      for (int e = threadIdx.x * 8; e < (h1 - h0) * d.d_c; e += blockDim.x * 8) {
+        T* dst = q_abs + (tok_index * d.H + h0 + e / d.d_c) * d.d_qk + e % d.d_c;
+        uint4 v = *(const uint4*)dst;
+        uint32_t* w = (uint32_t*)&v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __uint_as_float(w[k] << 16) * inv, hi = __uint_as_float(w[k] & 0xFFFF0000u) * inv;
+          w[k] = (uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(lo)) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(hi)) << 16);
+        }
+        *(uint4*)dst = v;
+      }
+    } else {
+      for (int e = threadIdx.x; e < (h1 - h0) * d.d_c; e += blockDim.x) {
+        T* dst = q_abs + (tok_index * d.H + h0 + e / d.d_c) * d.d_qk;
+        const int j = e % d.d_c;
+        Elem<T>::store(dst, j, Elem<T>::load(dst, j) * inv);
+      }
+    }
   }
 }
 
@@ -296,13 +349,15 @@ hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const flo
 }
 
 hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,
-                         const int* q_first, void* q_abs, hipStream_t st) {
+                         const int* q_first, const void* q_nope, void* q_abs, hipStream_t st) {
   dim3 grid(n_q, batch, (d.H + 15) / 16);
   size_t shm = (size_t)d.d_r * sizeof(float);
   if (d.dtype == MLA_BF16)
-    q_rope_kernel<bf16_t><<<grid, 256, shm, st>>>(d, g, (const bf16_t*)q_rope, n_q, q_first, (bf16_t*)q_abs);
+    q_rope_kernel<bf16_t><<<grid, 256, shm, st>>>(d, g, (const bf16_t*)q_rope, n_q, q_first, (const bf16_t*)q_nope,
+                                                  (bf16_t*)q_abs);
   else
-    q_rope_kernel<float><<<grid, 256, shm, st>>>(d, g, (const float*)q_rope, n_q, q_first, (float*)q_abs);
+    q_rope_kernel<float><<<grid, 256, shm, st>>>(d, g, (const float*)q_rope, n_q, q_first, (const float*)q_nope,
+                                                 (float*)q_abs);
   return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ typedef struct {
   int32_t dtype;       /* MLA_F32 or MLA_BF16 */
   int32_t cache_fmt;   /* MLA_CACHE_DENSE, MLA_CACHE_INT4 or MLA_CACHE_INT2 (low-bit: MLA_BF16 only) */
   int32_t qk_norm;     /* 1: QK-normalised attention (see "QK normalisation"), 0: off */
-  float qk_norm_eps;   /* >= 0, added to the mean square inside the root (qk_norm = 1) */
+  float qk_norm_eps;   /* >= 0, added to the mean square inside the root (qk_norm = 1; d_c % 32 == 0) */
 } mla_dims;
 
 /* Cache geometry shared by every sequence of a batch. */
@@ -201,13 +201,17 @@ mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream
  *      gram [d_c, d_c] float (pass it to mla_cache_key_norm)
  * mla_cache_key_norm: after mla_cache_append with the same n_tokens and
  *   frame (or after rows were written otherwise), stores inv_k of those rows,
- *   computed from the stored latent (what attention reads).
+ *   computed from the stored latent (what attention reads); workspace: >=
+ *   mla_key_norm_workspace_size() bytes (0 when the call has many tokens;
+ *   partial sums otherwise, added in a fixed order).
  * With qk_norm = 1, mla_absorb_q_folded returns MLA_ERR_UNSUPPORTED.
  */
 mla_status mla_qk_norm_prepare(const mla_dims* dims, void* stream, const void* w_uk, const void* g_q,
                                const void* g_k, void* w_uk_folded, float* gram);
+size_t mla_key_norm_workspace_size(const mla_dims* dims, const mla_geom* geom, int32_t n_tokens);
 mla_status mla_cache_key_norm(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_tokens,
-                              const int32_t* frame, const float* gram, const void* cache, void* cache_aux);
+                              const int32_t* frame, const float* gram, const void* cache, void* cache_aux,
+                              void* workspace, size_t workspace_bytes);
 
 /*
  * Low-rank query with the key up-projection folded in when the weights are

@@ -215,11 +215,17 @@ def test_qk_norm_entry_checks(lib):
     fake = ctypes.c_void_p(0x1000)
     # key norm without qk_norm set
     assert lib.mla_cache_key_norm(ctypes.byref(d), ctypes.byref(g), None, cfg.tokens_per_frame, fake, fake, fake,
-                                  fake) == _lib.MLA_ERR_INVALID_ARG
+                                  fake, None, 0) == _lib.MLA_ERR_INVALID_ARG
     d.qk_norm, d.qk_norm_eps = 1, 1e-6
     # a token count that is not a whole number of frames
     assert lib.mla_cache_key_norm(ctypes.byref(d), ctypes.byref(g), None, cfg.tokens_per_frame + 1, fake, fake,
-                                  fake, fake) == _lib.MLA_ERR_INVALID_ARG
+                                  fake, fake, None, 0) == _lib.MLA_ERR_INVALID_ARG
+    # a small call (one token per sequence) needs the partial-sum workspace
+    dec = SMALL_CONFIGS[2]
+    dd, gd = _dims(dec, qk_norm=1, qk_norm_eps=1e-6), _geom(dec)
+    assert lib.mla_key_norm_workspace_size(ctypes.byref(dd), ctypes.byref(gd), 1) > 0
+    assert lib.mla_cache_key_norm(ctypes.byref(dd), ctypes.byref(gd), None, 1, fake, fake, fake, fake, None,
+                                  0) == _lib.MLA_ERR_WORKSPACE
     # the folded-query absorb has no query content values to normalise
     assert lib.mla_absorb_q_folded(ctypes.byref(d), ctypes.byref(g), None, 4, 64, fake, fake, fake, fake,
                                    fake) == _lib.MLA_ERR_UNSUPPORTED
