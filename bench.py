@@ -217,6 +217,7 @@ def main():
     attn_call_ms = start.elapsed_time(end) / args.steps
 
     # ---- operations beside the step (not part of `value`) ----
+    print(f"[bench] step timed ({ms_per_step:.4f} ms); operations beside the step", file=sys.stderr, flush=True)
     adjacent = {}
     # rotary-key shift of every slot of every sequence (alternating +1 / -1
     # frames so the cache returns to its state); bytes: the rotary part of
@@ -273,50 +274,56 @@ def main():
                               "w_uq_bytes": w_uq_t.numel() * w_uq_t.element_size()}
     del w_fold, w_uq_t, c_q_t, qa_f
 
+    print("[bench] rotary-key shift and query fold timed", file=sys.stderr, flush=True)
     # QK normalisation: the same cache and queries with the content score
     # scaled by each key's inverse RMS (unit norm weights), against the plain
     # call on the same cache set; plus the per-append key statistic and the
     # query statistic inside the absorb
     cfg_q = cfg.replace(qk_norm=True)
     dims_q = api.dims_from_config(cfg_q)
-    _, na_q = api.cache_nbytes(dims_q, geom)
-    c0, a0 = caches[0]
-    aux_q = torch.zeros(na_q // 2, dtype=torch.float16, device=dev)
-    if a0 is not None:
-        aux_q[:a0.numel()].copy_(a0)          # the low-bit scales keep their offsets
-    gram = torch.empty((cfg.d_c, cfg.d_c), dtype=torch.float32, device=dev)
-    w_uk_q = torch.empty_like(w_uk)
-    ones = torch.ones((H, cfg.d_nope), dtype=dt, device=dev)
-    api.qk_norm_prepare(dims_q, w_uk, ones, ones, w_uk_q, gram)
-    f0 = max(0, cfg.newest + 1 - cfg.window)
-    api.cache_key_norm(dims_q, geom, (cfg.newest + 1 - f0) * P, torch.full((B,), f0, dtype=torch.int32, device=dev),
-                       gram, c0, aux_q)
-    f_new = torch.full((B,), cfg.newest, dtype=torch.int32, device=dev)
-    ws_kn = torch.empty(max(16, api.key_norm_workspace_bytes(dims_q, geom, P)), dtype=torch.uint8, device=dev)
-    qa_q, ol_q = torch.empty_like(q_abs[0]), torch.empty_like(o_lat[0])
-    api.absorb_q(dims_q, geom, q_nope, q_rope, q_first, w_uk_q, qa_q)
-    timed_q = {}
-    calls = (("attention_plain", lambda: api.attention(dims, geom, q_abs[0], q_first, newest, c0, a0, o_lat[0],
-                                                       lse, workspace=ws_attn)),
-             ("attention_qk_norm", lambda: api.attention(dims_q, geom, qa_q, q_first, newest, c0, aux_q, ol_q,
-                                                         lse, workspace=ws_attn)),
-             ("key_norm_per_append", lambda: api.cache_key_norm(dims_q, geom, P, f_new, gram, c0, aux_q, ws_kn)),
-             ("absorb_q_qk_norm", lambda: api.absorb_q(dims_q, geom, q_nope, q_rope, q_first, w_uk_q, qa_q)))
-    for rnd in range(3):            # alternating rounds; the fastest round of each call
-        for name, call in calls:
-            call()
-            torch.cuda.synchronize()
-            start.record(stream)
-            for i in range(args.steps):
+    # (measured where the narrow MFMA kernel serves it: d_r = 64; wider rotary
+    # keys run QK normalisation on the generic kernel)
+    qkn_measured = cfg.d_r == 64
+    if qkn_measured:
+        _, na_q = api.cache_nbytes(dims_q, geom)
+        c0, a0 = caches[0]
+        aux_q = torch.zeros(na_q // 2, dtype=torch.float16, device=dev)
+        if a0 is not None:
+            aux_q[:a0.numel()].copy_(a0)          # the low-bit scales keep their offsets
+        gram = torch.empty((cfg.d_c, cfg.d_c), dtype=torch.float32, device=dev)
+        w_uk_q = torch.empty_like(w_uk)
+        ones = torch.ones((H, cfg.d_nope), dtype=dt, device=dev)
+        api.qk_norm_prepare(dims_q, w_uk, ones, ones, w_uk_q, gram)
+        f0 = max(0, cfg.newest + 1 - cfg.window)
+        api.cache_key_norm(dims_q, geom, (cfg.newest + 1 - f0) * P, torch.full((B,), f0, dtype=torch.int32, device=dev),
+                           gram, c0, aux_q)
+        f_new = torch.full((B,), cfg.newest, dtype=torch.int32, device=dev)
+        ws_kn = torch.empty(max(16, api.key_norm_workspace_bytes(dims_q, geom, P)), dtype=torch.uint8, device=dev)
+        qa_q, ol_q = torch.empty_like(q_abs[0]), torch.empty_like(o_lat[0])
+        api.absorb_q(dims_q, geom, q_nope, q_rope, q_first, w_uk_q, qa_q)
+        timed_q = {}
+        calls = (("attention_plain", lambda: api.attention(dims, geom, q_abs[0], q_first, newest, c0, a0, o_lat[0],
+                                                           lse, workspace=ws_attn)),
+                 ("attention_qk_norm", lambda: api.attention(dims_q, geom, qa_q, q_first, newest, c0, aux_q, ol_q,
+                                                             lse, workspace=ws_attn)),
+                 ("key_norm_per_append", lambda: api.cache_key_norm(dims_q, geom, P, f_new, gram, c0, aux_q, ws_kn)),
+                 ("absorb_q_qk_norm", lambda: api.absorb_q(dims_q, geom, q_nope, q_rope, q_first, w_uk_q, qa_q)))
+        for rnd in range(3):            # alternating rounds; the fastest round of each call
+            for name, call in calls:
                 call()
-            end.record(stream)
-            torch.cuda.synchronize()
-            t_ms = start.elapsed_time(end) / args.steps
-            timed_q[name] = min(t_ms, timed_q.get(name, t_ms))
-    adjacent["qk_norm"] = {k + "_ms": round(v, 5) for k, v in timed_q.items()}
-    adjacent["qk_norm"]["attention_overhead"] = round(timed_q["attention_qk_norm"] / timed_q["attention_plain"] - 1, 4)
-    del aux_q, gram, w_uk_q, qa_q, ol_q, ws_kn
+                torch.cuda.synchronize()
+                start.record(stream)
+                for i in range(args.steps):
+                    call()
+                end.record(stream)
+                torch.cuda.synchronize()
+                t_ms = start.elapsed_time(end) / args.steps
+                timed_q[name] = min(t_ms, timed_q.get(name, t_ms))
+        adjacent["qk_norm"] = {k + "_ms": round(v, 5) for k, v in timed_q.items()}
+        adjacent["qk_norm"]["attention_overhead"] = round(timed_q["attention_qk_norm"] / timed_q["attention_plain"] - 1, 4)
+        del aux_q, gram, w_uk_q, qa_q, ol_q, ws_kn
 
+    print("[bench] QK normalisation timed", file=sys.stderr, flush=True)
     # ---- algorithmic work of the attention call ----
     qf = np.arange(cfg.n_q) // P + cfg.q_first
     mask_keys = 0
