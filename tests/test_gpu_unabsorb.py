@@ -13,7 +13,9 @@ pytestmark = pytest.mark.gpu
 # (rows M, heads H, d_v, d_c, d_model)
 SHAPES = [(5, 41, 104, 64, 1000),      # K = 4264 (K % 64 = 40), N % 64 = 40, M < 32
           (32, 32, 128, 512, 4096),    # K = N = 4096, full tiles
-          (17, 64, 72, 128, 200)]      # K = 4608, N = 200 (3 blocks + tail)
+          (17, 64, 72, 128, 200),      # K = 4608, N = 200 (3 blocks + tail)
+          (5, 64, 128, 64, 8232),      # K = 8192, N = 8232 (ragged last column block)
+          (32, 128, 128, 64, 16384)]   # the decode output projection's shape (K = N = 16384)
 
 
 def _inputs(M, H, d_v, d_c, d_model, seed):
