@@ -281,9 +281,8 @@ def main():
     # query statistic inside the absorb
     cfg_q = cfg.replace(qk_norm=True)
     dims_q = api.dims_from_config(cfg_q)
-    # (measured where the narrow MFMA kernel serves it: d_r = 64; wider rotary
-    # keys run QK normalisation on the generic kernel)
-    qkn_measured = cfg.d_r == 64
+    # (the MFMA kernels serve it for d_r = 64 and d_r = 512)
+    qkn_measured = cfg.d_r in (64, 512) and cfg.d_c == 512 and cfg.dtype == "bf16"
     if qkn_measured:
         _, na_q = api.cache_nbytes(dims_q, geom)
         c0, a0 = caches[0]

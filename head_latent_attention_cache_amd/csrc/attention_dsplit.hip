@@ -49,7 +49,7 @@ constexpr size_t attn_dsplit_lds_bytes() {
          + 2 * 2 * 2048;                                // probabilities [buffer][row block]
 }
 
-template <int DC, int DR>
+template <int DC, int DR, bool QKN = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_dsplit_kernel(MfmaArgs ma) {
   constexpr int DQK = DC + DR;
@@ -60,6 +60,9 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   constexpr int WDIMS = DC / 4;             // output dims owned by one wave
   constexpr int NDB = WDIMS / 32;           // its 32-dim output blocks
   static_assert(DQK % 64 == 0 && WDIMS % 64 == 0 && TILE_BYTES % (256 * 16) == 0, "widths");
+  // QK normalisation: waves 0 and 1 hold the content quarters, 2 and 3 the
+  // rotary ones, so the reducing wave scales the sum of the first two
+  static_assert(!QKN || 2 * (DQK / 4) == DC, "content and rotary quarters");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sx = smem + 2 * TILE_BYTES;                 // [2 blocks][3 sources][4][64][16 B]
@@ -234,6 +237,27 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     uint8_t* tile = smem + bc * TILE_BYTES;
     const int k0 = (t_begin + cur) * MF_BN;
     const int cl = all_full ? (int)TILE_FULL : tile_class(cur);
+    // QK normalisation: the reducing waves read the inverse RMS of their
+    // keys (key 8 (e / 4) + 4 g + e % 4 of the tile for score element e)
+    // now; they are used after the score chain
+    float ksc[QKN ? 16 : 1];
+    if constexpr (QKN) {
+      if (wave < 2) {
+        const float* kr = a.kscale + (size_t)b * cap;
+        if ((cap & 3) == 0 && k0 + MF_BN <= cap) {
+          // four 16-byte loads (the keys 4 g .. 4 g + 3 of each group of 8)
+          typedef float f32x4_v __attribute__((ext_vector_type(4)));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4_v v = *(const f32x4_v*)(kr + k0 + 8 * j + 4 * g);
+            ksc[4 * j] = v[0]; ksc[4 * j + 1] = v[1]; ksc[4 * j + 2] = v[2]; ksc[4 * j + 3] = v[3];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ksc[e] = kr[min(k0 + 8 * (e >> 2) + 4 * g + (e & 3), cap - 1)];
+        }
+      }
+    }
     if (cl == TILE_MASKED_ZERO) {
       // zero never-written (or past-the-end) keys of this tile
       for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
@@ -296,6 +320,13 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     // barrier 2: partial scores complete; every wave holds its value
     // fragments of the previous tile, so its buffer takes the next tile
     lds_barrier();
+    if constexpr (QKN) {
+      // the key values have landed before the next tile's copy is issued (a
+      // wait placed after it would also wait for the copy)
+      if (wave < 2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) asm volatile("" ::"v"(ksc[e]));
+    }
     if (nxt < ntl) issue_loads(nxt, bc ^ 1);
 
     if (wave < 2) {
@@ -318,6 +349,11 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         else
 #pragma unroll
           for (int e = 0; e < 16; ++e) s[e] += pw[e];
+        if constexpr (QKN) {
+          if (w == 1)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] *= ksc[e];
+        }
       }
       if (cl != TILE_FULL) {
 #pragma unroll
@@ -446,8 +482,9 @@ bool attn_dsplit_supported(const Dims& d) {
     const char* e = getenv("MLA_ATTN_KERNEL");
     return e && strcmp(e, "generic") == 0;
   }();
-  // (QK normalisation is served by the narrow and the generic kernels)
-  if (generic || d.dtype != MLA_BF16 || d.cache_fmt != MLA_CACHE_DENSE || d.d_c != 512 || d.qk_norm) return false;
+  // (QK normalisation: content and rotary quarters must be whole waves, d_r = 512)
+  if (generic || d.dtype != MLA_BF16 || d.cache_fmt != MLA_CACHE_DENSE || d.d_c != 512) return false;
+  if (d.qk_norm && d.d_r != 512) return false;
   return d.d_r == 512 || (d.d_r == 64 && dsplit_forced());
 }
 
@@ -460,10 +497,10 @@ size_t attn_dsplit_workspace(const Dims& d, const Geo& g, int batch, int n_rows)
   return attn_plan_workspace(ma);
 }
 
-template <int DC, int DR>
+template <int DC, int DR, bool QKN>
 static hipError_t launch_dsplit_shape(const MfmaArgs& ma, int blocks, hipStream_t st) {
   const size_t shm = attn_dsplit_lds_bytes<DC, DR>();
-  auto kern = attn_dsplit_kernel<DC, DR>;
+  auto kern = attn_dsplit_kernel<DC, DR, QKN>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   kern<<<blocks, 256, shm, st>>>(ma);
@@ -476,8 +513,9 @@ hipError_t launch_attn_dsplit(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   const int blocks = attn_plan(a.d, a.g, a.batch, a.n_rows, DS_ROWS, &ma);
   if (ws_bytes < attn_plan_workspace(ma)) return hipErrorInvalidValue;
   attn_plan_bind(&ma, ws);
-  hipError_t e = a.d.d_r == 512 ? launch_dsplit_shape<512, 512>(ma, blocks, st)
-                                : launch_dsplit_shape<512, 64>(ma, blocks, st);
+  hipError_t e = a.d.d_r != 512 ? launch_dsplit_shape<512, 64, false>(ma, blocks, st)
+                 : a.kscale     ? launch_dsplit_shape<512, 512, true>(ma, blocks, st)
+                                : launch_dsplit_shape<512, 512, false>(ma, blocks, st);
   if (e != hipSuccess) return e;
   return launch_attn_merge(ma, st);
 }
