@@ -203,18 +203,41 @@ def main():
         torch.cuda.synchronize()
         ms_per_step, timing = start.elapsed_time(end) / args.steps, "HIP graph replay"
 
-    # the attention call alone, back to back over the rotated cache sets: its
-    # mean duration (attention kernel + split merge) is the roofline's launch
-    # time, comparable with the kernel trace
+    # the attention call alone, back to back over the rotated cache sets
+    # (at least 100 calls where they fit in ~10 s): its mean duration
+    # (attention kernel + split merge) is the roofline's launch time,
+    # comparable with the kernel trace
+    n_attn = max(args.steps, min(100, int(10000.0 / max(call_ms["attention"], 1e-3))))
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(n_attn):
         k = (args.warmup + i) % n_sets
         api.attention(dims, geom, q_abs[k], q_first, newest, caches[k][0], caches[k][1], o_lat[k], lse,
                       workspace=ws_attn)
     end.record(stream)
     torch.cuda.synchronize()
-    attn_call_ms = start.elapsed_time(end) / args.steps
+    attn_call_ms = start.elapsed_time(end) / n_attn
+    # a second run with events around every call (they add a gap between
+    # calls, so the mean above is taken without them): median, minimum and
+    # 90th percentile of the call duration
+    n_dist = max(10, min(100, int(5000.0 / max(attn_call_ms, 1e-3))))
+    call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    for i in range(n_dist):
+        k = (args.warmup + i) % n_sets
+        call_ev[i][0].record(stream)
+        api.attention(dims, geom, q_abs[k], q_first, newest, caches[k][0], caches[k][1], o_lat[k], lse,
+                      workspace=ws_attn)
+        call_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([e0.elapsed_time(e1) for e0, e1 in call_ev])
+    attn_stats = {"calls": n_attn, "mean_ms": round(attn_call_ms, 5), "timed_singly": n_dist,
+                  "median_ms": round(float(np.median(per_call)), 5), "min_ms": round(float(per_call.min()), 5),
+                  "p90_ms": round(float(np.percentile(per_call, 90)), 5)}
+
+    # achievable peaks of this device, measured in the same process: a
+    # stream of independent bf16 MFMAs and a streaming HBM read
+    print("[bench] measuring achievable MFMA and HBM rates", file=sys.stderr, flush=True)
+    peaks = measure_peaks(stream)
 
     # ---- operations beside the step (not part of `value`) ----
     print(f"[bench] step timed ({ms_per_step:.4f} ms); operations beside the step", file=sys.stderr, flush=True)
@@ -354,6 +377,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
         alg_per_launch = {"flops": flops}
+    ach = peaks["hbm_read_gbs"] if hbm_bound else peaks["mfma_bf16_tflops"]
+    roof["achievable_peak"] = ach
+    roof["frac_achievable"] = round(roof["achieved"] / ach, 4) if ach else None
     roof["traffic"] = None
     roof["kernel"] = "mla_attention"
     roof["launch_ms"] = round(attn_ms, 5)
@@ -379,7 +405,8 @@ def main():
                       "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                       "cache_gbs": round(cache_gbs, 1), "cache_hbm_frac": round(cache_gbs / PEAK_HBM_GBS, 4),
                       "query_tokens_per_s": round(queries / attn_s, 1),
-                      "algorithmic_per_launch": alg_per_launch, "source_hash": src},
+                      "algorithmic_per_launch": alg_per_launch, "source_hash": src, "per_call": attn_stats},
+        "peaks_measured": peaks,
         "breakdown_ms": {k: round(v, 5) for k, v in call_ms.items()},
         "timing": {"step": timing, "direct_calls_ms_per_step": round(eager_ms_per_step, 5)},
         "roofline": roof,
@@ -404,6 +431,43 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def measure_peaks(stream):
+    """Best of five launches of each probe (after one warm-up launch)."""
+    import torch
+    from head_latent_attention_cache_amd import api
+    dev = "cuda"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_rate(launch, work):
+        launch()
+        torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(5):
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, work / (e0.elapsed_time(e1) / 1e3))
+        return best
+
+    # 1024 work-groups (4 waves per SIMD on 256 CUs), 64,000 MFMAs per wave
+    n_wg, iters = 1024, 4000
+    out_f = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    flops = api.probe_mfma(n_wg, iters, out_f)
+    mfma = best_rate(lambda: api.probe_mfma(n_wg, iters, out_f), flops) / 1e12
+    # 4 GiB read once per launch (16x the 256 MB last-level cache)
+    n_wg_r = 4096
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    out_u = torch.empty(n_wg_r * 256, dtype=torch.int32, device=dev)
+    nbytes = buf.numel()
+    hbm = best_rate(lambda: api.probe_hbm_read(buf, n_wg_r, out_u), nbytes) / 1e9
+    del buf, out_u, out_f
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(hbm, 1),
+            "mfma_probe": f"{n_wg} work-groups x 4 waves x {iters * 16} independent 32x32x16 bf16 MFMAs",
+            "hbm_probe": f"streaming read of {nbytes >> 30} GiB, {n_wg_r} work-groups, 16-byte loads",
+            "method": "best of 5 launches, HIP events on the library's stream"}
 
 
 def cpu_baseline(cfg, inp, budget_s):

@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_size_t, c_void_p
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_amd.so")
@@ -60,6 +60,8 @@ SIGNATURES = {
                                  c_void_p, c_void_p]),
     "mla_cache_dequant": (c_int, [_D, _G, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_cache_rope_shift": (c_int, [_D, _G, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "mla_probe_mfma": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "mla_probe_hbm_read": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "mla_status_string": (c_char_p, [c_int]),
     "mla_last_error": (c_char_p, []),
     "mla_abi_version": (c_int, []),

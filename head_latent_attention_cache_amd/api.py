@@ -295,6 +295,29 @@ def cache_rope_shift(dims, geom, delta, slot_begin, n_slots, cache, cache_aux):
                                    _ptr(cache), _ptr(cache_aux)))
 
 
+def probe_mfma(n_workgroups, iters, out):
+    """Launch the bf16 MFMA rate probe (measurement only); returns the
+    floating-point operations of the launch.  out: float32 device tensor of
+    n_workgroups * 256 elements."""
+    lib = load()
+    _need(out, "out", torch.float32, n_workgroups * 256)
+    flops = ctypes.c_double(0.0)
+    check(lib.mla_probe_mfma(_stream(), int(n_workgroups), int(iters), _ptr(out), ctypes.byref(flops)))
+    return flops.value
+
+
+def probe_hbm_read(src, n_workgroups, out):
+    """Launch the streaming-read probe over the bytes of `src` (measurement
+    only).  out: int32 device tensor of n_workgroups * 256 elements."""
+    lib = load()
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous GPU tensor")
+    _need(out, "out", torch.int32, n_workgroups * 256)
+    n_bytes = src.numel() * src.element_size()
+    check(lib.mla_probe_hbm_read(_stream(), _ptr(src), int(n_bytes), int(n_workgroups), _ptr(out)))
+    return n_bytes
+
+
 def raw_lib():
     """The loaded ctypes library (for callers passing their own pointers)."""
     return _lib.load()

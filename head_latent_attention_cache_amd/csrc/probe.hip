@@ -1,0 +1,83 @@
+// Roofline references measured on the device that runs the MLA kernels: a
+// stream of independent bf16 MFMAs (the matrix-core rate the attention
+// kernels are compared with) and a coalesced streaming read (the HBM rate of
+// the decode cache read).  Measurement only: no MLA arithmetic here.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace mla {
+
+namespace {
+
+typedef __bf16 probe_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int PROBE_CHAINS = 4;      // independent accumulators per wave
+constexpr int PROBE_ROUNDS = 4;      // MFMAs per chain per loop iteration
+
+// each wave: iters * PROBE_ROUNDS * PROBE_CHAINS 32x32x16 bf16 MFMAs
+// (2 * 32 * 32 * 16 flop each); one float per thread keeps the result live
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* out) {
+  probe_bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)((float)((threadIdx.x + e) & 7) * 0.0625f);
+    b[e] = (__bf16)((float)((threadIdx.x * 3 + e) & 7) * 0.0625f);
+  }
+  probe_f32x16 acc[PROBE_CHAINS];
+#pragma unroll
+  for (int k = 0; k < PROBE_CHAINS; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[k][e] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int r = 0; r < PROBE_ROUNDS; ++r)
+#pragma unroll
+      for (int k = 0; k < PROBE_CHAINS; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < PROBE_CHAINS; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[k][e];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// grid-stride read of n16 16-byte words, four loads in flight per thread;
+// the XOR of everything read is written per thread so no load is dead
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                          uint32_t* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    x ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
+    x ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
+}  // namespace
+
+double probe_mfma_flops(int n_workgroups, int iters) {
+  return (double)n_workgroups * (256 / 64) * iters * PROBE_ROUNDS * PROBE_CHAINS * (2.0 * 32 * 32 * 16);
+}
+
+hipError_t launch_probe_mfma(int n_workgroups, int iters, float* out, hipStream_t st) {
+  probe_mfma_kernel<<<n_workgroups, 256, 0, st>>>(iters, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* src, size_t n_bytes, int n_workgroups, uint32_t* out, hipStream_t st) {
+  probe_read_kernel<<<n_workgroups, 256, 0, st>>>((const uint4*)src, n_bytes / 16, out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -229,3 +229,17 @@ def test_qk_norm_entry_checks(lib):
     # the folded-query absorb has no query content values to normalise
     assert lib.mla_absorb_q_folded(ctypes.byref(d), ctypes.byref(g), None, 4, 64, fake, fake, fake, fake,
                                    fake) == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_probe_argument_checks(lib):
+    """The measurement probes reject bad sizes and pointers before any launch."""
+    inv = -1
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: the checks fail first
+    assert lib.mla_probe_mfma(None, 0, 1, fake, None) == inv
+    assert lib.mla_probe_mfma(None, 1, 0, fake, None) == inv
+    assert lib.mla_probe_mfma(None, 1, 1, None, None) == inv
+    assert lib.mla_probe_hbm_read(None, fake, 0, 1, fake) == inv
+    assert lib.mla_probe_hbm_read(None, fake, 24, 1, fake) == inv
+    assert lib.mla_probe_hbm_read(None, fake, 32, 0, fake) == inv
+    assert lib.mla_probe_hbm_read(None, None, 32, 1, fake) == inv
+    assert lib.mla_probe_hbm_read(None, fake, 32, 1, ctypes.c_void_p(3)) == inv
