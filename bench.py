@@ -429,7 +429,10 @@ def main():
 
     # ---- CPU oracle on a bounded sample ----
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        cb = cpu_baseline(cfg, inp, args.cpu_seconds)
+        cb.update(host_info())
+        cb["gpu_over_oracle"] = round(value / cb["value"], 1) if cb["value"] else None
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 
@@ -468,6 +471,28 @@ def measure_peaks(stream):
             "mfma_probe": f"{n_wg} work-groups x 4 waves x {iters * 16} independent 32x32x16 bf16 MFMAs",
             "hbm_probe": f"streaming read of {nbytes >> 30} GiB, {n_wg_r} work-groups, 16-byte loads",
             "method": "best of 5 launches, HIP events on the library's stream"}
+
+
+def host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS library NumPy calls."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import numpy  # noqa: F401  (loads its BLAS)
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
 
 
 def cpu_baseline(cfg, inp, budget_s):
