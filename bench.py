@@ -458,8 +458,9 @@ def measure_peaks(stream):
     # 1024 work-groups (4 waves per SIMD on 256 CUs), 64,000 MFMAs per wave
     n_wg, iters = 1024, 4000
     out_f = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
-    flops = api.probe_mfma(n_wg, iters, out_f)
-    mfma = best_rate(lambda: api.probe_mfma(n_wg, iters, out_f), flops) / 1e12
+    flops = api.probe_mfma(n_wg, iters, out_f, False)
+    mfma_const = best_rate(lambda: api.probe_mfma(n_wg, iters, out_f, False), flops) / 1e12
+    mfma = best_rate(lambda: api.probe_mfma(n_wg, iters, out_f, True), flops) / 1e12
     # 4 GiB read once per launch (16x the 256 MB last-level cache)
     n_wg_r = 4096
     buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
@@ -467,8 +468,10 @@ def measure_peaks(stream):
     nbytes = buf.numel()
     hbm = best_rate(lambda: api.probe_hbm_read(buf, n_wg_r, out_u), nbytes) / 1e9
     del buf, out_u, out_f
-    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(hbm, 1),
-            "mfma_probe": f"{n_wg} work-groups x 4 waves x {iters * 16} independent 32x32x16 bf16 MFMAs",
+    return {"mfma_bf16_tflops": round(mfma, 1), "mfma_bf16_tflops_fixed_operands": round(mfma_const, 1),
+            "hbm_read_gbs": round(hbm, 1),
+            "mfma_probe": f"{n_wg} work-groups x 4 waves x {iters * 16} independent 32x32x16 bf16 MFMAs; "
+                          "two pseudo-random operand pairs in turn (fixed operands: one small-integer pair)",
             "hbm_probe": f"streaming read of {nbytes >> 30} GiB, {n_wg_r} work-groups, 16-byte loads",
             "method": "best of 5 launches, HIP events on the library's stream"}
 

@@ -60,7 +60,7 @@ SIGNATURES = {
                                  c_void_p, c_void_p]),
     "mla_cache_dequant": (c_int, [_D, _G, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_cache_rope_shift": (c_int, [_D, _G, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
-    "mla_probe_mfma": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "mla_probe_mfma": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "mla_probe_hbm_read": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "mla_status_string": (c_char_p, [c_int]),
     "mla_last_error": (c_char_p, []),

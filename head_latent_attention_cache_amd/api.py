@@ -295,14 +295,16 @@ def cache_rope_shift(dims, geom, delta, slot_begin, n_slots, cache, cache_aux):
                                    _ptr(cache), _ptr(cache_aux)))
 
 
-def probe_mfma(n_workgroups, iters, out):
+def probe_mfma(n_workgroups, iters, out, toggle=True):
     """Launch the bf16 MFMA rate probe (measurement only); returns the
     floating-point operations of the launch.  out: float32 device tensor of
-    n_workgroups * 256 elements."""
+    n_workgroups * 256 elements; toggle: alternate two pseudo-random operand
+    pairs (True) or repeat one fixed pair (False)."""
     lib = load()
     _need(out, "out", torch.float32, n_workgroups * 256)
     flops = ctypes.c_double(0.0)
-    check(lib.mla_probe_mfma(_stream(), int(n_workgroups), int(iters), _ptr(out), ctypes.byref(flops)))
+    check(lib.mla_probe_mfma(_stream(), int(n_workgroups), int(iters), int(bool(toggle)), _ptr(out),
+                             ctypes.byref(flops)))
     return flops.value
 
 

@@ -145,7 +145,7 @@ size_t elem_size(const Dims& d) { return d.dtype == MLA_BF16 ? 2 : 4; }
 
 namespace mla {
 double probe_mfma_flops(int n_workgroups, int iters);
-hipError_t launch_probe_mfma(int n_workgroups, int iters, float* out, hipStream_t st);
+hipError_t launch_probe_mfma(int n_workgroups, int iters, int toggle, float* out, hipStream_t st);
 hipError_t launch_probe_read(const void* src, size_t n_bytes, int n_workgroups, uint32_t* out, hipStream_t st);
 }  // namespace mla
 
@@ -436,13 +436,15 @@ mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* s
   return hip_status(launch_dequant(d, g, geom->batch, cache, cache_aux, out, st), st, "cache dequant");
 }
 
-mla_status mla_probe_mfma(void* stream, int32_t n_workgroups, int32_t iters, float* out, double* flops) {
+mla_status mla_probe_mfma(void* stream, int32_t n_workgroups, int32_t iters, int32_t toggle, float* out,
+                          double* flops) {
   if (n_workgroups <= 0 || n_workgroups > (1 << 20) || iters <= 0 || iters > (1 << 24))
     return fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [1, 2^20] and iters in [1, 2^24]");
+  if (toggle != 0 && toggle != 1) return fail(MLA_ERR_INVALID_ARG, "toggle must be 0 or 1");
   NEED_PTR(out);
   if (flops) *flops = probe_mfma_flops(n_workgroups, iters);
   hipStream_t st = (hipStream_t)stream;
-  return hip_status(launch_probe_mfma(n_workgroups, iters, out, st), st, "MFMA probe");
+  return hip_status(launch_probe_mfma(n_workgroups, iters, toggle, out, st), st, "MFMA probe");
 }
 
 mla_status mla_probe_hbm_read(void* stream, const void* src, int64_t n_bytes, int32_t n_workgroups,

@@ -17,14 +17,27 @@ typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
 constexpr int PROBE_CHAINS = 4;      // independent accumulators per wave
 constexpr int PROBE_ROUNDS = 4;      // MFMAs per chain per loop iteration
 
+// a bf16 in [-1, 1) from 16 pseudo-random bits (the "lowbias32" 32-bit
+// integer hash published by C. Wellons)
+__device__ __forceinline__ __bf16 probe_rand_bf16(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return (__bf16)((float)(int)(x & 0xffffu) * (1.0f / 32768.0f) - 1.0f);
+}
+
 // each wave: iters * PROBE_ROUNDS * PROBE_CHAINS 32x32x16 bf16 MFMAs
-// (2 * 32 * 32 * 16 flop each); one float per thread keeps the result live
-__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* out) {
-  probe_bf16x8 a, b;
+// (2 * 32 * 32 * 16 flop each); one float per thread keeps the result live.
+// toggle = 0: one fixed, small-integer operand pair; toggle = 1: two pairs of
+// pseudo-random operands used in turn, so the multiplier inputs change on
+// every instruction as they do with real data (more switching power)
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int toggle, float* out) {
+  probe_bf16x8 a, b, a1, b1;
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)((float)((threadIdx.x + e) & 7) * 0.0625f);
-    b[e] = (__bf16)((float)((threadIdx.x * 3 + e) & 7) * 0.0625f);
+    a[e] = toggle ? probe_rand_bf16(t * 32u + e) : (__bf16)((float)((threadIdx.x + e) & 7) * 0.0625f);
+    b[e] = toggle ? probe_rand_bf16(t * 32u + 8 + e) : (__bf16)((float)((threadIdx.x * 3 + e) & 7) * 0.0625f);
+    a1[e] = toggle ? probe_rand_bf16(t * 32u + 16 + e) : a[e];
+    b1[e] = toggle ? probe_rand_bf16(t * 32u + 24 + e) : b[e];
   }
   probe_f32x16 acc[PROBE_CHAINS];
 #pragma unroll
@@ -35,7 +48,8 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* out) 
 #pragma unroll
     for (int r = 0; r < PROBE_ROUNDS; ++r)
 #pragma unroll
-      for (int k = 0; k < PROBE_CHAINS; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+      for (int k = 0; k < PROBE_CHAINS; ++k)
+        acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((r + k) & 1 ? a1 : a, (r + k) & 1 ? b1 : b, acc[k], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
@@ -70,8 +84,8 @@ double probe_mfma_flops(int n_workgroups, int iters) {
   return (double)n_workgroups * (256 / 64) * iters * PROBE_ROUNDS * PROBE_CHAINS * (2.0 * 32 * 32 * 16);
 }
 
-hipError_t launch_probe_mfma(int n_workgroups, int iters, float* out, hipStream_t st) {
-  probe_mfma_kernel<<<n_workgroups, 256, 0, st>>>(iters, out);
+hipError_t launch_probe_mfma(int n_workgroups, int iters, int toggle, float* out, hipStream_t st) {
+  probe_mfma_kernel<<<n_workgroups, 256, 0, st>>>(iters, toggle, out);
   return hipGetLastError();
 }
 

@@ -310,6 +310,10 @@ mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* s
  *
  * mla_probe_mfma: n_workgroups work-groups of 256 threads; every wave issues
  *   iters * 16 independent 32x32x16 bf16 MFMAs (four accumulator chains).
+ *   toggle = 0 uses one fixed operand pair; toggle = 1 alternates two pairs
+ *   of pseudo-random bf16 operands, so the inputs change on every
+ *   instruction as with real data (the clock then settles where the power
+ *   limit holds it).
  *   out [n_workgroups * 256] float (device, caller-owned) receives one value
  *   per thread (kept so the work is not removed); *flops (host, optional)
  *   receives the floating-point operations of the launch.
@@ -321,7 +325,8 @@ mla_status mla_cache_dequant(const mla_dims* dims, const mla_geom* geom, void* s
  * MLA_ERR_INVALID_ARG; launch failures MLA_ERR_HIP.  Both are asynchronous on
  * `stream`; time them with events on that stream.
  */
-mla_status mla_probe_mfma(void* stream, int32_t n_workgroups, int32_t iters, float* out, double* flops);
+mla_status mla_probe_mfma(void* stream, int32_t n_workgroups, int32_t iters, int32_t toggle, float* out,
+                          double* flops);
 mla_status mla_probe_hbm_read(void* stream, const void* src, int64_t n_bytes, int32_t n_workgroups,
                               uint32_t* out);
 

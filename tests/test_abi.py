@@ -235,9 +235,10 @@ def test_probe_argument_checks(lib):
     """The measurement probes reject bad sizes and pointers before any launch."""
     inv = -1
     fake = ctypes.c_void_p(1 << 20)          # never dereferenced: the checks fail first
-    assert lib.mla_probe_mfma(None, 0, 1, fake, None) == inv
-    assert lib.mla_probe_mfma(None, 1, 0, fake, None) == inv
-    assert lib.mla_probe_mfma(None, 1, 1, None, None) == inv
+    assert lib.mla_probe_mfma(None, 0, 1, 0, fake, None) == inv
+    assert lib.mla_probe_mfma(None, 1, 0, 0, fake, None) == inv
+    assert lib.mla_probe_mfma(None, 1, 1, 2, fake, None) == inv
+    assert lib.mla_probe_mfma(None, 1, 1, 1, None, None) == inv
     assert lib.mla_probe_hbm_read(None, fake, 0, 1, fake) == inv
     assert lib.mla_probe_hbm_read(None, fake, 24, 1, fake) == inv
     assert lib.mla_probe_hbm_read(None, fake, 32, 0, fake) == inv

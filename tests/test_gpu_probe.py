@@ -24,15 +24,16 @@ def test_read_probe_reads_every_word_once(gpu_lib, n_bytes, n_wg):
     assert got == want
 
 
-def test_mfma_probe_count_and_determinism(gpu_lib):
+@pytest.mark.parametrize("toggle", [False, True])
+def test_mfma_probe_count_and_determinism(gpu_lib, toggle):
     import torch
     from head_latent_attention_cache_amd import api
     print("[case] MFMA probe", flush=True)
     n_wg, iters = 8, 10
     a = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    flops = api.probe_mfma(n_wg, iters, a)
+    flops = api.probe_mfma(n_wg, iters, a, toggle)
     assert flops == n_wg * 4 * iters * 16 * 2 * 32 * 32 * 16
-    api.probe_mfma(n_wg, iters, b)
+    api.probe_mfma(n_wg, iters, b, toggle)
     torch.cuda.synchronize()
     assert torch.isfinite(a).all() and torch.equal(a, b) and a.abs().sum() > 0
