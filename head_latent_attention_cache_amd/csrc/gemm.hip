@@ -210,6 +210,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   constexpr int CPR = SEG / 8;                 // 16-byte chunks per weight row and stage
+  static_assert(CPR % 16 == 0, "the row swizzle permutes chunks in groups of 16");
   constexpr int WLOADS = BN * CPR / 256;       // 16-byte weight loads per lane and stage
   constexpr int NB = BN / 32;                  // 32-column MFMA blocks
   constexpr int TSTEPS = SEG / 64;             // 16-wide MFMA steps per wave and stage
@@ -235,7 +236,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
   // weight loads: load q of this lane takes linear chunk (q * 4 + wave) * 64 + lane
   // of the stage block (row-major [BN][CPR]), so each wave instruction reads
   // 1 KB of consecutive row bytes; LDS keeps a row's chunk c at position
-  // c ^ (row & 7) (conflict-free fragment reads)
+  // c ^ (row & 15): a row is a multiple of 256 bytes, so every row starts at
+  // the same bank, and the fragment reads take 16 consecutive rows (one chunk
+  // each) per 16-lane phase of the 64-bank LDS: the 16 rows land on 16
+  // distinct 16-byte bank groups, and the row-major stores stay a
+  // permutation of each row's chunks
   const bf16_t* wrow[WLOADS];
   int wcol[WLOADS], wlds[WLOADS];
 #pragma unroll
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
     const int r = L / CPR, c = L % CPR;
     wrow[q] = B + (size_t)min(n0 + r, a.N - 1) * a.ldb;
     wcol[q] = c * 8;
-    wlds[q] = r * (SEG * 2) + ((c ^ (r & 7)) << 4);
+    wlds[q] = r * (SEG * 2) + ((c ^ (r & 15)) << 4);
   }
   // fragments: lane (l32, g) of MFMA step t of this wave reads chunk
   // c = 2 * (TSTEPS * wave + t) + g of weight row 32 * j + l32 (B, block j)
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int r = 32 * j + l32;
-        const u32x4v wv = *(const __attribute__((address_space(3))) u32x4v*)(wb + r * (SEG * 2) + ((c ^ (r & 7)) << 4));
+        const u32x4v wv = *(const __attribute__((address_space(3))) u32x4v*)(wb + r * (SEG * 2) + ((c ^ (r & 15)) << 4));
         const uint32_t mb = (k < a.K && n0 + r < a.N) ? ~0u : 0u;
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8_t, wv & mb), acc[j], 0, 0, 0);
       }
