@@ -141,6 +141,10 @@ struct MfmaArgs {
   int nsplit;        // max(ns_a, ns_b): split slots of the partial buffers
   bf16_t* ws_o;      // [nsplit][B][n_rows][d_c] partial outputs (normalised, bf16)
   float* ws_lse;     // [nsplit][B][n_rows]
+  // softmax: a row reruns the key loop once its maximum exceeds the fixed
+  // reference by more than this many log2 units (64; smaller values make the
+  // rerun fire on ordinary inputs, for testing)
+  float rerun_log2;
 };
 
 // split count of row block rb (of any sequence)
@@ -231,6 +235,11 @@ __device__ __forceinline__ uint8_t classify_tile(int k0, int cap, int P, int new
   if (floor_div(fmax, fpb) <= floor_div(gfq_min, fpb) && gfq_max - fmin < W) return TILE_FULL;
   return TILE_MASKED;
 }
+
+// the rerun threshold of the fixed-reference softmax: 64 log2 units, or
+// MLA_SOFTMAX_RERUN_SLACK=<x> (>= 0; testing: 0 reruns every row whose maximum
+// is not in its first visible tile)
+float softmax_rerun_slack();
 
 // launch plan (key-split fields of MfmaArgs) for row blocks of `rows_per_wg`
 // and MF_BN-key tiles; returns the number of work-groups (the grid must be

@@ -370,7 +370,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       mloc = halves_max(mloc) * c_l2;
       m_seen = fmaxf(m_seen, mloc);
       if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
-      else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
+      else if (mloc > m_run + ma.rerun_log2) overflow = true; // rerun with the final maxima
       const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
       float lsum = 0.f;
       LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + pb * 4096 + wave * 2 * 1024);

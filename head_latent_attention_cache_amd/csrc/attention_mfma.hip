@@ -520,7 +520,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     mloc = halves_max(mloc) * c_l2;
     m_seen = fmaxf(m_seen, mloc);
     if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
-    else if (mloc > m_run + 64.f) overflow = true; // rerun with the final maxima
+    else if (mloc > m_run + ma.rerun_log2) overflow = true; // rerun with the final maxima
     return m_run == -INFINITY ? 0.f : -m_run;
   };
   auto softmax_publish = [&](const f32x16_t& s, float neg_m, int pbuf) {
@@ -920,7 +920,17 @@ static PlanVal cached_plan(const PlanKey& k) {
   return v;
 }
 
+float softmax_rerun_slack() {
+  static const float v = [] {
+    const char* e = getenv("MLA_SOFTMAX_RERUN_SLACK");
+    const float x = e ? (float)atof(e) : 64.f;
+    return x >= 0.f && x <= 64.f ? x : 64.f;
+  }();
+  return v;
+}
+
 int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma) {
+  ma->rerun_log2 = softmax_rerun_slack();
   ma->n_rb = (n_rows + rows_per_wg - 1) / rows_per_wg;
   ma->rows_wg = rows_per_wg;
   ma->tiles = (g.capacity + MF_BN - 1) / MF_BN;

@@ -63,40 +63,34 @@ def test_fullsize_video_chunk(gpu_lib, key):
 
 def test_fullsize_long_video(gpu_lib):
     """Batch 2, 4680 query tokens x 32 heads over 74,880 keys of 1024-wide
-    rows: sampled cache rows, the absorbed queries of the last query frame,
-    attention for sampled (token, head) pairs given the stored cache, and the
-    un-absorb of sampled tokens."""
+    rows: sampled cache rows, every absorbed query, and attention for sampled
+    (token, head) pairs of all three query frames against the oracle's own
+    cache (frames 45 and 46 see a frame-causal part of the window: the masked
+    key tiles of the benchmark's split plan), plus the un-absorb of sampled
+    tokens."""
     cfg = CONFIGS[4]
     _case(cfg.name)
     inp = make_workload(cfg, seed=0)
     got = gp.run_gpu(cfg, inp)
     P = cfg.tokens_per_frame
-    w_dkr = om.as_f64(inp["w_dkr"])
-    # cache rows against the oracle's projection and rotation
-    for b in (0, 1):
-        for f in (0, 23, cfg.n_frames - 1):
-            toks = np.array([0, 777, P - 1])
-            rows = om.project_rows(cfg, om.as_f64(inp["x"][b, f, toks]), w_dkr, f, toks)
-            slots = om.slot_index(cfg, f, toks)
-            gp.compare("cache rows", got["cache"][b, slots], om.round_to_storage(rows, cfg.dtype), cfg.dtype)
-    # absorbed queries of the last query frame
-    last = cfg.q_frames - 1
-    sl = slice(last * P, (last + 1) * P)
-    cfg1 = cfg.replace(q_frames=1)
-    q_ref = om.absorb_query(cfg1, om.as_f64(inp["q_nope"][:, sl]), om.as_f64(inp["q_rope"][:, sl]),
-                            om.as_f64(inp["w_uk"]), cfg.q_first + last)
-    gp.compare("q_abs", got["q_abs"][:, sl], q_ref, cfg.dtype)
-    # attention on the stored cache for sampled tokens (of the last frame) and heads
-    st = {"values": got["cache"], "newest": cfg.newest}
-    q_nope = np.zeros((cfg.batch, cfg.n_q, cfg.n_heads, cfg.d_nope))
-    q_rot = np.zeros((cfg.batch, cfg.n_q, cfg.n_heads, cfg.d_r))
-    q_nope[:, sl] = om.as_f64(inp["q_nope"][:, sl])
-    q_rot[:, sl] = q_ref[..., cfg.d_c:]
-    toks = [(0, last * P + 5), (1, last * P + 900), (1, cfg.n_q - 1)]
+    st = om.build_cache(cfg, inp)
+    # cache rows: every written slot of both sequences against the oracle's projection
+    gp.compare("cache", got["cache"], st["values"], cfg.dtype)
+    del got["cache"]
+    # absorbed queries of every token
+    w_uk = om.as_f64(inp["w_uk"])
+    q_ref = om.absorb_query(cfg, om.as_f64(inp["q_nope"]), om.as_f64(inp["q_rope"]), w_uk, cfg.q_first)
+    gp.compare("q_abs", got["q_abs"], q_ref, cfg.dtype)
+    # attention for tokens of query frames 45, 46 and 47 (both sequences)
+    toks = [(0, 5), (1, 777), (0, P + 3), (1, P + 1111), (0, 2 * P + 5), (1, 2 * P + 900), (1, cfg.n_q - 1)]
     heads = [0, 13, 31]
-    _, o_lat, lse = om.attend(cfg, st, q_nope, q_rot, om.as_f64(inp["w_uk"]), om.as_f64(inp["w_uv"]),
-                              cfg.q_first, tokens=toks, heads=heads)
+    _, o_lat, lse = om.attend(cfg, st, om.as_f64(inp["q_nope"]), q_ref[..., cfg.d_c:], w_uk,
+                              om.as_f64(inp["w_uv"]), cfg.q_first, tokens=toks, heads=heads)
+    mask = om.mask_matrix(cfg, cfg.q_first, st["newest"])
     for i, (b, t) in enumerate(toks):
+        frame = cfg.q_first + t // P
+        n_vis = int(mask[t].sum())
+        _case(f"long video b={b} t={t} frame={frame} visible keys={n_vis}")
         gp.compare("o_lat", got["o_lat"][b, t, heads], o_lat[i, heads], cfg.dtype)
         gp.compare("lse", got["lse"][b, t, heads], lse[i, heads], cfg.dtype)
     # un-absorb of sampled tokens from the path's own latent output

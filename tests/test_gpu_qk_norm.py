@@ -66,12 +66,21 @@ def run_qkn(cfg, inp, g_q, g_k, fill=None):
 
 
 # decode (bf16), video chunk (bf16), INT4 and INT2 chunks (narrow MFMA kernel),
-# the fp32 tiny video and the d_r = 512 long video (generic kernel)
-@pytest.mark.parametrize("key", [2, 3, 5, 6, 1, 4])
+# the fp32 tiny video (generic kernel), the d_r = 512 long video (wide-row
+# kernel; capacity 90 reads the key statistic one value at a time) and a
+# 4 x 5 grid of the long video (capacity 120, a multiple of 4: the wide-row
+# kernel's 16-byte reads of the key statistic, with a ragged last tile)
+QKN_CASES = {key: SMALL_CONFIGS[key] for key in (2, 3, 5, 6, 1, 4)}
+QKN_CASES["4x5"] = SMALL_CONFIGS[4].replace(name="long_video_small_4x5", grid_h=4, grid_w=5)
+
+
+@pytest.mark.parametrize("key", list(QKN_CASES))
 def test_qk_norm_matches_oracle(gpu_lib, key):
     import torch
     from head_latent_attention_cache_amd import api
-    cfg = SMALL_CONFIGS[key].replace(qk_norm=True, qk_eps=EPS)
+    cfg = QKN_CASES[key].replace(qk_norm=True, qk_eps=EPS)
+    if key == "4x5":
+        assert cfg.capacity % 4 == 0 and cfg.capacity % 32 != 0
     _case(f"qk norm {cfg.name}")
     inp = make_workload(cfg, seed=41)
     g_q, g_k = _weights(cfg, 42)
