@@ -39,12 +39,22 @@ __device__ __forceinline__ void lds_barrier() {
 // with s_waitcnt vmcnt before the barrier that publishes the tile (the
 // compiler's own tracking would add vmcnt(0) waits in front of later
 // transposed LDS reads, draining the prefetch pipeline).
+// The compiler inserts no wait states in front of inline assembly, so each
+// block carries its own: one after the scalar write of M0 that an LDS-DMA load
+// reads, and five for a scalar base address, which the register allocator may
+// restore with v_readlane (a VALU write of the SGPR) right before the block:
+// a vector-memory read of an SGPR needs five wait states after a VALU write
+// of it, or it sees the old value (a wrong address).
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_base) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_base) : "memory");
 }
 // same, with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
 __device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
+// one dword per lane (same conventions as dma16)
+__device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "{m0}"(lds_base) : "memory");
 }
 
 // acc += A . B with v_mfma_f32_32x32x16_bf16, the accumulator in VGPRs (the

@@ -178,7 +178,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
       if (wave == 0 && lane < MF_BN) {
         const float* src = ksc_row + min((t_begin + i) * MF_BN + lane, cap - 1);
         const uint32_t dst = (uint32_t)(uintptr_t)(LDS_AS float*)(ksl + slot * MF_BN);
-        asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+        dma4(src, dst);
       }
     }
   };
