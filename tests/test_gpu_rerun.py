@@ -118,7 +118,7 @@ for b in range(B):
         o, _, l = om.attention_core(q_abs[b, :, h], K, K[:, :DC], mask, scale)
         ref_o[b, :, h] = o
         ref_l[b, :, h] = l
-planted = {(b, s) for b, s, _, _, _ in plants}
+planted = {{(b, s) for b, s, _, _, _ in plants}}
 for b, s, t, h, score in plants:
     assert mask[t, s], ("planted key not visible", b, s, t)
     # the planted key outscores every other visible key of its row by more
