@@ -56,6 +56,8 @@ SIGNATURES = {
     "mla_attention_workspace_size": (c_size_t, [_D, _G, c_int32]),
     "mla_attention": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t]),
+    "mla_attention_noalloc": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_unabsorb_out": (c_int, [_D, _G, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p]),
     "mla_cache_dequant": (c_int, [_D, _G, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -261,6 +261,24 @@ def attention(dims, geom, q_abs, q_first, newest, cache, cache_aux, o_lat, lse=N
                             _ptr(workspace), ws_bytes))
 
 
+def attention_noalloc(dims, geom, q_abs, q_first, newest, cache, cache_aux, o_lat, lse=None):
+    """mla_attention_noalloc: as ``attention`` with the library's static
+    scratch instead of a workspace (nothing is allocated)."""
+    lib = load()
+    dt = torch_dtype(dims)
+    B, H = geom.batch, dims.n_heads
+    n_q = q_abs.shape[1]
+    _need(q_abs, "q_abs", dt, B * n_q * H * (dims.d_c + dims.d_r))
+    _need(q_first, "q_first", torch.int32, B)
+    _need(newest, "newest", torch.int32, B)
+    _check_cache(dims, geom, cache, cache_aux)
+    _need(o_lat, "o_lat", dt, B * n_q * H * dims.d_c)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, B * n_q * H)
+    check(lib.mla_attention_noalloc(_rd(dims), _rd(geom), _stream(), n_q, _ptr(q_abs), _ptr(q_first),
+                                    _ptr(newest), _ptr(cache), _ptr(cache_aux), _ptr(o_lat), _ptr(lse)))
+
+
 def unabsorb_out(dims, geom, o_lat, w_uv, w_o, o_heads, y):
     """o_lat [B, n_q, H, d_c] -> o_heads [B, n_q, H * d_v], y [B, n_q, d_model]."""
     lib = load()

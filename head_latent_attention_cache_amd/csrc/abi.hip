@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -335,10 +336,47 @@ size_t mla_attention_workspace_size(const mla_dims* dims, const mla_geom* geom, 
   return 0;
 }
 
-mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
-                         const void* q_abs, const int32_t* q_first, const int32_t* newest,
-                         const void* cache, const void* cache_aux, void* o_lat, float* lse,
-                         void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free attention call: a file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes the array's name to a kernel: it stands for a host
+// shadow there; the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];   // device address of `scratch` per device (null: not looked up yet)
+
+mla_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(MLA_ERR_UNSUPPORTED, "device %d: the static scratch is kept for devices 0 .. %d", dev,
+                MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+// mla_attention and mla_attention_noalloc: validation, then the kernels with
+// the caller's workspace (noalloc = false) or the static scratch
+mla_status attention_impl(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                          const void* q_abs, const int32_t* q_first, const int32_t* newest,
+                          const void* cache, const void* cache_aux, void* o_lat, float* lse,
+                          void* workspace, size_t workspace_bytes, bool noalloc) {
   Dims d;
   Geo g;
   CHECK(check_dims(dims, &d));
@@ -373,13 +411,42 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
   const bool narrow = attn_mfma_supported(d, g), wide = !narrow && attn_dsplit_supported(d);
   if (narrow || wide) {
     const size_t need = narrow ? attn_mfma_workspace(d, g, B, a.n_rows) : attn_dsplit_workspace(d, g, B, a.n_rows);
-    if (need && (workspace_bytes < need || !workspace))
-      return fail(MLA_ERR_WORKSPACE, "attention workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    if (need && !aligned16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (noalloc) {
+      if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(MLA_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the library's static scratch holds %zu "
+                    "(use mla_attention with a workspace)", need, NOALLOC_SCRATCH_BYTES);
+      workspace = nullptr;
+      workspace_bytes = NOALLOC_SCRATCH_BYTES;
+      if (need) CHECK(scratch_of_current_device(&workspace));
+    } else {
+      if (need && (workspace_bytes < need || !workspace))
+        return fail(MLA_ERR_WORKSPACE, "attention workspace needs %zu bytes, got %zu", need, workspace_bytes);
+      if (need && !aligned16(workspace)) return fail(MLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    }
     if (narrow) return hip_status(launch_attn_mfma(a, workspace, workspace_bytes, st), st, "latent attention (MFMA)");
     return hip_status(launch_attn_dsplit(a, workspace, workspace_bytes, st), st, "latent attention (MFMA, split rows)");
   }
   return hip_status(launch_attn_simt(a, st), st, "latent attention");
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                         const void* q_abs, const int32_t* q_first, const int32_t* newest,
+                         const void* cache, const void* cache_aux, void* o_lat, float* lse,
+                         void* workspace, size_t workspace_bytes) {
+  return attention_impl(dims, geom, stream, n_q, q_abs, q_first, newest, cache, cache_aux, o_lat, lse, workspace,
+                        workspace_bytes, false);
+}
+
+mla_status mla_attention_noalloc(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                                 const void* q_abs, const int32_t* q_first, const int32_t* newest,
+                                 const void* cache, const void* cache_aux, void* o_lat, float* lse) {
+  return attention_impl(dims, geom, stream, n_q, q_abs, q_first, newest, cache, cache_aux, o_lat, lse, nullptr, 0,
+                        true);
 }
 
 mla_status mla_unabsorb_out(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,

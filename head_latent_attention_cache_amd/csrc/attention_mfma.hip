@@ -909,14 +909,23 @@ static PlanVal search_plan(const PlanKey& k) {
   return mixed_cost < best_cost * 0.98 ? mixed : best;
 }
 
+// (a fixed table: choosing a plan allocates nothing, so the call can run
+// where the caller forbids allocation)
 static PlanVal cached_plan(const PlanKey& k) {
+  constexpr int CAP = 256;
   static std::mutex mu;
-  static std::vector<std::pair<PlanKey, PlanVal>> cache;
+  static PlanKey keys[CAP];
+  static PlanVal vals[CAP];
+  static int n = 0;
   std::lock_guard<std::mutex> lock(mu);
-  for (const auto& e : cache)
-    if (memcmp(&e.first, &k, sizeof(PlanKey)) == 0) return e.second;
+  for (int i = 0; i < n; ++i)
+    if (memcmp(&keys[i], &k, sizeof(PlanKey)) == 0) return vals[i];
   const PlanVal v = search_plan(k);
-  if (cache.size() < 256) cache.push_back({k, v});
+  if (n < CAP) {
+    keys[n] = k;
+    vals[n] = v;
+    ++n;
+  }
   return v;
 }
 

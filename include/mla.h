@@ -261,6 +261,28 @@ mla_status mla_attention(const mla_dims* dims, const mla_geom* geom, void* strea
                          void* o_lat, float* lse, void* workspace, size_t workspace_bytes);
 
 /*
+ * mla_attention_noalloc: mla_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as mla_attention minus
+ * the workspace: the split-key partials go to a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends, its address looked up on the first call on each device).
+ * Nothing is allocated, freed or cleared by the call.
+ *   - A call whose partials need more than MLA_NOALLOC_SCRATCH_BYTES (see
+ *     mla_attention_workspace_size) returns MLA_ERR_WORKSPACE before anything
+ *     is launched; decode at batch 32 x 128 heads needs about 32 MiB, a
+ *     1560-token video chunk about 245 MiB (use mla_attention there).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (concurrent streams, or host threads) race and give wrong results.
+ *     Serialise them, or use mla_attention with a workspace per stream.
+ *   - The stream must belong to the calling thread's current device.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_attention_noalloc(const mla_dims* dims, const mla_geom* geom, void* stream, int32_t n_q,
+                                 const void* q_abs, const int32_t* q_first, const int32_t* newest,
+                                 const void* cache, const void* cache_aux, void* o_lat, float* lse);
+
+/*
  * mla_unabsorb_out: [MLA concept, Low-rank joint compression] (W^UV is absorbed
  * on the output side, as W^UK is on the query side); [MLA explainer, On-the-Fly
  * Reconstruction and Matrix Absorption].
