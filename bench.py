@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy kernel (for HBM counter calibration)")
+    ap.add_argument("--no-chunk-block", action="store_true",
+                    help="with the decode workload, skip the video-chunk attention block of the line")
     ap.add_argument("--eager", action="store_true",
                     help="time the steps as direct library calls instead of replays of a captured HIP graph")
     return ap.parse_args()
@@ -72,7 +74,6 @@ def main():
     import numpy as np
     import torch
 
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     import head_latent_attention_cache_amd as mla
     from head_latent_attention_cache_amd import api
     from mla_inputs import get_config, make_workload
@@ -427,6 +428,11 @@ def main():
                                    "read_bytes": rows * 1024 * 2, "write_bytes": rows * 1024 * 2}
         del src_t, big
 
+    # ---- the MFMA-bound half of the metric: video-chunk attention ----
+    if args.config == 2 and not args.no_chunk_block:
+        print("[bench] video-chunk attention block", file=sys.stderr, flush=True)
+        out["video_chunk"] = chunk_block(stream, peaks)
+
     # ---- CPU oracle on a bounded sample ----
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cfg, inp, args.cpu_seconds)
@@ -434,6 +440,99 @@ def main():
         cb["gpu_over_oracle"] = round(value / cb["value"], 1) if cb["value"] else None
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
+
+
+def attention_flops(cfg):
+    """Algorithmic FLOPs of one attention call: 2 (d_c + d_r + d_c) per
+    (row, visible key), rows = batch x query tokens x heads."""
+    import numpy as np
+    P = cfg.tokens_per_frame
+    qf = np.arange(cfg.n_q) // P + cfg.q_first
+    keys = 0
+    for f in qf:
+        lo = max(cfg.newest - cfg.window + 1, 0)
+        keys += sum(P for fk in range(lo, cfg.newest + 1)
+                    if fk // cfg.frames_per_block <= f // cfg.frames_per_block and f - fk < cfg.window)
+    return 2.0 * cfg.batch * cfg.n_heads * keys * (cfg.d_qk + cfg.d_c)
+
+
+def chunk_block(stream, peaks, n_calls=120, warmup=10):
+    """Video-chunk attention (1560 query tokens x 32 heads over an 18,720-key
+    window): the cache built by appending 12 frames, the absorbed queries of
+    the last frame, then back-to-back mla_attention calls timed with HIP
+    events on the library's stream; FLOP-based roofline."""
+    import numpy as np
+    import torch
+    from head_latent_attention_cache_amd import api
+    from mla_inputs import get_config, make_workload
+
+    cfg = get_config(3)
+    dev = "cuda"
+    dims, geom = api.dims_from_config(cfg), api.geom_from_config(cfg)
+    B, H, P = cfg.batch, cfg.n_heads, cfg.tokens_per_frame
+    inp = make_workload(cfg, seed=0)
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = dev_t(inp["x"])
+    w_dkr, w_uk = dev_t(inp["w_dkr"]), dev_t(inp["w_uk"])
+    cache, aux = api.new_cache(dims, geom)
+    ws_app = torch.empty(max(16, api.append_workspace_bytes(dims, geom, P)), dtype=torch.uint8, device=dev)
+    for f in range(cfg.n_frames):
+        api.cache_append(dims, geom, x[:, f].contiguous(), torch.full((B,), f, dtype=torch.int32, device=dev),
+                         w_dkr, cache, aux, workspace=ws_app)
+    del x
+    q_first = torch.full((B,), cfg.q_first, dtype=torch.int32, device=dev)
+    newest = torch.full((B,), cfg.newest, dtype=torch.int32, device=dev)
+    q_abs = torch.empty((B, cfg.n_q, H, cfg.d_qk), dtype=torch.bfloat16, device=dev)
+    api.absorb_q(dims, geom, dev_t(inp["q_nope"]), dev_t(inp["q_rope"]), q_first, w_uk, q_abs)
+    o_lat = torch.empty((B, cfg.n_q, H, cfg.d_c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, cfg.n_q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, api.attention_workspace_bytes(dims, geom, cfg.n_q)), dtype=torch.uint8, device=dev)
+
+    def call():
+        api.attention(dims, geom, q_abs, q_first, newest, cache, aux, o_lat, lse, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_calls
+    single = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        single.append((a, b))
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in single])
+    flops = attention_flops(cfg)
+    tflops = flops / (ms / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "achievable_peak": peaks["mfma_bf16_tflops"],
+            "frac_achievable": round(tflops / peaks["mfma_bf16_tflops"], 4) if peaks["mfma_bf16_tflops"] else None,
+            "traffic": None, "kernel": "mla_attention", "launch_ms": round(ms, 5)}
+    src = source_hash()
+    tfile = os.path.join(ROOT, "profiles", f"attention_traffic_{cfg.name}.json")
+    if os.path.exists(tfile):
+        tr = json.load(open(tfile))
+        if tr.get("source_hash") == src:
+            roof["traffic"] = tr.get("hbm_bytes_per_launch")
+    return {"workload": cfg.name, "calls": n_calls, "warmup": warmup, "ms": round(ms, 5),
+            "median_ms": round(float(np.median(per)), 5), "min_ms": round(float(per.min()), 5),
+            "p90_ms": round(float(np.percentile(per, 90)), 5), "tflops": round(tflops, 2),
+            "query_tokens_per_s": round(B * cfg.n_q / (ms / 1e3), 1), "algorithmic_flops": flops,
+            "config": {"batch": B, "heads": H, "query_tokens": cfg.n_q, "keys": cfg.capacity, "d_c": cfg.d_c,
+                       "d_r": cfg.d_r, "grid": [cfg.grid_h, cfg.grid_w], "window_frames": cfg.window},
+            "source_hash": src, "roofline": roof}
 
 
 def measure_peaks(stream):
@@ -498,48 +597,77 @@ def host_info():
     return {"cpu_model": model, "blas": blas}
 
 
-def cpu_baseline(cfg, inp, budget_s):
-    """Time the float64 oracle on whole sequences (decode) or a strided subset
-    of query tokens (chunk workloads) on this host's cores."""
-    import numpy as np
+_WORKER = {}
+
+
+def _oracle_worker_init(cfg_name, chunk):
+    """Pool initializer: the seeded inputs (and, for chunk workloads, the
+    oracle's cache, which a resident-input measurement excludes) built once
+    per worker, outside the timed region."""
     import oracle.mla as om
+    from mla_inputs import get_config, make_workload
+    cfg = get_config(cfg_name)
+    inp = make_workload(cfg, seed=0)
+    _WORKER.update(cfg=cfg, inp=inp, st=om.build_cache(cfg, inp) if chunk else None)
+
+
+def _oracle_task(arg):
+    """One timed unit of oracle work: a whole decode sequence (cache rows,
+    absorb, attention with materialised heads, output projection) or one
+    query token of a chunk workload (all heads, the whole window)."""
+    import oracle.mla as om
+    cfg, inp, st = _WORKER["cfg"], _WORKER["inp"], _WORKER["st"]
+    t0 = time.time()
+    if st is None:
+        b = arg
+        sub = {k: (v[b:b + 1] if k in ("q_nope", "q_rope", "cache_c", "cache_r", "x_new") else v)
+               for k, v in inp.items()}
+        om.run(cfg.replace(batch=1), sub)
+    else:
+        om.run(cfg, inp, tokens=[(0, arg)], st=st)
+    return time.time() - t0
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    """Time the float64 oracle (untuned) on this host's cores: a process pool
+    with one worker per core of this process's affinity (at most 16) and one
+    BLAS thread per worker, on a bounded sample of the workload: one decode
+    sequence per worker (one query token, all heads, the full cache), or
+    query tokens of a chunk workload (all heads, the whole window; the cache
+    build excluded)."""
+    import multiprocessing as mp
+    import numpy as np
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"                       # read by each worker's BLAS at its NumPy import
+    chunk = not cfg.cache_given
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    if cfg.cache_given:
-        # whole sequences: build the cache (given rows + the appended token),
-        # absorb, attend, project
-        done, t_used = 0, 0.0
-        while done < cfg.batch and (done == 0 or t_used < budget_s * 0.7):
-            b = done
-            sub_cfg = cfg.replace(batch=1)
-            sub = {k: (v[b:b + 1] if k in ("q_nope", "q_rope", "cache_c", "cache_r", "x_new") else v)
-                   for k, v in inp.items()}
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers, initializer=_oracle_worker_init, initargs=(cfg.name, chunk)) as pool:
+            pool.map(time.sleep, [0.0] * workers, chunksize=1)      # every worker initialised
+            if not chunk:
+                n = min(cfg.batch, workers)
+                tasks = list(range(n))
+                what = (f"{n} of {cfg.batch} sequences (1 query token each, all {cfg.n_heads} heads, full "
+                        f"{cfg.n_frames}-token cache)")
+            else:
+                n = workers * max(1, int(budget_s // 8))
+                tasks = [int(t) for t in np.linspace(0, cfg.n_q - 1, n).astype(int)]
+                what = (f"{n} of {cfg.n_q} query tokens of sample 0 (all {cfg.n_heads} heads, full key window; "
+                        f"cache build excluded)")
             t0 = time.time()
-            om.run(sub_cfg, sub)
-            t_used += time.time() - t0
-            done += 1
-        return {"value": round(done / t_used, 4), "unit": "query-tokens/s", "cores": cores,
-                "kind": "oracle", "sample": f"{done} of {cfg.batch} sequences (1 query token each, all "
-                                            f"{cfg.n_heads} heads, full {cfg.n_frames}-token cache), "
-                                            f"{t_used:.1f} s"}
-    # chunk workloads: cache build excluded (resident input); attend a strided
-    # subset of query tokens with all heads, then extrapolate per token
-    st = om.build_cache(cfg, inp)
-    n = 1
-    while True:
-        toks = [(0, int(t)) for t in np.linspace(0, cfg.n_q - 1, n).astype(int)]
-        t0 = time.time()
-        om.run(cfg, inp, tokens=toks, st=st)
-        dt_ = time.time() - t0
-        if dt_ > budget_s * 0.3 or n >= cfg.n_q:
-            break
-        n = min(cfg.n_q, max(n + 1, int(n * budget_s * 0.6 / max(dt_, 1e-3))))
-    return {"value": round(len(toks) / dt_, 4), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(toks)} of {cfg.n_q} query tokens of sample 0 (all {cfg.n_heads} heads, "
-                      f"full key window; cache build excluded), {dt_:.1f} s"}
+            per = pool.map(_oracle_task, tasks, chunksize=1)
+            wall = time.time() - t0
+        return {"value": round(len(tasks) / wall, 4), "unit": "query-tokens/s", "cores": workers, "kind": "oracle",
+                "sample": f"{what} on a pool of {workers} processes with one BLAS thread each: {wall:.1f} s wall, "
+                          f"{sum(per):.1f} s of oracle work"}
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 if __name__ == "__main__":
