@@ -59,9 +59,9 @@ __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_base) {
 
 // acc += A . B with v_mfma_f32_32x32x16_bf16, the accumulator in VGPRs (the
 // builtin lets the register allocator pick AGPRs).  A chain of these on one
-// accumulator needs no waits between steps (same-shape source-C forwarding);
-// mfma_vgpr_settle() must follow the last one before any other instruction
-// reads the accumulator.
+// accumulator needs no waits between steps (same-shape source-C forwarding,
+// also with an independent MFMA between two steps); the chain's last step is
+// mfma_vgpr_last(), which carries the wait states a later read needs.
 __device__ __forceinline__ void mfma_vgpr(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
@@ -70,10 +70,14 @@ __device__ __forceinline__ void mfma_vgpr(f32x16_t& acc, const bf16x8_t& a, cons
 __device__ __forceinline__ void mfma_vgpr_zero(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
-// wait states between an MFMA writing VGPRs and a VALU / memory read of them:
-// the 8-pass 32x32x16 MFMA needs about a dozen, 20 are given here
-__device__ __forceinline__ void mfma_vgpr_settle(f32x16_t& acc) {
-  asm volatile("s_nop 15\n\ts_nop 3" : "+v"(acc));
+// the last step of a chain with its wait states (the 8-pass 32x32x16 MFMA
+// needs about a dozen before a VALU or memory instruction reads its result;
+// 20 are given) in the same asm statement: the compiler takes an asm's
+// outputs as ready when the statement ends, so wait states in a statement of
+// their own would not stop it from copying the accumulator to other
+// registers between the MFMA and the waits
+__device__ __forceinline__ void mfma_vgpr_last(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 3" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 // wait states between a VALU write of the accumulator and an MFMA reading it

@@ -454,7 +454,10 @@ void attn_mfma_kernel(MfmaArgs ma) {
         kb[ks % KPF] = *kaddr(ks + KPF);
         if (ks + KPF >= NKS_REG) qb[ks % KPF] = *qaddr(ks + KPF);
       }
+      // (the chain's last step, and its last content step under QK
+      // normalisation, carry their wait states: their result is read next)
       if (ks == 0) mfma_vgpr_zero(s, cur_k, cur_q);
+      else if (ks == NKS - 1 || (QKN && ks == NKS_C - 1)) mfma_vgpr_last(s, cur_k, cur_q);
       else mfma_vgpr(s, cur_k, cur_q);
       if constexpr (QKN) {
         if (dma && ks == 0) ksl_dma(dp.tile, dp.kslot);   // the next tile's values, with its copy
@@ -468,7 +471,6 @@ void attn_mfma_kernel(MfmaArgs ma) {
           }
         }
         if (ks == NKS_C - 1) {
-          mfma_vgpr_settle(s);
 #pragma unroll
           for (int e = 0; e < 16; ++e) s[e] *= ksc[e];
           mfma_vgpr_after_valu(s);
@@ -495,7 +497,6 @@ void attn_mfma_kernel(MfmaArgs ma) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    mfma_vgpr_settle(s);
     return s;
   };
   // branch-free (selects only), so the score registers stay put

@@ -39,6 +39,38 @@ def test_scanner_flags_a_restored_base_and_an_early_m0():
     assert ah.scan(good) == []
 
 
+def test_scanner_flags_an_early_read_of_an_asm_mfma_result():
+    bad = "\n".join([
+        "\t;;#ASMSTART",
+        "\tv_mfma_f32_32x32x16_bf16 v[16:31], v[2:5], v[6:9], v[16:31]",
+        "\t;;#ASMEND",
+        "\tv_mov_b64_e32 v[0:1], v[16:17]",
+    ])
+    found = ah.scan(bad)
+    assert len(found) == 1 and "MFMA result" in found[0][2]
+    good = "\n".join([
+        "\t;;#ASMSTART",
+        "\tv_mfma_f32_32x32x16_bf16 v[16:31], v[2:5], v[6:9], v[16:31]",
+        "\ts_nop 15",
+        "\ts_nop 3",
+        "\t;;#ASMEND",
+        "\tv_mov_b64_e32 v[0:1], v[16:17]",
+    ])
+    assert ah.scan(good) == []
+    chain = "\n".join([
+        "\t;;#ASMSTART",
+        "\tv_mfma_f32_32x32x16_bf16 v[16:31], v[2:5], v[6:9], v[16:31]",
+        "\t;;#ASMEND",
+        "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[10:13], v[6:9], a[0:15]",
+        "\t;;#ASMSTART",
+        "\tv_mfma_f32_32x32x16_bf16 v[16:31], v[2:5], v[6:9], v[16:31]",
+        "\ts_nop 15",
+        "\ts_nop 3",
+        "\t;;#ASMEND",
+    ])
+    assert ah.scan(chain) == []
+
+
 @pytest.mark.parametrize("src", sorted(os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "*.hip"))))
 def test_kernel_assembly_has_no_hand_written_load_hazard(src, tmp_path):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
