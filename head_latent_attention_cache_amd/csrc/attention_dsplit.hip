@@ -10,30 +10,29 @@
 // the 512-wide content latents.  A wave cannot keep a 1024-wide query block in
 // registers next to its output accumulators, so here the row is cut in four:
 //
-// Work-group: 4 waves, 64 rows (2 blocks of 32), 32-key tiles.
+// Work-group: 4 waves, 64 rows (2 blocks of 32), 32-key tiles, two LDS tile
+// buffers.  One tile step:
+//  * The tile has landed (barrier); the next tile's copy into the other
+//    buffer is issued right away, one 1 KB piece per wave after each score
+//    MFMA, so it has a whole step to arrive.
 //  * Wave w holds the queries of both row blocks for dims [w, w + 1) * DQK / 4
 //    in registers and forms partial scores S^T_w = K_w . Q_w^T for both
 //    blocks with v_mfma_f32_32x32x16_bf16 (each key fragment read from LDS
-//    feeds two MFMAs).
-//  * The partial scores go through LDS; wave r (r = 0, 1) adds the four
-//    quarters in a fixed order (deterministic) for row block r, applies the
-//    mask and the softmax against the row's fixed reference maximum (the
-//    same scheme as the narrow kernel: no accumulator rescaling, a rerun of
-//    the key loop if a row's maximum outgrows its reference by 2^64), and
-//    publishes the bf16 probabilities.
-//  * O^T (d_c x 64 rows): wave w owns d_c / 4 output dims of both row blocks;
-//    value fragments come from the same LDS tile with ds_read_b64_tr_b16.
-//  * The output product runs one tile behind: in the step of tile i every
-//    wave first reads its value fragments of tile i - 1 into registers, and
-//    after the partial scores of tile i are exchanged, waves 2 and 3 issue
-//    the output MFMAs of tile i - 1 while waves 0 and 1 run the softmax of
-//    tile i (then their own output MFMAs).  Probabilities are double
-//    buffered; two barriers per tile (tile ready and previous probabilities
-//    published; partial scores ready and previous values read).
-//  * Key tiles stream into two LDS buffers with global_load_lds_dwordx4, one
-//    tile ahead (the copy of tile i + 1 overwrites tile i - 1 once its value
-//    fragments are in registers).  Tile classes are computed when needed
-//    (wave-uniform integer arithmetic), which keeps the LDS at 160 KB.
+//    feeds two MFMAs, two independent accumulation chains).  The four waves'
+//    fp32 partials go to LDS (barrier).
+//  * The softmax is shared by all four waves: wave w takes rows 16 w .. 16 w
+//    + 15 of the work-group, four lanes per row and eight keys per lane.  A
+//    lane adds its eight scores over the four quarters in a fixed order
+//    (deterministic), masks, takes the row maximum over the row's four lanes
+//    (two lane swaps) and exponentiates against the row's fixed reference
+//    (the maximum of its first visible tile; no rescaling of the output
+//    accumulators, and a rerun of the key loop if a row's maximum outgrows
+//    its reference by 2^64, as in the narrow kernel).  The bf16
+//    probabilities go back to LDS, into partial-score entries this wave has
+//    already read (barrier).
+//  * O^T (d_c x 64 rows): wave w owns d_c / 4 output dims of both row blocks
+//    and adds this tile's product, value fragments read with
+//    ds_read_b64_tr_b16 from the same LDS tile (issued during the softmax).
 //  * Key splits over work-groups with the deterministic log-sum-exp merge,
 //    XCD-aware block order, as in the narrow kernel.
 #include "attention_common.hpp"
@@ -45,8 +44,7 @@ constexpr int DS_ROWS = 64;   // rows per work-group (2 blocks of 32)
 template <int DC, int DR>
 constexpr size_t attn_dsplit_lds_bytes() {
   return 2 * (size_t)((DC + DR) / 64) * MF_BN * 128   // two key tiles
-         + 6 * 4096                                     // partial scores (row sums at the end)
-         + 2 * 2 * 2048;                                // probabilities [buffer][row block]
+         + 2 * 4 * 64 * 64;                             // partial scores [block][quarter][lane][16 floats]
 }
 
 template <int DC, int DR, bool QKN = false>
@@ -60,14 +58,14 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   constexpr int WDIMS = DC / 4;             // output dims owned by one wave
   constexpr int NDB = WDIMS / 32;           // its 32-dim output blocks
   static_assert(DQK % 64 == 0 && WDIMS % 64 == 0 && TILE_BYTES % (256 * 16) == 0, "widths");
+  static_assert(LOADS <= NKSW, "one copy piece per score step");
   // QK normalisation: waves 0 and 1 hold the content quarters, 2 and 3 the
-  // rotary ones, so the reducing wave scales the sum of the first two
+  // rotary ones, so the content part of a score is the sum of the first two
   static_assert(!QKN || 2 * (DQK / 4) == DC, "content and rotary quarters");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* sx = smem + 2 * TILE_BYTES;                 // [2 blocks][3 sources][4][64][16 B]
-  uint8_t* plds = sx + 6 * 4096;                       // [2 buffers][2 blocks][2 steps][64][16 B]
-  float* lrow = (float*)sx;                            // [64] row sums (epilogue, over the partials)
+  uint8_t* sx = smem + 2 * TILE_BYTES;      // partial scores, then probabilities; row sums at the end
+  float* lrow = (float*)sx;                 // [64] row sums (epilogue)
   const AttnArgs& a = ma.a;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,9 +104,19 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   bool not_full = false;
   for (int i = tid; i < ntl; i += 256) not_full |= tile_class(i) != TILE_FULL;
 
-  // row of this lane in the softmax waves (wave r < 2 owns row block r)
-  const int srow = row0 + (wave & 1) * 32 + (lane & 31);
+  // softmax lane: row 16 wave + ri of the work-group (row block sb, row r32
+  // of the block), keys of score elements 8 sj .. 8 sj + 7 of MFMA lane sl
+  // (keys 16 sj + 4 sg + i and 16 sj + 8 + 4 sg + i, i = 0 .. 3)
+  const int ri = lane & 15, sc = lane >> 4, sj = sc >> 1, sg = sc & 1;
+  const int sb = wave >> 1, r32 = 16 * (wave & 1) + ri;
+  const int sl = r32 + 32 * sg;
+  const int srow = row0 + 32 * sb + r32;
   const int fq = qf0 + (min(srow, n_rows - 1) / H) / P;
+  // partial-score entry (block, quarter, MFMA lane): 64 bytes, its four
+  // 16-byte chunks rotated by the lane (conflict-free 16-lane phases)
+  auto sx_chunk = [&](int blk, int q, int ml, int k) -> LDS_AS uint8_t* {
+    return (LDS_AS uint8_t*)(sx + ((blk * 4 + q) * 64 + ml) * 64 + ((k ^ ((ml >> 2) & 3)) << 4));
+  };
 
   // queries of both row blocks, this wave's quarter of the row
   bf16x8_t qf[2][NKSW];
@@ -141,76 +149,66 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     while (i < ntl && tile_class(i) == TILE_SKIP) ++i;
     return i;
   };
-  // DMA of a key tile: load q of wave w fills 1 KB block (q * 4 + w) = 64-dim
-  // group q, keys 8w .. 8w+7, 8 swizzled chunks per key
+  // DMA of a key tile: piece q of wave w fills 1 KB block (q * 4 + w) =
+  // 64-dim group q, keys 8w .. 8w+7, 8 swizzled chunks per key; past-the-end
+  // keys of the last tile read the last slot (zeroed later)
   const int dma_key = (wave << 3) + (lane >> 3);
   const uint32_t dma_off = (uint32_t)(dma_key * DQK * 2 + (((lane & 7) ^ key_swizzle(dma_key)) << 4));
-  auto issue_loads = [&](int i, int buf) {
+  struct DmaPlan { const uint8_t* tb; uint32_t voff, lds0; };
+  auto dma_plan = [&](int i, int buf) -> DmaPlan {
     const int k0 = (t_begin + i) * MF_BN;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * TILE_BYTES) + wave * 1024;
-    if (k0 + MF_BN <= cap) {
-      const uint8_t* tb = (const uint8_t*)(cache_b + (size_t)k0 * DQK);
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q) dma16_sv(tb + q * 128, dma_off, lds0 + q * 4096);
-    } else {
-      // past-the-end keys of the last tile read the last slot (zeroed later)
-      const bf16_t* tb = cache_b + (size_t)k0 * DQK;
+    DmaPlan d;
+    d.tb = (const uint8_t*)(cache_b + (size_t)k0 * DQK);
+    d.lds0 = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * TILE_BYTES) + wave * 1024;
+    d.voff = dma_off;
+    if (k0 + MF_BN > cap) {
       const int key = min(dma_key, cap - 1 - k0);
-      const int chunk = (lane & 7) ^ key_swizzle(dma_key);
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q) dma16(tb + key * DQK + q * 64 + chunk * 8, lds0 + q * 4096);
+      d.voff = (uint32_t)(key * DQK * 2 + (((lane & 7) ^ key_swizzle(dma_key)) << 4));
     }
+    return d;
   };
-  // O^T[wave's dims][both row blocks] += V^T . P^T for the tile in `vbuf`; the
+  auto dma_piece = [&](const DmaPlan& d, int q) { dma16_sv(d.tb + q * 128, d.voff, d.lds0 + q * 4096); };
+  // value fragments of the tile in `vbuf` for this wave's output dims; the
   // probabilities' key order is the score accumulators' (a fixed
   // permutation), and the value fragments are read in the same order
   const int kq = 4 * g + (li >> 2);
   const int cpart = 2 * (gg & 1) + ((li >> 1) & 1);
   const int vhalf = (li & 1) * 8;
   const int vsw0 = key_swizzle(kq), vsw1 = key_swizzle(kq + 8);
-  // value fragments of the tile in `vbuf` (registers), then the output
-  // MFMAs with the probabilities of P buffer `pbuf`
-  struct VFrag { i16x4_t v0[2][NDB], v1[2][NDB]; };
-  auto read_values = [&](int vbuf, VFrag& f) {
+  struct VFrag { i16x4_t v0[NDB], v1[NDB]; };
+  auto read_values = [&](int vbuf, int j, VFrag& f) {
     const LDS_AS uint8_t* vt =
         (const LDS_AS uint8_t*)(smem + vbuf * TILE_BYTES) + (WDIMS / 64) * wave * MF_BN * 128;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
-        f.v0[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)(gbase + ((((d & 1) * 4 + cpart) ^ vsw0) << 4)));
-        f.v1[j][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
-      }
+    for (int d = 0; d < NDB; ++d) {
+      const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
+      f.v0[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4_t*)(gbase + ((((d & 1) * 4 + cpart) ^ vsw0) << 4)));
+      f.v1[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
+    }
   };
-  auto output_mfma = [&](const VFrag& f, int pbuf) {
-    const LDS_AS uint8_t* pbase = (const LDS_AS uint8_t*)(plds + pbuf * 4096) + lane * 16;
-    bf16x8_t pfr[2][2];
+  // O^T[wave's dims][both row blocks] += V^T . P^T for key step j; the
+  // probabilities of block r, step j sit in chunk 0 of partial-score entry
+  // (r, j, lane)
+  auto output_mfma = [&](const VFrag& f, int j) {
+    bf16x8_t pfr[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int r = 0; r < 2; ++r) pfr[r] = *(const LDS_AS bf16x8_t*)sx_chunk(r, j, lane, 0);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) pfr[j][r] = *(const LDS_AS bf16x8_t*)(pbase + (r * 2 + j) * 1024);
+    for (int d = 0; d < NDB; ++d) {
+      const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[d]);
+      bf16x8_t vf;
+      vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
+      vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[j][d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[j][d]);
-        bf16x8_t vf;
-        vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
-        vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-          o[d * 2 + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[j][r], o[d * 2 + r], 0, 0, 0);
-      }
+      for (int r = 0; r < 2; ++r)
+        o[d * 2 + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[r], o[d * 2 + r], 0, 0, 0);
+    }
   };
-  // partial-score slot of source wave w for row block r (the reducer's own
-  // quarter stays in registers)
-  auto sx_slot = [&](int r, int w) -> LDS_AS uint8_t* {
-    const int src = r == 0 ? w - 1 : (w == 0 ? 0 : w - 1);
-    return (LDS_AS uint8_t*)(sx + (r * 3 + src) * 4096) + lane * 16;
-  };
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  // the softmax lane's eight key positions in the tile (score elements 8 sj + i)
+  auto skey = [&](int i) -> int { return 16 * sj + 8 * (i >> 2) + 4 * sg + (i & 3); };
 
   for (int pass = 0;; ++pass) {
 #pragma unroll
@@ -221,41 +219,38 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   m_run = pass == 0 ? -INFINITY : m_seen;
   bool overflow = false;
 
-  int cur = next_tile(0), bc = 0, pb = 0;
-  bool first = true;
-  // P buffer 1: zeros, for the output product issued in the first step
-  for (int i = tid; i < 2 * 2 * 64; i += 256)
-    *(uint4*)(plds + 4096 + i * 16) = make_uint4(0, 0, 0, 0);
-  if (cur < ntl) issue_loads(cur, 0);
+  int cur = next_tile(0), bc = 0;
+  if (cur < ntl) {
+    const DmaPlan d0 = dma_plan(cur, 0);
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) dma_piece(d0, q);
+  }
   while (cur < ntl) {
     const int nxt = next_tile(cur + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // barrier 1: this tile is in LDS; the previous probabilities are
-    // published; every wave is done with the previous step
+    // barrier 1: this tile is in LDS; every wave is done with the previous
+    // tile (its buffer takes the next one; the probability area is free)
     lds_barrier();
     uint8_t* tile = smem + bc * TILE_BYTES;
     const int k0 = (t_begin + cur) * MF_BN;
     const int cl = all_full ? (int)TILE_FULL : tile_class(cur);
-    // QK normalisation: the reducing waves read the inverse RMS of their
-    // keys (key 8 (e / 4) + 4 g + e % 4 of the tile for score element e)
-    // now; they are used after the score chain
-    float ksc[QKN ? 16 : 1];
+    const bool do_dma = nxt < ntl;
+    const DmaPlan dp = dma_plan(do_dma ? nxt : cur, bc ^ 1);
+    // QK normalisation: the key inverse RMS of this lane's eight keys, read
+    // now and used after the scores
+    float ksc[QKN ? 8 : 1];
     if constexpr (QKN) {
-      if (wave < 2) {
-        const float* kr = a.kscale + (size_t)b * cap;
-        if ((cap & 3) == 0 && k0 + MF_BN <= cap) {
-          // four 16-byte loads (the keys 4 g .. 4 g + 3 of each group of 8)
-          typedef float f32x4_v __attribute__((ext_vector_type(4)));
+      const float* kr = a.kscale + (size_t)b * cap;
+      if ((cap & 3) == 0 && k0 + MF_BN <= cap) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4_v v = *(const f32x4_v*)(kr + k0 + 8 * j + 4 * g);
-            ksc[4 * j] = v[0]; ksc[4 * j + 1] = v[1]; ksc[4 * j + 2] = v[2]; ksc[4 * j + 3] = v[3];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) ksc[e] = kr[min(k0 + 8 * (e >> 2) + 4 * g + (e & 3), cap - 1)];
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t v = *(const f32x4_t*)(kr + k0 + skey(4 * h));
+          ksc[4 * h] = v[0]; ksc[4 * h + 1] = v[1]; ksc[4 * h + 2] = v[2]; ksc[4 * h + 3] = v[3];
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ksc[i] = kr[min(k0 + skey(i), cap - 1)];
       }
     }
     if (cl == TILE_MASKED_ZERO) {
@@ -272,12 +267,9 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       lds_barrier();
     }
-    // value fragments of the previous tile (first step: this tile, which the
-    // zero probabilities cancel)
-    VFrag vf;
-    read_values(first ? bc : bc ^ 1, vf);
 
-    // ---- partial scores of both row blocks over this wave's quarter ----
+    // ---- partial scores of both row blocks over this wave's quarter; the
+    // next tile's copy issued between the MFMAs ----
     f32x16_t s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
@@ -300,118 +292,96 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         if (ks + KPF < NKSW) kb[ks % KPF] = *kaddr(ks + KPF);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, qf[0][ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, qf[1][ks], s1, 0, 0, 0);
+        if (ks < LOADS && do_dma) dma_piece(dp, ks);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    typedef float f32x4_t __attribute__((ext_vector_type(4)));
-    if (wave != 0) {
-      LDS_AS uint8_t* dst = sx_slot(0, wave);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(LDS_AS f32x4_t*)(dst + q * 1024) = f32x4_t{s0[4 * q], s0[4 * q + 1], s0[4 * q + 2], s0[4 * q + 3]};
-    }
-    if (wave != 1) {
-      LDS_AS uint8_t* dst = sx_slot(1, wave);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(LDS_AS f32x4_t*)(dst + q * 1024) = f32x4_t{s1[4 * q], s1[4 * q + 1], s1[4 * q + 2], s1[4 * q + 3]};
+    for (int k = 0; k < 4; ++k) {
+      *(LDS_AS f32x4_t*)sx_chunk(0, wave, lane, k) = f32x4_t{s0[4 * k], s0[4 * k + 1], s0[4 * k + 2], s0[4 * k + 3]};
+      *(LDS_AS f32x4_t*)sx_chunk(1, wave, lane, k) = f32x4_t{s1[4 * k], s1[4 * k + 1], s1[4 * k + 2], s1[4 * k + 3]};
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // barrier 2: partial scores complete; every wave holds its value
-    // fragments of the previous tile, so its buffer takes the next tile
+    // barrier 2: every quarter's partial scores are in LDS
     lds_barrier();
-    if constexpr (QKN) {
-      // the key values have landed before the next tile's copy is issued (a
-      // wait placed after it would also wait for the copy)
-      if (wave < 2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) asm volatile("" ::"v"(ksc[e]));
-    }
-    if (nxt < ntl) issue_loads(nxt, bc ^ 1);
 
-    if (wave < 2) {
-      // full scores of row block `wave`: quarters summed in dim order
-      f32x16_t s;
+    // ---- softmax of this lane's row and eight keys ----
+    float sv[8];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        f32x16_t pw;
-        if (w == wave) {
-          pw = wave == 0 ? s0 : s1;
-        } else {
-          const LDS_AS uint8_t* src = sx_slot(wave, w);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t lo = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj);
+      const f32x4_t hi = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj + 1);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4_t v = *(const LDS_AS f32x4_t*)(src + q * 1024);
-            pw[4 * q] = v[0]; pw[4 * q + 1] = v[1]; pw[4 * q + 2] = v[2]; pw[4 * q + 3] = v[3];
-          }
-        }
-        if (w == 0) s = pw;
-        else
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s[e] += pw[e];
-        if constexpr (QKN) {
-          if (w == 1)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[e] *= ksc[e];
-        }
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = q == 0 ? lo[i] : sv[i] + lo[i];
+        sv[4 + i] = q == 0 ? hi[i] : sv[4 + i] + hi[i];
       }
-      if (cl != TILE_FULL) {
+      if constexpr (QKN) {
+        if (q == 1)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int sl = k0 + 8 * (e >> 2) + 4 * g + (e & 3);
-          bool vis = sl < cap;
-          if (vis) vis = key_visible(fq, ring_frame(sl / P, newest, nm, W), W, fpb);
-          if (!vis) s[e] = -INFINITY;
-        }
+          for (int i = 0; i < 8; ++i) sv[i] *= ksc[i];
       }
-      float mloc = s[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, s[e]);
-      mloc = halves_max(mloc) * c_l2;
-      m_seen = fmaxf(m_seen, mloc);
-      if (m_run == -INFINITY) m_run = mloc;          // first visible tile of the row
-      else if (mloc > m_run + ma.rerun_log2) overflow = true; // rerun with the final maxima
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      float lsum = 0.f;
-      LDS_AS uint8_t* pw = (LDS_AS uint8_t*)(plds + pb * 4096 + wave * 2 * 1024);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8_t pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[j * 8 + e], c_l2, neg_m));
-          lsum += p;
-          pf[e] = (__bf16)p;
-        }
-        // the B-fragment layout of the output product
-        *(LDS_AS bf16x8_t*)(pw + (j * 64 + lane) * 16) = pf;
-      }
-      l_run += lsum;
     }
-    // the previous tile's output product (waves 2 and 3 meanwhile the softmax above)
-    output_mfma(vf, pb ^ 1);
-    bc ^= 1;
-    pb ^= 1;
-    cur = nxt;
-    first = false;
-  }
-  if (!first) {
-    // the last tile's output product
+    // the value fragments of this tile's first key step, read while the
+    // softmax runs
+    VFrag vf0;
+    read_values(bc, 0, vf0);
+    if (cl != TILE_FULL) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int sl2 = k0 + skey(i);
+        bool vis = sl2 < cap;
+        if (vis) vis = key_visible(fq, ring_frame(sl2 / P, newest, nm, W), W, fpb);
+        if (!vis) sv[i] = -INFINITY;
+      }
+    }
+    float mloc = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, sv[i]);
+    {
+      // over the row's four lanes (lane ^ 16, lane ^ 32)
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+      mloc = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+      mloc = halves_max(mloc) * c_l2;
+    }
+    m_seen = fmaxf(m_seen, mloc);
+    if (m_run == -INFINITY) m_run = mloc;                   // first visible tile of the row
+    else if (mloc > m_run + ma.rerun_log2) overflow = true; // rerun with the final maxima
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    bf16x8_t pf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sv[i], c_l2, neg_m));
+      l_run += p;
+      pf[i] = (__bf16)p;
+    }
+    // (chunk 0 of entry (sb, sj, sl): this wave read it above; every lane
+    // that reads this entry's chunks belongs to this wave and has read them)
+    *(LDS_AS bf16x8_t*)sx_chunk(sb, sj, sl, 0) = pf;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // barrier 3: every row's probabilities of this tile are published
     lds_barrier();
-    VFrag vf;
-    read_values(bc ^ 1, vf);
-    output_mfma(vf, pb ^ 1);
+
+    // ---- this tile's output product ----
+    VFrag vf1;
+    read_values(bc, 1, vf1);
+    output_mfma(vf0, 0);
+    output_mfma(vf1, 1);
+    bc ^= 1;
+    cur = nxt;
   }
   if (!block_any(overflow)) break;
   }
 
   // ---- epilogue: row sums to every wave, then O / l ----
-  if (wave < 2) {
-    const float l_tot = halves_sum(l_run);
+  {
+    // the row's sum over its four lanes
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    const float l2 = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const float l_tot = halves_sum(l2);
     const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-    if (g == 0) lrow[wave * 32 + lane] = l_tot;
-    if (g == 0 && srow < n_rows) {
+    if (sc == 0) lrow[32 * sb + r32] = l_tot;
+    if (sc == 0 && srow < n_rows) {
       if (!pc.part_o) {
         if (a.lse) a.lse[(size_t)b * n_rows + srow] = lse;
       } else {
