@@ -219,7 +219,32 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   m_run = pass == 0 ? -INFINITY : m_seen;
   bool overflow = false;
 
+  // QK normalisation: the key inverse RMS of this lane's eight keys of tile
+  // t, loaded one step before the tile is scored (into ksc_next), ahead of
+  // that step's tile copy; the wait at the top of the next step (a
+  // compiler-visible s_waitcnt) covers them, so neither the copy into ksc nor
+  // the use waits for a tile copy in flight.  (ksc_next is not loaded before
+  // the loop: a value from outside the loop would be merged with the loop's
+  // by a register copy, which waits for the load.)
+  float ksc[QKN ? 8 : 1], ksc_next[QKN ? 8 : 1];
+  auto load_ksc = [&](int t, float* dst) {
+    if constexpr (QKN) {
+      const float* kr = a.kscale + (size_t)b * cap;
+      const int kt = (t_begin + t) * MF_BN;
+      if ((cap & 3) == 0 && kt + MF_BN <= cap) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t v = *(const f32x4_t*)(kr + kt + skey(4 * h));
+          dst[4 * h] = v[0]; dst[4 * h + 1] = v[1]; dst[4 * h + 2] = v[2]; dst[4 * h + 3] = v[3];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = kr[min(kt + skey(i), cap - 1)];
+      }
+    }
+  };
   int cur = next_tile(0), bc = 0;
+  bool first_step = true;
   if (cur < ntl) {
     const DmaPlan d0 = dma_plan(cur, 0);
 #pragma unroll
@@ -227,8 +252,10 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   }
   while (cur < ntl) {
     const int nxt = next_tile(cur + 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // vmcnt(0) lgkmcnt(0), as the builtin: the compiler counts it as done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("" ::: "memory");
     // barrier 1: this tile is in LDS; every wave is done with the previous
     // tile (its buffer takes the next one; the probability area is free)
     lds_barrier();
@@ -237,22 +264,21 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     const int cl = all_full ? (int)TILE_FULL : tile_class(cur);
     const bool do_dma = nxt < ntl;
     const DmaPlan dp = dma_plan(do_dma ? nxt : cur, bc ^ 1);
-    // QK normalisation: the key inverse RMS of this lane's eight keys, read
-    // now and used after the scores
-    float ksc[QKN ? 8 : 1];
     if constexpr (QKN) {
-      const float* kr = a.kscale + (size_t)b * cap;
-      if ((cap & 3) == 0 && k0 + MF_BN <= cap) {
+      // (this tile's values arrived before the wait above; the first tile of
+      // a pass loads its own here, and its use waits for this step's copy)
+      if (first_step) {
+        load_ksc(cur, ksc);
+        // wait for them here, before this step's tile copy is issued
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4_t v = *(const f32x4_t*)(kr + k0 + skey(4 * h));
-          ksc[4 * h] = v[0]; ksc[4 * h + 1] = v[1]; ksc[4 * h + 2] = v[2]; ksc[4 * h + 3] = v[3];
-        }
+        for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(ksc[i]));
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ksc[i] = kr[min(k0 + skey(i), cap - 1)];
+        for (int i = 0; i < 8; ++i) ksc[i] = ksc_next[i];
       }
+      load_ksc(do_dma ? nxt : cur, ksc_next);   // (unconditional: no merge copy that would wait for it)
     }
+    first_step = false;
     if (cl == TILE_MASKED_ZERO) {
       // zero never-written (or past-the-end) keys of this tile
       for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
