@@ -22,11 +22,14 @@
 //    fragments (A operand) are read in the same permuted order with
 //    ds_read_b64_tr_b16 from the very LDS tile that served as the keys.
 //  * Key tiles stream into LDS with global_load_lds_dwordx4 (no register
-//    staging) into three buffers, two tiles ahead, with one barrier per tile.
-//    Every tile of the work-group's key range is classified once up front
-//    (skipped / fully visible / masked / masked with never-written keys).  Tile layout: [64-dim group][key][8 x 16 B],
-//    16-byte chunks XOR-swizzled by (key & 7), so that the 16-byte key reads
-//    (consecutive keys, one chunk) hit distinct banks.
+//    staging) into three buffers: the tile being scored, the previous tile
+//    (its output product runs during this tile's score chain) and the next
+//    tile, whose copy is issued between this tile's score MFMAs; one barrier
+//    per tile.  Every tile of the work-group's key range is classified once
+//    up front (skipped / fully visible / masked / masked with never-written
+//    keys).  Tile layout: [64-dim group][key][8 x 16 B], chunk c of key k
+//    stored at c ^ key_swizzle(k) (attention_common.hpp), so that the 16-byte
+//    key reads and the transposed value reads hit distinct banks.
 //  * Softmax in the log2 domain against a fixed reference per row: the
 //    maximum of the row's first visible tile.  Probabilities are
 //    exp2(score - reference), so later scores above the reference only grow
@@ -50,7 +53,7 @@
 
 namespace mla {
 
-constexpr int MF_NBUF = 3;               // LDS tile buffers (loads run two tiles ahead)
+constexpr int MF_NBUF = 3;               // LDS tile buffers: scored, previous (output product), next (copy)
 constexpr int MF_QLDS_STEPS = 8;         // query 16-dim steps kept in LDS (per wave 8 KB)
 constexpr int PREAD_AHEAD = 3;           // score steps between the probability reads and the chain's end
 
