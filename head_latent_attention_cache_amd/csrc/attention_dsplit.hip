@@ -112,11 +112,16 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int sl = r32 + 32 * sg;
   const int srow = row0 + 32 * sb + r32;
   const int fq = qf0 + (min(srow, n_rows - 1) / H) / P;
-  // partial-score entry (block, quarter, MFMA lane): 64 bytes, its four
-  // 16-byte chunks rotated by the lane (conflict-free 16-lane phases)
+  // partial scores in LDS: chunk k (score elements 4k .. 4k + 3) of MFMA
+  // lane ml, block blk, quarter q at [blk][q][k][ml] (16 bytes each): every
+  // MFMA-layout write and probability read is one contiguous 1 KB, every
+  // softmax read four contiguous 256-byte runs.  (Entries of 64 bytes per
+  // lane, even with their chunks rotated, made the 1 KB writes bank-conflict:
+  // a third of the LDS cycles.)
   auto sx_chunk = [&](int blk, int q, int ml, int k) -> LDS_AS uint8_t* {
-    return (LDS_AS uint8_t*)(sx + ((blk * 4 + q) * 64 + ml) * 64 + ((k ^ ((ml >> 2) & 3)) << 4));
+    return (LDS_AS uint8_t*)(sx + (((blk * 4 + q) * 4 + k) * 64 + ml) * 16);
   };
+
 
   // queries of both row blocks, this wave's quarter of the row
   bf16x8_t qf[2][NKSW];
