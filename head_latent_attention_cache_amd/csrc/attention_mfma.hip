@@ -479,8 +479,10 @@ void attn_mfma_kernel(MfmaArgs ma) {
           mfma_vgpr_after_valu(s);
         }
       }
-      // one piece of the next tile's copy every NKS / LOADS steps
-      if (ks % (NKS / LOADS) == 0 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
+      // one piece of the next tile's copy every NKS / LOADS steps, two steps
+      // into each group (measured: decode 2.70 -> 2.27 us per tile step,
+      // chunk 2.48 -> 2.35, against the first step of each group)
+      if (ks % (NKS / LOADS) == 2 && ks / (NKS / LOADS) < LOADS && dma) dma_piece(dp, ks / (NKS / LOADS));
       if (ks >= 1 && ks <= 2 * NDB) pv_read_v1(vprev, f, (ks - 1) / NDB, (ks - 1) % NDB);
       if (!Q4 && ks == NKS - PREAD_AHEAD) pv_read_p(pprev, f);   // (INT4: registers are short)
       if constexpr (Q4) {
