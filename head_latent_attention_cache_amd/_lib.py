@@ -11,6 +11,7 @@ from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_amd.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libmla_probe.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
@@ -62,14 +63,20 @@ SIGNATURES = {
                                  c_void_p, c_void_p]),
     "mla_cache_dequant": (c_int, [_D, _G, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_cache_rope_shift": (c_int, [_D, _G, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
-    "mla_probe_mfma": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
-    "mla_probe_hbm_read": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "mla_status_string": (c_char_p, [c_int]),
     "mla_last_error": (c_char_p, []),
     "mla_abi_version": (c_int, []),
 }
 
+# the measurement probes (include/mla_probe.h, libmla_probe.so)
+PROBE_SIGNATURES = {
+    "mla_probe_mfma": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "mla_probe_hbm_read": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
+    "mla_probe_last_error": (c_char_p, []),
+}
+
 _lib = None
+_probe_lib = None
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -88,6 +95,23 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn.restype = res
         fn.argtypes = args
     _lib = lib
+    return lib
+
+
+def load_probe(path: str | None = None) -> ctypes.CDLL:
+    """Load the measurement-probe library once; raise if it is not built."""
+    global _probe_lib
+    if _probe_lib is not None:
+        return _probe_lib
+    path = path or PROBE_LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m head_latent_attention_cache_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in PROBE_SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _probe_lib = lib
     return lib
 
 

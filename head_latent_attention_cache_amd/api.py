@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 from ._lib import (MLA_BF16, MLA_CACHE_DENSE, MLA_CACHE_INT2, MLA_CACHE_INT4, MLA_F32, MlaDims, MlaGeom,
-                   check, load)
+                   check, load, load_probe)
 
 _TORCH_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
 
@@ -318,24 +318,30 @@ def probe_mfma(n_workgroups, iters, out, toggle=True):
     floating-point operations of the launch.  out: float32 device tensor of
     n_workgroups * 256 elements; toggle: alternate two pseudo-random operand
     pairs (True) or repeat one fixed pair (False)."""
-    lib = load()
+    lib = load_probe()
     _need(out, "out", torch.float32, n_workgroups * 256)
     flops = ctypes.c_double(0.0)
-    check(lib.mla_probe_mfma(_stream(), int(n_workgroups), int(iters), int(bool(toggle)), _ptr(out),
-                             ctypes.byref(flops)))
+    _check_probe(lib.mla_probe_mfma(_stream(), int(n_workgroups), int(iters), int(bool(toggle)), _ptr(out),
+                                    ctypes.byref(flops)))
     return flops.value
 
 
 def probe_hbm_read(src, n_workgroups, out):
     """Launch the streaming-read probe over the bytes of `src` (measurement
     only).  out: int32 device tensor of n_workgroups * 256 elements."""
-    lib = load()
+    lib = load_probe()
     if not (src.is_cuda and src.is_contiguous()):
         raise ValueError("src must be a contiguous GPU tensor")
     _need(out, "out", torch.int32, n_workgroups * 256)
     n_bytes = src.numel() * src.element_size()
-    check(lib.mla_probe_hbm_read(_stream(), _ptr(src), int(n_bytes), int(n_workgroups), _ptr(out)))
+    _check_probe(lib.mla_probe_hbm_read(_stream(), _ptr(src), int(n_bytes), int(n_workgroups), _ptr(out)))
     return n_bytes
+
+
+def _check_probe(status):
+    if status != _lib.MLA_OK:
+        raise _lib.MLAError(status, f"{load().mla_status_string(status).decode()}: "
+                                    f"{load_probe().mla_probe_last_error().decode()}")
 
 
 def raw_lib():

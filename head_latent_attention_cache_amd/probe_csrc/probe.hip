@@ -6,6 +6,9 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <string>
+
+#include "../../include/mla_probe.h"
 
 namespace mla {
 
@@ -95,3 +98,51 @@ hipError_t launch_probe_read(const void* src, size_t n_bytes, int n_workgroups, 
 }
 
 }  // namespace mla
+
+namespace {
+
+thread_local std::string g_probe_error;
+
+mla_status probe_fail(mla_status st, const char* msg) {
+  g_probe_error = msg;
+  return st;
+}
+
+mla_status probe_launched(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_OK;
+  g_probe_error = std::string(what) + ": " + hipGetErrorString(e);
+  return MLA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_probe_last_error(void) { return g_probe_error.c_str(); }
+
+mla_status mla_probe_mfma(void* stream, int32_t n_workgroups, int32_t iters, int32_t toggle, float* out,
+                          double* flops) {
+  g_probe_error.clear();
+  if (n_workgroups <= 0 || n_workgroups > (1 << 20) || iters <= 0 || iters > (1 << 24))
+    return probe_fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [1, 2^20] and iters in [1, 2^24]");
+  if (toggle != 0 && toggle != 1) return probe_fail(MLA_ERR_INVALID_ARG, "toggle must be 0 or 1");
+  if (!out || !aligned16(out)) return probe_fail(MLA_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
+  if (flops) *flops = mla::probe_mfma_flops(n_workgroups, iters);
+  return probe_launched(mla::launch_probe_mfma(n_workgroups, iters, toggle, out, (hipStream_t)stream), "MFMA probe");
+}
+
+mla_status mla_probe_hbm_read(void* stream, const void* src, int64_t n_bytes, int32_t n_workgroups,
+                              uint32_t* out) {
+  g_probe_error.clear();
+  if (n_bytes <= 0 || n_bytes % 16) return probe_fail(MLA_ERR_INVALID_ARG, "n_bytes must be a positive multiple of 16");
+  if (n_workgroups <= 0 || n_workgroups > (1 << 20))
+    return probe_fail(MLA_ERR_INVALID_ARG, "n_workgroups must be in [1, 2^20]");
+  if (!src || !aligned16(src)) return probe_fail(MLA_ERR_INVALID_ARG, "src is NULL or not 16-byte aligned");
+  if (!out || !aligned16(out)) return probe_fail(MLA_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
+  return probe_launched(mla::launch_probe_read(src, (size_t)n_bytes, n_workgroups, out, (hipStream_t)stream),
+                        "HBM read probe");
+}
+
+}  // extern "C"

@@ -13,10 +13,11 @@ from mla_inputs import CONFIGS, SMALL_CONFIGS, get_config
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "mla_probe.h")
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text))
 
@@ -32,6 +33,18 @@ def test_every_declared_symbol_is_exported(lib):
     assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
+    assert not any(n.startswith("mla_probe") for n in names)
+
+
+def test_probe_library_exports_its_header():
+    """The measurement probes live in their own library, off the MLA ABI."""
+    plib = _lib.load_probe()
+    names = _declared(PROBE_HEADER)
+    assert names == set(_lib.PROBE_SIGNATURES), names ^ set(_lib.PROBE_SIGNATURES)
+    for n in names:
+        assert hasattr(plib, n), n
+    mla_lib = _lib.load()
+    assert not hasattr(mla_lib, "mla_probe_mfma") and not hasattr(mla_lib, "mla_probe_hbm_read")
 
 
 def test_version_and_status_strings(lib):
@@ -231,8 +244,9 @@ def test_qk_norm_entry_checks(lib):
                                    fake) == _lib.MLA_ERR_UNSUPPORTED
 
 
-def test_probe_argument_checks(lib):
+def test_probe_argument_checks():
     """The measurement probes reject bad sizes and pointers before any launch."""
+    lib = _lib.load_probe()
     inv = -1
     fake = ctypes.c_void_p(1 << 20)          # never dereferenced: the checks fail first
     assert lib.mla_probe_mfma(None, 0, 1, 0, fake, None) == inv
@@ -244,3 +258,4 @@ def test_probe_argument_checks(lib):
     assert lib.mla_probe_hbm_read(None, fake, 32, 0, fake) == inv
     assert lib.mla_probe_hbm_read(None, None, 32, 1, fake) == inv
     assert lib.mla_probe_hbm_read(None, fake, 32, 1, ctypes.c_void_p(3)) == inv
+    assert b"aligned" in lib.mla_probe_last_error()
