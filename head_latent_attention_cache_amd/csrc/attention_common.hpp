@@ -114,6 +114,39 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// Eight cache values bf16(q * s) from their packed codes (the low-bit
+// cache: INT4 or INT2 content codes, INT4 rotary codes) and their fp16 scale
+// s (already converted, 0 for never-written slots).  Each value is rounded
+// once to nearest even from the exact product (q * s is exact in fp32: at
+// most 4 x 11 significant bits).  4-bit codes (`codes`: 8 nibbles, element
+// 2i in the low nibble of byte i): offset binary (code ^ 8 = q + 8) in single
+// bytes, byte to float, then q s = (q + 8) s - 8 s in one exact FMA.  2-bit
+// codes (`codes`: bits 2k .. 2k + 1 of byte j hold element 4j + k): the four
+// values bf16(q s), q = 0, 1, -2, -1 (two's complement), form an 8-byte table
+// that v_perm_b32 indexes.
+__device__ __forceinline__ u32x4_t dequant8_bf16(uint32_t codes, float sc, bool two_bit) {
+  u32x4_t out;
+  if (two_bit) {
+    const uint32_t lut_lo = pack2_bf16(0.f, sc), lut_hi = pack2_bf16(-2.f * sc, -sc);
+    const uint32_t w = codes | (codes << 14);   // code 2p + 1 copied to bit 4p + 16
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // codes 2p, 2p + 1 at bits 0 and 16, then byte selectors (2c, 2c + 1) per half
+      const uint32_t t = (w >> (4 * p)) & 0x00030003u;
+      out[p] = __builtin_amdgcn_perm(lut_hi, lut_lo, t * 0x202u + 0x01000100u);
+    }
+  } else {
+    const uint32_t ev = (codes & 0x0F0F0F0Fu) ^ 0x08080808u;          // elements 0, 2, 4, 6
+    const uint32_t od = ((codes >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1, 3, 5, 7
+    const float off = -8.f * sc;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      out[p] = pack2_bf16(fmaf((float)((ev >> (8 * p)) & 0xFFu), sc, off),
+                          fmaf((float)((od >> (8 * p)) & 0xFFu), sc, off));
+  }
+  return out;
+}
+
 // 16-byte chunk swizzle of a key row: chunk c of key k sits at position
 // c ^ key_swizzle(k) of the row's 128 bytes (a key row spans half of the
 // 256-byte, 64-bank LDS period).  Requirements:

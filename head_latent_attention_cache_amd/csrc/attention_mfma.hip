@@ -369,9 +369,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
                       : *(const LDS_AS uint16_t*)(d.sp + Q4_CODE_BYTES + Q4_CS_BYTES + dq_key * 2);
     return r;
   };
-  // Every value is bf16(q * s) rounded once to nearest even from the exact
-  // product (q * s is exact in fp32: at most 4 x 11 significant bits), the
-  // same bits as converting q, multiplying and rounding.
+  // every value is bf16(q * s), rounded once (dequant8_bf16)
   auto dq_store = [&](const DqPlan& d, int i, DqRaw r) {
     const bool content = i < DC / 64;
     // the conversion starts here, not next to the reads (no early wait for them)
@@ -379,31 +377,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
     // a zero scale for never-written slots (their bytes are arbitrary)
     const float s16 = __half2float(__ushort_as_half((unsigned short)r.sbits));
     const float sc = d.keep != 0.f ? s16 : 0.f;
-    u32x4_t out;
-    if (content && CB == 2) {
-      // 2-bit codes: the four values bf16(q s), q = 0, 1, -2, -1 (code
-      // 0 .. 3, two's complement), form an 8-byte table that v_perm_b32
-      // indexes; element 4j + k is bits 2k .. 2k + 1 of byte j
-      const uint32_t lut_lo = pack2_bf16(0.f, sc), lut_hi = pack2_bf16(-2.f * sc, -sc);
-      const uint32_t w = r.codes | (r.codes << 14);   // code 2p + 1 copied to bit 4p + 16
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        // codes 2p, 2p + 1 at bits 0 and 16, then byte selectors (2c, 2c + 1) per half
-        const uint32_t t = (w >> (4 * p)) & 0x00030003u;
-        out[p] = __builtin_amdgcn_perm(lut_hi, lut_lo, t * 0x202u + 0x01000100u);
-      }
-    } else {
-      // 4-bit codes: offset binary (code ^ 8 = q + 8) in single bytes, byte
-      // to float conversion, then q s = (q + 8) s - 8 s in one exact FMA
-      const uint32_t ev = (r.codes & 0x0F0F0F0Fu) ^ 0x08080808u;          // elements 0, 2, 4, 6
-      const uint32_t od = ((r.codes >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1, 3, 5, 7
-      const float off = -8.f * sc;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        out[p] = pack2_bf16(fmaf((float)((ev >> (8 * p)) & 0xFFu), sc, off),
-                            fmaf((float)((od >> (8 * p)) & 0xFFu), sc, off));
-    }
-    *(LDS_AS u32x4_t*)(d.tp + i * MF_BN * 128) = out;
+    *(LDS_AS u32x4_t*)(d.tp + i * MF_BN * 128) = dequant8_bf16(r.codes, sc, content && CB == 2);
   };
   auto dequant_chunk = [&](const DqPlan& d, int i) { dq_store(d, i, dq_load(d, i)); };
   auto dequant = [&](int t, int sidx, int tbuf) {
@@ -762,6 +736,40 @@ void attn_mfma_kernel(MfmaArgs ma) {
   }
 }
 
+// A low-bit cache attended by a chunk of queries (two or more row blocks per
+// sequence) is dequantised once per call into a bf16 copy in the workspace
+// ([B][capacity][d_c + d_r], the dense cache layout), which the dense kernel
+// then reads: the fused path dequantises every tile once per row block that
+// reads it, on the VALU, while the copy costs one pass over the packed bytes
+// and the bf16 rows.  The values are those the fused path forms
+// (dequant8_bf16); never-written slots hold whatever their codes give, and
+// the dense kernel zeroes them in LDS as it does for a dense cache.  Thread:
+// one 16-byte chunk (8 values) of one row; INT4 or INT2 content codes, INT4
+// rotary codes.
+template <int CB>
+__global__ __launch_bounds__(256) void predequant_kernel(size_t rows, const uint8_t* __restrict__ codes,
+                                                         const __half* __restrict__ cscale,
+                                                         const __half* __restrict__ rscale, bf16_t* __restrict__ out) {
+  constexpr int DC = 512, DR = 64, DQK = DC + DR, CH = DQK / 8;
+  constexpr int CODE_ROW = DC * CB / 8 + DR / 2;
+  const size_t total = rows * CH;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    const size_t r = e / CH;
+    const int c = (int)(e % CH);
+    const uint8_t* row = codes + r * CODE_ROW;
+    uint32_t w;
+    float sc;
+    if (c < DC / 8) {
+      w = CB == 4 ? *(const uint32_t*)(row + 4 * c) : (uint32_t)*(const uint16_t*)(row + 2 * c);
+      sc = __half2float(cscale[r * (DC / 32) + c / 4]);
+    } else {
+      w = *(const uint32_t*)(row + DC * CB / 8 + 4 * (c - DC / 8));
+      sc = __half2float(rscale[r]);
+    }
+    *(u32x4_t*)(out + r * DQK + c * 8) = dequant8_bf16(w, sc, CB == 2 && c < DC / 8);
+  }
+}
+
 // merge of the key splits: o = sum_i w_i o_i / sum_i w_i, w_i = exp(lse_i - max)
 // one wave per row, 8 consecutive dims per lane; fixed split order
 // (deterministic).  The LSEs and partial rows of MG splits are loaded
@@ -992,23 +1000,63 @@ void attn_plan_bind(MfmaArgs* ma, void* ws) {
   }
 }
 
+// the low-bit cache dequantised once per call (see predequant_kernel): when
+// each cache row is read by two or more row blocks; MLA_LOWBIT_PREDEQUANT=0 or
+// =1 forces either path (testing)
+static bool use_predequant(const Dims& d, int n_rows) {
+  static const int forced = [] {
+    const char* e = getenv("MLA_LOWBIT_PREDEQUANT");
+    return e && (e[0] == '0' || e[0] == '1') ? e[0] - '0' : -1;
+  }();
+  if (!lowbit_cache(d)) return false;
+  if (forced >= 0) return forced == 1;
+  return (n_rows + MF_ROWS - 1) / MF_ROWS >= 2;
+}
+
+// workspace: the plan's partials, then (dequantised path) the bf16 rows at a 256-byte boundary
+static size_t predequant_offset(size_t plan_bytes) { return (plan_bytes + 255) & ~(size_t)255; }
+static size_t predequant_bytes(const Dims& d, const Geo& g, int batch) {
+  return (size_t)batch * g.capacity * (d.d_c + d.d_r) * sizeof(bf16_t);
+}
+
 size_t attn_mfma_workspace(const Dims& d, const Geo& g, int batch, int n_rows) {
   MfmaArgs ma;
   ma.a.d = d;
   ma.a.batch = batch;
   ma.a.n_rows = n_rows;
   attn_plan(d, g, batch, n_rows, MF_ROWS, &ma);
-  return attn_plan_workspace(ma);
+  const size_t plan = attn_plan_workspace(ma);
+  return use_predequant(d, n_rows) ? predequant_offset(plan) + predequant_bytes(d, g, batch) : plan;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   MfmaArgs ma;
   ma.a = a;
   const int blocks = attn_plan(a.d, a.g, a.batch, a.n_rows, MF_ROWS, &ma);
-  if (ws_bytes < attn_plan_workspace(ma)) return hipErrorInvalidValue;
+  const size_t plan = attn_plan_workspace(ma);
+  if (use_predequant(a.d, a.n_rows)) {
+    // the packed rows once into bf16, then the dense kernel over them
+    const size_t off = predequant_offset(plan), rows = (size_t)a.batch * a.g.capacity;
+    if (ws_bytes < off + predequant_bytes(a.d, a.g, a.batch)) return hipErrorInvalidValue;
+    bf16_t* dq = (bf16_t*)((uint8_t*)ws + off);
+    const __half* cs = (const __half*)a.aux;
+    const __half* rs = cs + rows * (a.d.d_c / 32);
+    const size_t chunks = rows * ((a.d.d_c + a.d.d_r) / 8);
+    const unsigned grid = (unsigned)std::min<size_t>((chunks + 255) / 256, 65536);
+    if (a.d.cache_fmt == MLA_CACHE_INT2)
+      predequant_kernel<2><<<grid, 256, 0, st>>>(rows, (const uint8_t*)a.cache, cs, rs, dq);
+    else
+      predequant_kernel<4><<<grid, 256, 0, st>>>(rows, (const uint8_t*)a.cache, cs, rs, dq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ma.a.cache = dq;
+    ma.a.d.cache_fmt = MLA_CACHE_DENSE;
+  } else if (ws_bytes < plan) {
+    return hipErrorInvalidValue;
+  }
   attn_plan_bind(&ma, ws);
   constexpr int DC = 512, DR = 64;
-  const int fmt = a.d.cache_fmt;
+  const int fmt = ma.a.d.cache_fmt;
   const bool qkn = a.kscale != nullptr;
   const size_t shm = fmt == MLA_CACHE_INT4   ? (qkn ? attn_mfma_lds_bytes<DC, DR, true, 4, true>()
                                                     : attn_mfma_lds_bytes<DC, DR, true, 4>())

@@ -70,3 +70,16 @@ def test_two_group_split_plan(gpu_lib, key, plan, tmp_path):
     d = _run(key, {"MLA_ATTN_PLAN": plan}, "plan", tmp_path)
     one = _run(key, {"MLA_ATTN_SPLITS": "1"}, "one", tmp_path)
     assert np.max(np.abs(d - one)) <= 2e-2
+
+
+@pytest.mark.parametrize("key", [5, 6])
+def test_lowbit_dequantised_once_matches_fused(gpu_lib, key, tmp_path):
+    # a low-bit cache read by several row blocks is dequantised once per call
+    # into bf16 rows that the dense kernel reads; the fused path (every tile
+    # dequantised in LDS) forced on the same inputs; both against the oracle
+    # in the child, and the two agree to the bit (same bf16 operands, same
+    # kernel arithmetic)
+    once = _run(key, {"MLA_LOWBIT_PREDEQUANT": "1"}, "once", tmp_path)
+    fused = _run(key, {"MLA_LOWBIT_PREDEQUANT": "0"}, "fused", tmp_path)
+    assert np.max(np.abs(once - fused)) <= 2e-2
+    print("[case] bit-identical:", bool(np.array_equal(once, fused)), flush=True)
