@@ -736,7 +736,7 @@ void attn_mfma_kernel(MfmaArgs ma) {
   }
 }
 
-// A low-bit cache attended by a chunk of queries (two or more row blocks per
+// A low-bit cache attended by a chunk of queries (four or more row blocks per
 // sequence) is dequantised once per call into a bf16 copy in the workspace
 // ([B][capacity][d_c + d_r], the dense cache layout), which the dense kernel
 // then reads: the fused path dequantises every tile once per row block that
@@ -1001,8 +1001,10 @@ void attn_plan_bind(MfmaArgs* ma, void* ws) {
 }
 
 // the low-bit cache dequantised once per call (see predequant_kernel): when
-// each cache row is read by two or more row blocks; MLA_LOWBIT_PREDEQUANT=0 or
-// =1 forces either path (testing)
+// each cache row is read by four or more row blocks (with fewer, e.g. a few
+// decode tokens over a long cache, writing and re-reading the bf16 copy can
+// cost more than dequantising each tile a few times); MLA_LOWBIT_PREDEQUANT=0
+// or =1 forces either path (testing)
 static bool use_predequant(const Dims& d, int n_rows) {
   static const int forced = [] {
     const char* e = getenv("MLA_LOWBIT_PREDEQUANT");
@@ -1010,7 +1012,7 @@ static bool use_predequant(const Dims& d, int n_rows) {
   }();
   if (!lowbit_cache(d)) return false;
   if (forced >= 0) return forced == 1;
-  return (n_rows + MF_ROWS - 1) / MF_ROWS >= 2;
+  return (n_rows + MF_ROWS - 1) / MF_ROWS >= 4;
 }
 
 // workspace: the plan's partials, then (dequantised path) the bf16 rows at a 256-byte boundary
