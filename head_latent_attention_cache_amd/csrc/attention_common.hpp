@@ -211,8 +211,13 @@ struct Piece {
 // the piece of this work-group.  Work-group id runs on XCD id % 8 as number
 // id / 8 of that XCD; every XCD takes its share of the first group's pieces
 // first, then of the second group's, each group in (b, split, rb) order
-// (consecutive work-groups of an XCD attend the same key range).
-__device__ __forceinline__ Piece wg_piece(const MfmaArgs& ma) {
+// (consecutive work-groups of an XCD attend the same key range).  With
+// `chip_order` and a one-group plan the pieces go in work-group id order
+// instead: the 256 work-groups running at once (32 per XCD) attend one key
+// range, so a key range too large for the L2s is streamed from HBM once into
+// the last-level cache that all XCDs share, not once per pair of XCDs with
+// four ranges competing for that cache.
+__device__ __forceinline__ Piece wg_piece(const MfmaArgs& ma, bool chip_order = false) {
   const int B = ma.a.batch, n_rows = ma.a.n_rows, DC = ma.a.d.d_c;
   const int N = gridDim.x, id = blockIdx.x;
   const int x = id & 7, j = id >> 3;
@@ -221,7 +226,7 @@ __device__ __forceinline__ Piece wg_piece(const MfmaArgs& ma) {
   const int big_before = x * (NB / 8) + min(x, NB % 8);
   int b, split, rb, tps;
   if (j < big_x) {
-    const int k = big_before + j;
+    const int k = chip_order && NB == N ? id : big_before + j;
     const int per_b = ma.ns_a * ma.n_a;
     b = k / per_b;
     split = (k % per_b) / ma.n_a;

@@ -1,5 +1,6 @@
 // Latent attention on bf16 MFMA for wide cache rows: the score contraction
-// split over the waves of a work-group.
+// split over the waves of a work-group, the softmax of one key tile hidden
+// under the score products of the next.
 //
 // "VideoMLA: Compressing Video Diffusion Memory by 92.7% with Low-Rank Latent
 // Attention" (review), Core Mechanism: the long-horizon cache row is a
@@ -9,62 +10,81 @@
 // dot product with the concatenated row), while the output still sums only
 // the 512-wide content latents.  A wave cannot keep a 1024-wide query block in
 // registers next to its output accumulators, so here the row is cut in four:
+// wave w takes content dims [w, w + 1) * d_c / 4 and rotary dims
+// [w, w + 1) * d_r / 4 of both 32-row blocks of the work-group (64 rows).
 //
-// Work-group: 4 waves, 64 rows (2 blocks of 32), 32-key tiles, two LDS tile
-// buffers.  One tile step:
-//  * The tile has landed (barrier); the next tile's copy into the other
-//    buffer is issued right away, one 1 KB piece per wave after each score
-//    MFMA, so it has a whole step to arrive.
-//  * Wave w holds the queries of both row blocks for dims [w, w + 1) * DQK / 4
-//    in registers and forms partial scores S^T_w = K_w . Q_w^T for both
-//    blocks with v_mfma_f32_32x32x16_bf16 (each key fragment read from LDS
-//    feeds two MFMAs, two independent accumulation chains).  The four waves'
-//    fp32 partials go to LDS (barrier).
-//  * The softmax is shared by all four waves: wave w takes rows 16 w .. 16 w
-//    + 15 of the work-group, four lanes per row and eight keys per lane.  A
-//    lane adds its eight scores over the four quarters in a fixed order
+// Only the content part of a key tile goes through LDS (it is read twice:
+// as keys by the scores and, transposed, as values by the output product);
+// each wave loads its rotary quarter of the tile's keys straight into the
+// registers the score MFMAs take (no LDS bytes for it), one tile ahead.  The
+// content is loaded into registers one step ahead as well and written to its
+// LDS buffer at the top of the step that scores it.  Three content buffers
+// (96 KB), the partial scores (32 KB) and the probabilities (4 KB) take
+// 132 KB of LDS.  Step s of the key loop, with tiles t_s (attended now),
+// t_s+1 (scored now) and t_s+2 (loaded now):
+//  * top: every load of the previous step has landed; t_s+1's content goes
+//    to LDS; barrier A (the partial scores of t_s and t_s+1's content are in
+//    LDS).  Wave 0 starts the L2 prefetch of a slice of the tile eight steps
+//    ahead.
+//  * phase 1: the partial scores of t_s+1 for both row blocks,
+//    S^T_w = K_w . Q_w^T with v_mfma_f32_32x32x16_bf16 (each key fragment
+//    feeds two MFMAs: two independent accumulation chains), rotary steps from
+//    registers (each register set reloaded with t_s+2 right after its
+//    MFMAs) alternating with content steps from LDS, and t_s+2's content
+//    loads between them; and, spread between the same MFMAs, the softmax of
+//    t_s: wave w takes rows 16 w .. 16 w + 15, four lanes per row and eight
+//    keys per lane, adds the four quarters' partials in a fixed order
 //    (deterministic), masks, takes the row maximum over the row's four lanes
 //    (two lane swaps) and exponentiates against the row's fixed reference
 //    (the maximum of its first visible tile; no rescaling of the output
 //    accumulators, and a rerun of the key loop if a row's maximum outgrows
-//    its reference by 2^64, as in the narrow kernel).  The bf16
-//    probabilities go back to LDS, into partial-score entries this wave has
-//    already read (barrier).
-//  * O^T (d_c x 64 rows): wave w owns d_c / 4 output dims of both row blocks
-//    and adds this tile's product, value fragments read with
-//    ds_read_b64_tr_b16 from the same LDS tile (issued during the softmax).
-//  * Key splits over work-groups with the deterministic log-sum-exp merge,
-//    XCD-aware block order, as in the narrow kernel.
+//    its reference by 2^64, as in the narrow kernel); the bf16 probabilities
+//    go to LDS.  Barrier B.
+//  * phase 2: O^T (d_c x 64 rows) += V^T . P^T for t_s (wave w owns d_c / 4
+//    output dims of both row blocks, value fragments read with
+//    ds_read_b64_tr_b16 from t_s's content buffer during phase 1), with the
+//    partial scores of t_s+1 written to LDS between its two key steps.
+// What bounds it: the vector-memory side.  64 KB of cache rows per 64 rows
+// and 32 keys is 2.5 times the bytes per MFMA of the narrow kernel (128
+// rows per 1152-byte row); a step with every load removed runs in 60 % of
+// the time.  Key splits over work-groups with the deterministic log-sum-exp
+// merge, as in the narrow kernel; pieces in work-group id order.
 #include "attention_common.hpp"
 
 namespace mla {
 
 constexpr int DS_ROWS = 64;   // rows per work-group (2 blocks of 32)
 
+constexpr int DS_PF_AHEAD = 8;  // L2 prefetch distance (tiles)
+
 template <int DC, int DR>
 constexpr size_t attn_dsplit_lds_bytes() {
-  return 2 * (size_t)((DC + DR) / 64) * MF_BN * 128   // two key tiles
-         + 2 * 4 * 64 * 64;                             // partial scores [block][quarter][lane][16 floats]
+  return 3 * (size_t)(DC / 64) * MF_BN * 128   // three content tiles
+         + 2 * 4 * 64 * 64                       // partial scores [block][quarter][chunk][lane] (16 B)
+         + 2 * 2 * 64 * 16                       // probabilities [block][key step][lane] (16 B)
+         + 1024                                  // landing area of the L2 prefetch (never read)
+         + 2 * 256;                              // key scales of QK normalisation, two tiles
 }
 
 template <int DC, int DR, bool QKN = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_dsplit_kernel(MfmaArgs ma) {
   constexpr int DQK = DC + DR;
-  constexpr int NCG = DQK / 64;             // 64-dim groups per row (128 B)
-  constexpr int TILE_BYTES = NCG * MF_BN * 128;
-  constexpr int LOADS = TILE_BYTES / (256 * 16);
-  constexpr int NKSW = DQK / 64;            // 16-dim score steps of one wave (a quarter row)
+  constexpr int CT_BYTES = (DC / 64) * MF_BN * 128;   // content part of a key tile
+  constexpr int LOADS = CT_BYTES / (256 * 16);        // its 1 KB copy pieces per wave
+  constexpr int NKC = DC / 64;              // 16-dim content score steps of one wave (d_c / 4 dims)
+  constexpr int NKR = DR / 64;              // rotary score steps of one wave (d_r / 4 dims)
+  constexpr int NKS = NKC + NKR;
   constexpr int WDIMS = DC / 4;             // output dims owned by one wave
   constexpr int NDB = WDIMS / 32;           // its 32-dim output blocks
-  static_assert(DQK % 64 == 0 && WDIMS % 64 == 0 && TILE_BYTES % (256 * 16) == 0, "widths");
-  static_assert(LOADS <= NKSW, "one copy piece per score step");
-  // QK normalisation: waves 0 and 1 hold the content quarters, 2 and 3 the
-  // rotary ones, so the content part of a score is the sum of the first two
-  static_assert(!QKN || 2 * (DQK / 4) == DC, "content and rotary quarters");
+  static_assert(DC == 512 && DR % 64 == 0 && CT_BYTES % 4096 == 0, "widths");
+  static_assert(LOADS <= NKS, "one copy piece per score step");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* sx = smem + 2 * TILE_BYTES;      // partial scores, then probabilities; row sums at the end
+  uint8_t* sx = smem + 3 * CT_BYTES;        // partial scores; row sums at the end
+  uint8_t* pbuf = sx + 2 * 4 * 64 * 64;     // probabilities
+  uint8_t* pf_sink = pbuf + 2 * 2 * 64 * 16;  // L2 prefetch landing area
+  uint8_t* ksl = pf_sink + 1024;             // key scales, two 256-byte slots
   float* lrow = (float*)sx;                 // [64] row sums (epilogue)
   const AttnArgs& a = ma.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -72,7 +92,10 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int g = lane >> 5;
   const int P = a.g.P, W = a.g.window, cap = a.g.capacity, fpb = a.g.fpb;
 
-  const Piece pc = wg_piece(ma);
+  // (pieces in work-group id order: the long key ranges of this kernel's
+  // workloads exceed the L2s, and a key range shared by every XCD at once
+  // stays in the last-level cache; measured 15 % faster on the long video)
+  const Piece pc = wg_piece(ma, true);
   const int b = pc.rbg / ma.n_rb;
   const int rb = pc.rbg % ma.n_rb;
 
@@ -88,7 +111,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int t_begin = pc.t0;
   const int ntl = pc.t1 - pc.t0;
   // work-group OR through four flags in the partial-score area (free where
-  // this is called); HIP's __syncthreads_or would add static LDS beyond 160 KB
+  // this is called); HIP's __syncthreads_or would add static LDS
   auto block_any = [&](bool v) -> bool {
     const bool wv = __builtin_amdgcn_ballot_w64(v) != 0;
     __syncthreads();
@@ -114,25 +137,32 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   const int fq = qf0 + (min(srow, n_rows - 1) / H) / P;
   // partial scores in LDS: chunk k (score elements 4k .. 4k + 3) of MFMA
   // lane ml, block blk, quarter q at [blk][q][k][ml] (16 bytes each): every
-  // MFMA-layout write and probability read is one contiguous 1 KB, every
-  // softmax read four contiguous 256-byte runs.  (Entries of 64 bytes per
-  // lane, even with their chunks rotated, made the 1 KB writes bank-conflict:
-  // a third of the LDS cycles.)
+  // MFMA-layout write is one contiguous 1 KB, every softmax read four
+  // contiguous 256-byte runs.  (Entries of 64 bytes per lane, even with their
+  // chunks rotated, made the 1 KB writes bank-conflict: a third of the LDS
+  // cycles.)
   auto sx_chunk = [&](int blk, int q, int ml, int k) -> LDS_AS uint8_t* {
     return (LDS_AS uint8_t*)(sx + (((blk * 4 + q) * 4 + k) * 64 + ml) * 16);
   };
+  // probabilities of block blk, key step j (16 keys) in the MFMA B-operand
+  // layout of lane ml: 16 bytes at [blk][j][ml]
+  auto p_entry = [&](int blk, int j, int ml) -> LDS_AS uint8_t* {
+    return (LDS_AS uint8_t*)(pbuf + ((blk * 2 + j) * 64 + ml) * 16);
+  };
 
-
-  // queries of both row blocks, this wave's quarter of the row
-  bf16x8_t qf[2][NKSW];
+  // queries of both row blocks, this wave's content and rotary quarters:
+  // steps 0 .. NKC - 1 content dims wave * d_c / 4 + 16 ks, then rotary dims
+  // d_c + wave * d_r / 4 + 16 (ks - NKC)
+  bf16x8_t qf[2][NKS];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int row = row0 + r * 32 + (lane & 31);
     const bool ok = row < n_rows;
-    const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (ok ? row : 0)) * DQK + wave * (DQK / 4);
+    const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (ok ? row : 0)) * DQK + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < NKSW; ++ks) {
-      bf16x8_t v = *(const bf16x8_t*)(qrow + ks * 16 + g * 8);
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int dim = ks < NKC ? wave * (DC / 4) + ks * 16 : DC + wave * (DR / 4) + (ks - NKC) * 16;
+      bf16x8_t v = *(const bf16x8_t*)(qrow + dim);
       if (!ok) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
@@ -154,25 +184,55 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     while (i < ntl && tile_class(i) == TILE_SKIP) ++i;
     return i;
   };
-  // DMA of a key tile: piece q of wave w fills 1 KB block (q * 4 + w) =
-  // 64-dim group q, keys 8w .. 8w+7, 8 swizzled chunks per key; past-the-end
-  // keys of the last tile read the last slot (zeroed later)
-  const int dma_key = (wave << 3) + (lane >> 3);
-  const uint32_t dma_off = (uint32_t)(dma_key * DQK * 2 + (((lane & 7) ^ key_swizzle(dma_key)) << 4));
-  struct DmaPlan { const uint8_t* tb; uint32_t voff, lds0; };
-  auto dma_plan = [&](int i, int buf) -> DmaPlan {
-    const int k0 = (t_begin + i) * MF_BN;
-    DmaPlan d;
-    d.tb = (const uint8_t*)(cache_b + (size_t)k0 * DQK);
-    d.lds0 = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * TILE_BYTES) + wave * 1024;
-    d.voff = dma_off;
-    if (k0 + MF_BN > cap) {
-      const int key = min(dma_key, cap - 1 - k0);
-      d.voff = (uint32_t)(key * DQK * 2 + (((lane & 7) ^ key_swizzle(dma_key)) << 4));
-    }
-    return d;
+  auto class_of = [&](int i) -> int { return all_full ? (int)TILE_FULL : tile_class(i); };
+  // Copy of a tile's content into LDS through registers: piece q of wave w
+  // is 1 KB block (q * 4 + w) of the LDS tile (64-dim group q, keys 8w ..
+  // 8w + 7, 16 bytes per lane, chunk c of a key read from c ^ its swizzle),
+  // loaded into `cst` during one step and written at the top of the next;
+  // past-the-end keys of the last tile read the last slot (zeroed later).
+  // (Ordinary loads here: global-to-LDS DMA loads issued next to the rotary
+  // register loads cost this kernel several times what either costs alone.)
+  const int cp_key = (wave << 3) + (lane >> 3);
+  u32x4_t cst[LOADS];
+  auto content_src = [&](int t) -> const uint8_t* {
+    const int k0 = (t_begin + t) * MF_BN;
+    const int key = min(cp_key, cap - 1 - k0);
+    return (const uint8_t*)(cache_b + ((size_t)k0 + key) * DQK) + (((lane & 7) ^ key_swizzle(cp_key)) << 4);
   };
-  auto dma_piece = [&](const DmaPlan& d, int q) { dma16_sv(d.tb + q * 128, d.voff, d.lds0 + q * 4096); };
+  auto store_content = [&](int buf) {
+    LDS_AS uint8_t* dst = (LDS_AS uint8_t*)(smem + buf * CT_BYTES) + wave * 1024 + lane * 16;
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) *(LDS_AS u32x4_t*)(dst + q * 4096) = cst[q];
+  };
+  // the score steps that load a copy piece: every other step where the chain
+  // is long enough, else the first LOADS steps
+  auto copy_step = [](int i) -> bool { return NKS >= 2 * LOADS ? i % 2 == 1 && i / 2 < LOADS : i < LOADS; };
+  auto copy_piece = [](int i) -> int { return NKS >= 2 * LOADS ? i / 2 : i; };
+  // zero the content of never-written (or past-the-end) keys of tile t in
+  // buffer buf (their rotary scores are masked; their values must be 0)
+  auto zero_content = [&](int buf, int t) {
+    uint8_t* tile = smem + buf * CT_BYTES;
+    const int k0 = (t_begin + t) * MF_BN;
+    for (int e = tid; e < MF_BN * (DC / 64) * 8; e += 256) {
+      const int key = e / ((DC / 64) * 8), rest = e % ((DC / 64) * 8);
+      const int sl2 = k0 + key;
+      const bool ok = sl2 < cap && ring_frame(sl2 / P, newest, nm, W) >= 0;
+      if (!ok) {
+        const int cg = rest >> 3, pos = rest & 7;
+        *(uint4*)(tile + (cg * MF_BN + key) * 128 + pos * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+  };
+  // this wave's rotary key fragments of tile t (key lane & 31, 16 dims per
+  // score step), straight from the cache into registers; past-the-end keys
+  // read the last slot (their scores are masked)
+  bf16x8_t kr[NKR];
+  auto rope_src = [&](int t) -> const bf16_t* {
+    const int key = min((t_begin + t) * MF_BN + (lane & 31), cap - 1);
+    return cache_b + (size_t)key * DQK + DC + wave * (DR / 4) + g * 8;
+  };
   // value fragments of the tile in `vbuf` for this wave's output dims; the
   // probabilities' key order is the score accumulators' (a fixed
   // permutation), and the value fragments are read in the same order
@@ -183,7 +243,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   struct VFrag { i16x4_t v0[NDB], v1[NDB]; };
   auto read_values = [&](int vbuf, int j, VFrag& f) {
     const LDS_AS uint8_t* vt =
-        (const LDS_AS uint8_t*)(smem + vbuf * TILE_BYTES) + (WDIMS / 64) * wave * MF_BN * 128;
+        (const LDS_AS uint8_t*)(smem + vbuf * CT_BYTES) + (WDIMS / 64) * wave * MF_BN * 128;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
       const LDS_AS uint8_t* gbase = vt + (d >> 1) * MF_BN * 128 + (j * 16 + kq) * 128 + vhalf;
@@ -193,13 +253,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
           (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
     }
   };
-  // O^T[wave's dims][both row blocks] += V^T . P^T for key step j; the
-  // probabilities of block r, step j sit in chunk 0 of partial-score entry
-  // (r, j, lane)
-  auto output_mfma = [&](const VFrag& f, int j) {
-    bf16x8_t pfr[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) pfr[r] = *(const LDS_AS bf16x8_t*)sx_chunk(r, j, lane, 0);
+  // O^T[wave's dims][both row blocks] += V^T . P^T for key step j
+  auto output_mfma = [&](const VFrag& f, const bf16x8_t* pfr) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
       const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[d]);
@@ -215,6 +270,93 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   // the softmax lane's eight key positions in the tile (score elements 8 sj + i)
   auto skey = [&](int i) -> int { return 16 * sj + 8 * (i >> 2) + 4 * sg + (i & 3); };
 
+  // QK normalisation: the content part of a score is scaled by its key's
+  // inverse RMS.  The chain then takes its content steps first, multiplies
+  // the accumulators by the scales (the lane's sixteen keys 8k + 4g + i in
+  // the MFMA layout) and adds the rotary steps (content and rotary
+  // accumulators side by side do not fit the registers).  A tile's 32 scales reach
+  // LDS a step ahead, one 4-byte global-to-LDS load per lane of wave 1
+  // (lanes 32 .. 63 repeat lanes 0 .. 31), into one of two slots; the chain
+  // reads them from there just before the multiply (a global load in the
+  // step would make the chain wait for it, and registers are short).
+  float ksc[QKN ? 16 : 1];
+  auto ksc_copy = [&](int t, int slot) {
+    if (QKN && wave == 1) {
+      const int kt = (t_begin + t) * MF_BN;
+      dma4(a.kscale + (size_t)b * cap + min(kt + (lane & 31), cap - 1),
+           (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(ksl + slot * 256));
+    }
+  };
+  auto ksc_read = [&](int slot) {
+    if constexpr (QKN) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4_t v = *(const LDS_AS f32x4_t*)(ksl + slot * 256 + (8 * k + 4 * g) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ksc[4 * k + i] = v[i];
+      }
+    }
+  };
+
+  // Partial scores of both row blocks over this wave's quarters for the tile
+  // whose content sits in buffer kbuf and whose rotary fragments are in kr;
+  // kr is reloaded from `rnext` as it is consumed.  Rotary and content steps
+  // alternate (the register loads spread over the chain); with QK
+  // normalisation the content steps come first, then the rotary steps.
+  // stage(i) runs after score step i (copy pieces, softmax work).
+  f32x16_t s0, s1;
+  constexpr int NALT = QKN ? 0 : (NKR < NKC ? NKR : NKC);   // alternating pairs
+  auto score_chain = [&](int kbuf, int kslot, const bf16_t* rnext, auto&& stage) {
+    const int key = lane & 31;
+    const int sw = key_swizzle(key) ^ g;
+    const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(smem + kbuf * CT_BYTES + key * 128);
+    auto kaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
+      const int gks = wave * NKC + ks;
+      return (const LDS_AS bf16x8_t*)(krow + (gks >> 2) * MF_BN * 128 + ((((gks & 3) << 1) ^ sw) << 4));
+    };
+    constexpr int KPF = 4;
+    bf16x8_t kb[KPF];
+#pragma unroll
+    for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      const bool rot = i < 2 * NALT ? i % 2 == 0 : (QKN ? i >= NKC : NKR > NKC);
+      if (rot) {
+        const int kj = i < 2 * NALT ? i / 2 : i - (QKN ? NKC : NALT);
+        const bf16x8_t k = kr[kj];
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][NKC + kj], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][NKC + kj], s1, 0, 0, 0);
+        kr[kj] = *(const bf16x8_t*)(rnext + kj * 16);
+      } else {
+        const int ks = i < 2 * NALT ? i / 2 : i - NALT;
+        const bf16x8_t k = kb[ks % KPF];
+        if (ks + KPF < NKC) kb[ks % KPF] = *kaddr(ks + KPF);
+        if (QKN && ks == NKC - 2) ksc_read(kslot);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], s1, 0, 0, 0);
+        if (QKN && ks == NKC - 1) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            s0[e] *= ksc[e];
+            s1[e] *= ksc[e];
+          }
+        }
+      }
+      stage(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto write_partials = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      *(LDS_AS f32x4_t*)sx_chunk(0, wave, lane, k) = f32x4_t{s0[4 * k], s0[4 * k + 1], s0[4 * k + 2], s0[4 * k + 3]};
+      *(LDS_AS f32x4_t*)sx_chunk(1, wave, lane, k) = f32x4_t{s1[4 * k], s1[4 * k + 1], s1[4 * k + 2], s1[4 * k + 3]};
+    }
+  };
+
   for (int pass = 0;; ++pass) {
 #pragma unroll
   for (int d = 0; d < NDB * 2; ++d)
@@ -224,182 +366,167 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   m_run = pass == 0 ? -INFINITY : m_seen;
   bool overflow = false;
 
-  // QK normalisation: the key inverse RMS of this lane's eight keys of tile
-  // t, loaded one step before the tile is scored (into ksc_next), ahead of
-  // that step's tile copy; the wait at the top of the next step (a
-  // compiler-visible s_waitcnt) covers them, so neither the copy into ksc nor
-  // the use waits for a tile copy in flight.  (ksc_next is not loaded before
-  // the loop: a value from outside the loop would be merged with the loop's
-  // by a register copy, which waits for the load.)
-  float ksc[QKN ? 8 : 1], ksc_next[QKN ? 8 : 1];
-  auto load_ksc = [&](int t, float* dst) {
-    if constexpr (QKN) {
-      const float* kr = a.kscale + (size_t)b * cap;
-      const int kt = (t_begin + t) * MF_BN;
-      if ((cap & 3) == 0 && kt + MF_BN <= cap) {
+  int ta = next_tile(0);
+  if (ta < ntl) {
+    // ---- prologue: the first tile's content, rotary fragments and scores;
+    // the second tile's copy issued between its MFMAs ----
+    int tb = next_tile(ta + 1);
+    int ba = 0, bb = 1, bn = 2;   // content buffers of t_s, t_s+1 and t_s+2
+    int kslot = 1;                // key-scale slot of t_s+1
+    {
+      const uint8_t* cs = content_src(ta);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4_t v = *(const f32x4_t*)(kr + kt + skey(4 * h));
-          dst[4 * h] = v[0]; dst[4 * h + 1] = v[1]; dst[4 * h + 2] = v[2]; dst[4 * h + 3] = v[3];
-        }
-      } else {
+      for (int q = 0; q < LOADS; ++q) cst[q] = *(const u32x4_t*)(cs + q * 128);
+      const bf16_t* rs = rope_src(ta);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = kr[min(kt + skey(i), cap - 1)];
-      }
+      for (int i = 0; i < NKR; ++i) kr[i] = *(const bf16x8_t*)(rs + i * 16);
+      ksc_copy(ta, 0);
     }
-  };
-  int cur = next_tile(0), bc = 0;
-  bool first_step = true;
-  if (cur < ntl) {
-    const DmaPlan d0 = dma_plan(cur, 0);
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q) dma_piece(d0, q);
-  }
-  while (cur < ntl) {
-    const int nxt = next_tile(cur + 1);
     // vmcnt(0) lgkmcnt(0), as the builtin: the compiler counts it as done
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070);
     asm volatile("" ::: "memory");
-    // barrier 1: this tile is in LDS; every wave is done with the previous
-    // tile (its buffer takes the next one; the probability area is free)
+    store_content(ba);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     lds_barrier();
-    uint8_t* tile = smem + bc * TILE_BYTES;
-    const int k0 = (t_begin + cur) * MF_BN;
-    const int cl = all_full ? (int)TILE_FULL : tile_class(cur);
-    const bool do_dma = nxt < ntl;
-    const DmaPlan dp = dma_plan(do_dma ? nxt : cur, bc ^ 1);
-    if constexpr (QKN) {
-      // (this tile's values arrived before the wait above; the first tile of
-      // a pass loads its own here, and its use waits for this step's copy)
-      if (first_step) {
-        load_ksc(cur, ksc);
-        // wait for them here, before this step's tile copy is issued
-#pragma unroll
-        for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(ksc[i]));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ksc[i] = ksc_next[i];
-      }
-      load_ksc(do_dma ? nxt : cur, ksc_next);   // (unconditional: no merge copy that would wait for it)
+    int cla = class_of(ta);
+    if (cla == TILE_MASKED_ZERO) zero_content(ba, ta);
+    {
+      const bool have_b = tb < ntl;
+      ksc_copy(have_b ? tb : ta, 1);
+      const uint8_t* cs = content_src(have_b ? tb : ta);
+      score_chain(ba, 0, rope_src(have_b ? tb : ta), [&](int i) {
+        if (copy_step(i)) cst[copy_piece(i)] = *(const u32x4_t*)(cs + copy_piece(i) * 128);
+      });
+      write_partials();
     }
-    first_step = false;
-    if (cl == TILE_MASKED_ZERO) {
-      // zero never-written (or past-the-end) keys of this tile
-      for (int e = tid; e < MF_BN * NCG * 8; e += 256) {
-        const int key = e / (NCG * 8), rest = e % (NCG * 8);
-        const int sl = k0 + key;
-        const bool ok = sl < cap && ring_frame(sl / P, newest, nm, W) >= 0;
-        if (!ok) {
-          const int cg = rest >> 3, pos = rest & 7;
-          *(uint4*)(tile + (cg * MF_BN + key) * 128 + pos * 16) = make_uint4(0, 0, 0, 0);
-        }
-      }
+
+    for (;;) {
+      // ---- top of step: t_s+1's content and rotary fragments have landed
+      // in registers, this wave's partial scores of t_s are written; the
+      // content goes to its buffer (free since barrier B of the last step) ----
+      const bool have_b = tb < ntl;
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      asm volatile("" ::: "memory");
+      if (have_b) store_content(bb);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // barrier A: every partial score of t_s and t_s+1's content are in
+      // LDS; every wave is done with the probabilities
       lds_barrier();
-    }
+      const int tc = have_b ? next_tile(tb + 1) : ntl;
+      const bool have_c = tc < ntl;
+      ksc_copy(have_c ? tc : ta, kslot ^ 1);
+      // L2 prefetch of the tile DS_PF_AHEAD steps ahead: wave 0 loads one
+      // 16-byte piece of each of 64 of its 128-byte lines (a global-to-LDS
+      // load into a landing area nothing reads), slice (work-group / 8) of
+      // the tile's lines, so that the work-groups of an XCD, which walk the
+      // same tiles together, bring each tile into L2 before any of them
+      // needs it (one step's loads would otherwise wait on the fetch from
+      // beyond L2 together).  The wait at the top of the next step covers it.
+      if (wave == 0) {
+        constexpr int LPK = DQK / 64, TL = MF_BN * LPK, NSL = (TL + 63) / 64;   // lines per key, per tile
+        const int kp0 = (t_begin + min(ta + DS_PF_AHEAD, ntl - 1)) * MF_BN;
+        const int ln = min(64 * (int)((blockIdx.x >> 3) % NSL) + lane, TL - 1);
+        const int kk = min(ln / LPK, cap - 1 - kp0);
+        dma16((const uint8_t*)(cache_b + (size_t)(kp0 + kk) * DQK) + (ln % LPK) * 128,
+              (uint32_t)(uintptr_t)(LDS_AS uint8_t*)pf_sink);
+      }
+      const int clb = have_b ? class_of(tb) : (int)TILE_FULL;
+      if (clb == TILE_MASKED_ZERO) zero_content(bb, tb);
+      const int k0a = (t_begin + ta) * MF_BN;
+      const uint8_t* cs = content_src(have_c ? tc : ta);
 
-    // ---- partial scores of both row blocks over this wave's quarter; the
-    // next tile's copy issued between the MFMAs ----
-    f32x16_t s0, s1;
+      // ---- phase 1: scores of t_s+1 (a discarded repeat of t_s's content
+      // when there is none), the softmax of t_s between them ----
+      f32x4_t pr[8];
+      float sv[8];
+      float mloc = 0.f, neg_m = 0.f;
+      bf16x8_t pf;
+      VFrag vf0, vf1;
+      score_chain(have_b ? bb : ba, kslot, rope_src(have_c ? tc : ta), [&](int i) {
+        if (copy_step(i) && have_c) cst[copy_piece(i)] = *(const u32x4_t*)(cs + copy_piece(i) * 128);
+        if (i == 0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
-    {
-      const int key = lane & 31;
-      const int sw = key_swizzle(key) ^ g;
-      const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(tile + key * 128);
-      auto kaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
-        const int gks = wave * NKSW + ks;
-        return (const LDS_AS bf16x8_t*)(krow + (gks >> 2) * MF_BN * 128 + ((((gks & 3) << 1) ^ sw) << 4));
-      };
-      constexpr int KPF = 4;
-      bf16x8_t kb[KPF];
+          for (int q = 0; q < 4; ++q) {
+            pr[2 * q] = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj);
+            pr[2 * q + 1] = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj + 1);
+          }
+        } else if (i == 2) {
 #pragma unroll
-      for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i < NKSW ? i : 0);
+          for (int e = 0; e < 4; ++e) {
+            sv[e] = ((pr[0][e] + pr[2][e]) + pr[4][e]) + pr[6][e];
+            sv[4 + e] = ((pr[1][e] + pr[3][e]) + pr[5][e]) + pr[7][e];
+          }
+          if (cla != TILE_FULL) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int sl2 = k0a + skey(e);
+              bool vis = sl2 < cap;
+              if (vis) vis = key_visible(fq, ring_frame(sl2 / P, newest, nm, W), W, fpb);
+              if (!vis) sv[e] = -INFINITY;
+            }
+          }
+          mloc = sv[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
+        } else if (i == 3) {
+          // over the row's four lanes (lane ^ 16, lane ^ 32)
+          const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+          mloc = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+          mloc = halves_max(mloc) * c_l2;
+        } else if (i == 4) {
+          m_seen = fmaxf(m_seen, mloc);
+          if (m_run == -INFINITY) m_run = mloc;                   // first visible tile of the row
+          else if (mloc > m_run + ma.rerun_log2) overflow = true; // rerun with the final maxima
+          neg_m = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], c_l2, neg_m));
+            l_run += p;
+            pf[e] = (__bf16)p;
+          }
+        } else if (i == 5) {
+#pragma unroll
+          for (int e = 4; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], c_l2, neg_m));
+            l_run += p;
+            pf[e] = (__bf16)p;
+          }
+          *(LDS_AS bf16x8_t*)p_entry(sb, sj, sl) = pf;
+        }
+        // t_s's value fragments, read while the last score steps run
+        if (i == (NKS - 6 > 6 ? NKS - 6 : 6)) read_values(ba, 0, vf0);
+        if (i == (NKS - 3 > 7 ? NKS - 3 : 7)) read_values(ba, 1, vf1);
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // barrier B: every row's probabilities of t_s are published; every
+      // partial score of t_s has been read
+      lds_barrier();
+
+      // ---- phase 2: t_s+1's partial scores to LDS, t_s's output product ----
+      bf16x8_t pfr0[2], pfr1[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) pfr0[r] = *(const LDS_AS bf16x8_t*)p_entry(r, 0, lane);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) pfr1[r] = *(const LDS_AS bf16x8_t*)p_entry(r, 1, lane);
+      output_mfma(vf0, pfr0);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < NKSW; ++ks) {
-        const bf16x8_t cur_k = kb[ks % KPF];
-        if (ks + KPF < NKSW) kb[ks % KPF] = *kaddr(ks + KPF);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, qf[0][ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_k, qf[1][ks], s1, 0, 0, 0);
-        if (ks < LOADS && do_dma) dma_piece(dp, ks);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      // (after the first key step's MFMAs: its probability reads are not
+      // queued behind these writes)
+      if (have_b) write_partials();
+      __builtin_amdgcn_sched_barrier(0);
+      output_mfma(vf1, pfr1);
+      if (!have_b) break;
+      ta = tb;
+      tb = tc;
+      cla = clb;
+      const int bt = ba;
+      ba = bb;
+      bb = bn;
+      bn = bt;
+      kslot ^= 1;
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      *(LDS_AS f32x4_t*)sx_chunk(0, wave, lane, k) = f32x4_t{s0[4 * k], s0[4 * k + 1], s0[4 * k + 2], s0[4 * k + 3]};
-      *(LDS_AS f32x4_t*)sx_chunk(1, wave, lane, k) = f32x4_t{s1[4 * k], s1[4 * k + 1], s1[4 * k + 2], s1[4 * k + 3]};
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // barrier 2: every quarter's partial scores are in LDS
-    lds_barrier();
-
-    // ---- softmax of this lane's row and eight keys ----
-    float sv[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4_t lo = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj);
-      const f32x4_t hi = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj + 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = q == 0 ? lo[i] : sv[i] + lo[i];
-        sv[4 + i] = q == 0 ? hi[i] : sv[4 + i] + hi[i];
-      }
-      if constexpr (QKN) {
-        if (q == 1)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sv[i] *= ksc[i];
-      }
-    }
-    // the value fragments of this tile's first key step, read while the
-    // softmax runs
-    VFrag vf0;
-    read_values(bc, 0, vf0);
-    if (cl != TILE_FULL) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int sl2 = k0 + skey(i);
-        bool vis = sl2 < cap;
-        if (vis) vis = key_visible(fq, ring_frame(sl2 / P, newest, nm, W), W, fpb);
-        if (!vis) sv[i] = -INFINITY;
-      }
-    }
-    float mloc = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, sv[i]);
-    {
-      // over the row's four lanes (lane ^ 16, lane ^ 32)
-      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-      mloc = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-      mloc = halves_max(mloc) * c_l2;
-    }
-    m_seen = fmaxf(m_seen, mloc);
-    if (m_run == -INFINITY) m_run = mloc;                   // first visible tile of the row
-    else if (mloc > m_run + ma.rerun_log2) overflow = true; // rerun with the final maxima
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    bf16x8_t pf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sv[i], c_l2, neg_m));
-      l_run += p;
-      pf[i] = (__bf16)p;
-    }
-    // (chunk 0 of entry (sb, sj, sl): this wave read it above; every lane
-    // that reads this entry's chunks belongs to this wave and has read them)
-    *(LDS_AS bf16x8_t*)sx_chunk(sb, sj, sl, 0) = pf;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // barrier 3: every row's probabilities of this tile are published
-    lds_barrier();
-
-    // ---- this tile's output product ----
-    VFrag vf1;
-    read_values(bc, 1, vf1);
-    output_mfma(vf0, 0);
-    output_mfma(vf1, 1);
-    bc ^= 1;
-    cur = nxt;
   }
   if (!block_any(overflow)) break;
   }
@@ -424,7 +551,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   // normalised bf16 rows staged in LDS ([row][DC], 16-byte chunks XOR-swizzled
   // by row & 7, in the free tile buffers), then each wave writes 16 rows, one
   // 1 KB row per instruction (the final output or this split's partial)
-  static_assert(DC == 512 && 2 * TILE_BYTES >= DS_ROWS * DC * 2, "output staging");
+  static_assert(DC == 512 && 3 * CT_BYTES >= DS_ROWS * DC * 2, "output staging");
   LDS_AS uint8_t* ost = (LDS_AS uint8_t*)smem;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
