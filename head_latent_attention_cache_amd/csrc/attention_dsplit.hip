@@ -190,19 +190,30 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   // 8w + 7, 16 bytes per lane, chunk c of a key read from c ^ its swizzle),
   // loaded into `cst` during one step and written at the top of the next;
   // past-the-end keys of the last tile read the last slot (zeroed later).
-  // (Ordinary loads here: global-to-LDS DMA loads issued next to the rotary
-  // register loads cost this kernel several times what either costs alone.)
+  // With QK normalisation the pieces go straight to LDS instead
+  // (global_load_lds_dwordx4, the same speed here): the registers they free
+  // hold the chain's separate content accumulators.
+  constexpr bool CDMA = QKN;
   const int cp_key = (wave << 3) + (lane >> 3);
-  u32x4_t cst[LOADS];
+  u32x4_t cst[CDMA ? 1 : LOADS];
   auto content_src = [&](int t) -> const uint8_t* {
     const int k0 = (t_begin + t) * MF_BN;
     const int key = min(cp_key, cap - 1 - k0);
     return (const uint8_t*)(cache_b + ((size_t)k0 + key) * DQK) + (((lane & 7) ^ key_swizzle(cp_key)) << 4);
   };
   auto store_content = [&](int buf) {
-    LDS_AS uint8_t* dst = (LDS_AS uint8_t*)(smem + buf * CT_BYTES) + wave * 1024 + lane * 16;
+    if constexpr (!CDMA) {
+      LDS_AS uint8_t* dst = (LDS_AS uint8_t*)(smem + buf * CT_BYTES) + wave * 1024 + lane * 16;
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) *(LDS_AS u32x4_t*)(dst + q * 4096) = cst[q];
+      for (int q = 0; q < LOADS; ++q) *(LDS_AS u32x4_t*)(dst + q * 4096) = cst[q];
+    }
+  };
+  // piece q of the content at `cs` (content_src) toward buffer buf
+  auto copy_load = [&](const uint8_t* cs, int q, int buf) {
+    if constexpr (CDMA)
+      dma16(cs + q * 128, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * CT_BYTES) + wave * 1024 + q * 4096);
+    else
+      cst[q] = *(const u32x4_t*)(cs + q * 128);
   };
   // the score steps that load a copy piece: every other step where the chain
   // is long enough, else the first LOADS steps
@@ -271,13 +282,12 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   auto skey = [&](int i) -> int { return 16 * sj + 8 * (i >> 2) + 4 * sg + (i & 3); };
 
   // QK normalisation: the content part of a score is scaled by its key's
-  // inverse RMS.  The chain then takes its content steps first, multiplies
-  // the accumulators by the scales (the lane's sixteen keys 8k + 4g + i in
-  // the MFMA layout) and adds the rotary steps (content and rotary
-  // accumulators side by side do not fit the registers).  A tile's 32 scales reach
+  // inverse RMS.  The chain then keeps content and rotary accumulators and
+  // combines them at its end, s = c * scale + r (the scales of the lane's
+  // sixteen keys 8k + 4g + i in the MFMA layout).  A tile's 32 scales reach
   // LDS a step ahead, one 4-byte global-to-LDS load per lane of wave 1
   // (lanes 32 .. 63 repeat lanes 0 .. 31), into one of two slots; the chain
-  // reads them from there just before the multiply (a global load in the
+  // reads them from there just before the combination (a global load in the
   // step would make the chain wait for it, and registers are short).
   float ksc[QKN ? 16 : 1];
   auto ksc_copy = [&](int t, int slot) {
@@ -301,11 +311,10 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   // Partial scores of both row blocks over this wave's quarters for the tile
   // whose content sits in buffer kbuf and whose rotary fragments are in kr;
   // kr is reloaded from `rnext` as it is consumed.  Rotary and content steps
-  // alternate (the register loads spread over the chain); with QK
-  // normalisation the content steps come first, then the rotary steps.
+  // alternate (the register loads spread over the chain).
   // stage(i) runs after score step i (copy pieces, softmax work).
   f32x16_t s0, s1;
-  constexpr int NALT = QKN ? 0 : (NKR < NKC ? NKR : NKC);   // alternating pairs
+  constexpr int NALT = NKR < NKC ? NKR : NKC;   // alternating pairs
   auto score_chain = [&](int kbuf, int kslot, const bf16_t* rnext, auto&& stage) {
     const int key = lane & 31;
     const int sw = key_swizzle(key) ^ g;
@@ -318,14 +327,19 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     bf16x8_t kb[KPF];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
+    f32x16_t c0, c1;   // content parts (QK normalisation)
 #pragma unroll
     for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
+    if constexpr (QKN) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NKS; ++i) {
-      const bool rot = i < 2 * NALT ? i % 2 == 0 : (QKN ? i >= NKC : NKR > NKC);
+      const bool rot = i < 2 * NALT ? i % 2 == 0 : NKR > NKC;
       if (rot) {
-        const int kj = i < 2 * NALT ? i / 2 : i - (QKN ? NKC : NALT);
+        const int kj = i < 2 * NALT ? i / 2 : i - NALT;
         const bf16x8_t k = kr[kj];
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][NKC + kj], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][NKC + kj], s1, 0, 0, 0);
@@ -334,19 +348,24 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         const int ks = i < 2 * NALT ? i / 2 : i - NALT;
         const bf16x8_t k = kb[ks % KPF];
         if (ks + KPF < NKC) kb[ks % KPF] = *kaddr(ks + KPF);
-        if (QKN && ks == NKC - 2) ksc_read(kslot);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], s1, 0, 0, 0);
-        if (QKN && ks == NKC - 1) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            s0[e] *= ksc[e];
-            s1[e] *= ksc[e];
-          }
+        if constexpr (QKN) {
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], c1, 0, 0, 0);
+        } else {
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], s1, 0, 0, 0);
         }
       }
+      if (QKN && i == NKS - 2) ksc_read(kslot);
       stage(i);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (QKN) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s0[e] = fmaf(c0[e], ksc[e], s0[e]);
+        s1[e] = fmaf(c1[e], ksc[e], s1[e]);
+      }
     }
   };
   auto write_partials = [&]() {
@@ -376,7 +395,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     {
       const uint8_t* cs = content_src(ta);
 #pragma unroll
-      for (int q = 0; q < LOADS; ++q) cst[q] = *(const u32x4_t*)(cs + q * 128);
+      for (int q = 0; q < LOADS; ++q) copy_load(cs, q, ba);
       const bf16_t* rs = rope_src(ta);
 #pragma unroll
       for (int i = 0; i < NKR; ++i) kr[i] = *(const bf16x8_t*)(rs + i * 16);
@@ -396,7 +415,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       ksc_copy(have_b ? tb : ta, 1);
       const uint8_t* cs = content_src(have_b ? tb : ta);
       score_chain(ba, 0, rope_src(have_b ? tb : ta), [&](int i) {
-        if (copy_step(i)) cst[copy_piece(i)] = *(const u32x4_t*)(cs + copy_piece(i) * 128);
+        if (copy_step(i)) copy_load(cs, copy_piece(i), bb);
       });
       write_partials();
     }
@@ -445,7 +464,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       bf16x8_t pf;
       VFrag vf0, vf1;
       score_chain(have_b ? bb : ba, kslot, rope_src(have_c ? tc : ta), [&](int i) {
-        if (copy_step(i) && have_c) cst[copy_piece(i)] = *(const u32x4_t*)(cs + copy_piece(i) * 128);
+        if (copy_step(i) && have_c) copy_load(cs, copy_piece(i), bn);
         if (i == 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
