@@ -72,6 +72,9 @@ def run_qkn(cfg, inp, g_q, g_k, fill=None):
 # kernel's 16-byte reads of the key statistic, with a ragged last tile)
 QKN_CASES = {key: SMALL_CONFIGS[key] for key in (2, 3, 5, 6, 1, 4)}
 QKN_CASES["4x5"] = SMALL_CONFIGS[4].replace(name="long_video_small_4x5", grid_h=4, grid_w=5)
+# the long video with 4 of 6 ring frames written, the other slots (and their
+# key statistics) NaN bit patterns: masked tiles of the wide-row kernel
+QKN_CASES["4_partial"] = SMALL_CONFIGS[4].replace(name="long_video_small_partial", n_frames=4, q_first=1)
 
 
 @pytest.mark.parametrize("key", list(QKN_CASES))
@@ -84,7 +87,7 @@ def test_qk_norm_matches_oracle(gpu_lib, key):
     _case(f"qk norm {cfg.name}")
     inp = make_workload(cfg, seed=41)
     g_q, g_k = _weights(cfg, 42)
-    got = run_qkn(cfg, inp, g_q, g_k, fill=0xFF if cfg.cache_given else None)
+    got = run_qkn(cfg, inp, g_q, g_k, fill=0xFF if cfg.cache_given or key == "4_partial" else None)
     st = om.build_cache(cfg, inp)
     w_uk, w_uv = om.as_f64(inp["w_uk"]), om.as_f64(inp["w_uv"])
     q_nope = om.as_f64(inp["q_nope"])

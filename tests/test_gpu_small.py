@@ -52,9 +52,14 @@ def test_small_workload_end_to_end(gpu_lib, key):
     print({k: (f"{a:.2e}", f"{b:.2e}") for k, (a, b) in rep.items()}, flush=True)
 
 
-def test_partially_filled_ring_with_poisoned_slots(gpu_lib):
-    # 2 of 4 ring frames written; the rest hold NaN bit patterns
-    cfg = SMALL_CONFIGS[3].replace(name="ring_partial", n_frames=2, q_first=1)
+@pytest.mark.parametrize("key", [3, 4])
+def test_partially_filled_ring_with_poisoned_slots(gpu_lib, key):
+    # video chunk: 2 of 4 ring frames written; long video (wide-row kernel,
+    # whose rotary keys go straight from the cache into registers): 4 of 6;
+    # the rest hold NaN bit patterns
+    base = SMALL_CONFIGS[key]
+    cfg = base.replace(name=f"ring_partial_{base.name}", n_frames=base.q_frames + 1, q_first=1)
+    assert om.slot_frames(cfg, cfg.newest).min() < 0
     _case(cfg.name)
     inp = make_workload(cfg, seed=1)
     got = gp.run_gpu(cfg, inp, fill=0xFF, keep_device=True)
