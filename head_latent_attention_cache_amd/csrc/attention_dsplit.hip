@@ -219,6 +219,12 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   // is long enough, else the first LOADS steps
   auto copy_step = [](int i) -> bool { return NKS >= 2 * LOADS ? i % 2 == 1 && i / 2 < LOADS : i < LOADS; };
   auto copy_piece = [](int i) -> int { return NKS >= 2 * LOADS ? i / 2 : i; };
+  // in the key loop the first LP1 pieces go between the score MFMAs (one
+  // every four steps) and the rest between the output MFMAs, so that the
+  // vector-memory instructions spread over the whole step
+  constexpr int LP1 = NKS >= 2 * LOADS ? LOADS / 2 : LOADS;
+  auto loop_copy_step = [](int i) -> bool { return LP1 < LOADS ? i % 4 == 1 && i / 4 < LP1 : i < LOADS; };
+  auto loop_copy_piece = [](int i) -> int { return LP1 < LOADS ? i / 4 : i; };
   // zero the content of never-written (or past-the-end) keys of tile t in
   // buffer buf (their rotary scores are masked; their values must be 0)
   auto zero_content = [&](int buf, int t) {
@@ -263,6 +269,14 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       f.v1[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
     }
+  };
+  // one of its MFMAs: output-dim block d, row block r
+  auto output_one = [&](const VFrag& f, const bf16x8_t* pfr, int d, int r) {
+    const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[d]);
+    bf16x8_t vf;
+    vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
+    vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
+    o[d * 2 + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[r], o[d * 2 + r], 0, 0, 0);
   };
   // O^T[wave's dims][both row blocks] += V^T . P^T for key step j
   auto output_mfma = [&](const VFrag& f, const bf16x8_t* pfr) {
@@ -464,7 +478,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       bf16x8_t pf;
       VFrag vf0, vf1;
       score_chain(have_b ? bb : ba, kslot, rope_src(have_c ? tc : ta), [&](int i) {
-        if (copy_step(i) && have_c) copy_load(cs, copy_piece(i), bn);
+        if (loop_copy_step(i) && have_c) copy_load(cs, loop_copy_piece(i), bn);
         if (i == 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -529,13 +543,15 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       for (int r = 0; r < 2; ++r) pfr0[r] = *(const LDS_AS bf16x8_t*)p_entry(r, 0, lane);
 #pragma unroll
       for (int r = 0; r < 2; ++r) pfr1[r] = *(const LDS_AS bf16x8_t*)p_entry(r, 1, lane);
-      output_mfma(vf0, pfr0);
-      __builtin_amdgcn_sched_barrier(0);
-      // (after the first key step's MFMAs: its probability reads are not
-      // queued behind these writes)
-      if (have_b) write_partials();
-      __builtin_amdgcn_sched_barrier(0);
-      output_mfma(vf1, pfr1);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        output_one(m < 8 ? vf0 : vf1, m < 8 ? pfr0 : pfr1, (m & 7) >> 1, m & 1);
+        if (LP1 < LOADS && m % 4 == 1 && have_c) copy_load(cs, LP1 + m / 4, bn);
+        // (after the first key step's MFMAs: its probability reads are not
+        // queued behind these writes)
+        if (m == 7 && have_b) write_partials();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (!have_b) break;
       ta = tb;
       tb = tc;
