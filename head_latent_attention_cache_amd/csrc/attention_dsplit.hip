@@ -17,21 +17,20 @@
 // as keys by the scores and, transposed, as values by the output product);
 // each wave loads its rotary quarter of the tile's keys straight into the
 // registers the score MFMAs take (no LDS bytes for it), one tile ahead.  The
-// content is loaded into registers one step ahead as well and written to its
-// LDS buffer at the top of the step that scores it.  Three content buffers
-// (96 KB), the partial scores (32 KB) and the probabilities (4 KB) take
-// 132 KB of LDS.  Step s of the key loop, with tiles t_s (attended now),
-// t_s+1 (scored now) and t_s+2 (loaded now):
-//  * top: every load of the previous step has landed; t_s+1's content goes
-//    to LDS; barrier A (the partial scores of t_s and t_s+1's content are in
-//    LDS).  Wave 0 starts the L2 prefetch of a slice of the tile eight steps
-//    ahead.
+// content is copied into its LDS buffer one step ahead as well, by
+// global-to-LDS loads.  Three content buffers (96 KB), the partial scores
+// (32 KB) and the probabilities (4 KB) take 132 KB of LDS.  Step s of the
+// key loop, with tiles t_s (attended now), t_s+1 (scored now) and t_s+2
+// (loaded now):
+//  * top: every load of the previous step has landed; barrier A (the partial
+//    scores of t_s and t_s+1's content are in LDS).  Wave 0 starts the L2
+//    prefetch of a slice of the tile eight steps ahead.
 //  * phase 1: the partial scores of t_s+1 for both row blocks,
 //    S^T_w = K_w . Q_w^T with v_mfma_f32_32x32x16_bf16 (each key fragment
 //    feeds two MFMAs: two independent accumulation chains), rotary steps from
 //    registers (each register set reloaded with t_s+2 right after its
-//    MFMAs) alternating with content steps from LDS, and t_s+2's content
-//    loads between them; and, spread between the same MFMAs, the softmax of
+//    MFMAs) alternating with content steps from LDS, and half of t_s+2's
+//    content copy between them; and, spread between the same MFMAs, the softmax of
 //    t_s: wave w takes rows 16 w .. 16 w + 15, four lanes per row and eight
 //    keys per lane, adds the four quarters' partials in a fixed order
 //    (deterministic), masks, takes the row maximum over the row's four lanes
@@ -43,7 +42,8 @@
 //  * phase 2: O^T (d_c x 64 rows) += V^T . P^T for t_s (wave w owns d_c / 4
 //    output dims of both row blocks, value fragments read with
 //    ds_read_b64_tr_b16 from t_s's content buffer during phase 1), with the
-//    partial scores of t_s+1 written to LDS between its two key steps.
+//    other half of t_s+2's content copy between its MFMAs and the partial
+//    scores of t_s+1 written to LDS between its two key steps.
 // What bounds it: the vector-memory side.  64 KB of cache rows per 64 rows
 // and 32 keys is 2.5 times the bytes per MFMA of the narrow kernel (128
 // rows per 1152-byte row); a step with every load removed runs in 60 % of
@@ -185,35 +185,22 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     return i;
   };
   auto class_of = [&](int i) -> int { return all_full ? (int)TILE_FULL : tile_class(i); };
-  // Copy of a tile's content into LDS through registers: piece q of wave w
-  // is 1 KB block (q * 4 + w) of the LDS tile (64-dim group q, keys 8w ..
-  // 8w + 7, 16 bytes per lane, chunk c of a key read from c ^ its swizzle),
-  // loaded into `cst` during one step and written at the top of the next;
-  // past-the-end keys of the last tile read the last slot (zeroed later).
-  // With QK normalisation the pieces go straight to LDS instead
-  // (global_load_lds_dwordx4, the same speed here): the registers they free
-  // hold the chain's separate content accumulators.
-  constexpr bool CDMA = QKN;
+  // Copy of a tile's content into LDS: piece q of wave w is 1 KB block
+  // (q * 4 + w) of the LDS tile (64-dim group q, keys 8w .. 8w + 7, 16 bytes
+  // per lane, chunk c of a key read from c ^ its swizzle), one
+  // global_load_lds_dwordx4 per piece; past-the-end keys of the last tile
+  // read the last slot (zeroed later).  (Staged through registers and
+  // written at the top of the step instead, the copy's LDS writes sat in
+  // front of the step's barrier: 4 % slower.)
   const int cp_key = (wave << 3) + (lane >> 3);
-  u32x4_t cst[CDMA ? 1 : LOADS];
   auto content_src = [&](int t) -> const uint8_t* {
     const int k0 = (t_begin + t) * MF_BN;
     const int key = min(cp_key, cap - 1 - k0);
     return (const uint8_t*)(cache_b + ((size_t)k0 + key) * DQK) + (((lane & 7) ^ key_swizzle(cp_key)) << 4);
   };
-  auto store_content = [&](int buf) {
-    if constexpr (!CDMA) {
-      LDS_AS uint8_t* dst = (LDS_AS uint8_t*)(smem + buf * CT_BYTES) + wave * 1024 + lane * 16;
-#pragma unroll
-      for (int q = 0; q < LOADS; ++q) *(LDS_AS u32x4_t*)(dst + q * 4096) = cst[q];
-    }
-  };
-  // piece q of the content at `cs` (content_src) toward buffer buf
+  // piece q of the content at `cs` (content_src) into buffer buf
   auto copy_load = [&](const uint8_t* cs, int q, int buf) {
-    if constexpr (CDMA)
-      dma16(cs + q * 128, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * CT_BYTES) + wave * 1024 + q * 4096);
-    else
-      cst[q] = *(const u32x4_t*)(cs + q * 128);
+    dma16(cs + q * 128, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + buf * CT_BYTES) + wave * 1024 + q * 4096);
   };
   // the score steps that load a copy piece: every other step where the chain
   // is long enough, else the first LOADS steps
@@ -419,8 +406,6 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070);
     asm volatile("" ::: "memory");
-    store_content(ba);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     lds_barrier();
     int cla = class_of(ta);
     if (cla == TILE_MASKED_ZERO) zero_content(ba, ta);
@@ -435,15 +420,13 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     }
 
     for (;;) {
-      // ---- top of step: t_s+1's content and rotary fragments have landed
-      // in registers, this wave's partial scores of t_s are written; the
-      // content goes to its buffer (free since barrier B of the last step) ----
+      // ---- top of step: t_s+1's content (in LDS) and rotary fragments (in
+      // registers) have landed, this wave's partial scores of t_s are
+      // written ----
       const bool have_b = tb < ntl;
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0x0070);
       asm volatile("" ::: "memory");
-      if (have_b) store_content(bb);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       // barrier A: every partial score of t_s and t_s+1's content are in
       // LDS; every wave is done with the probabilities
       lds_barrier();
