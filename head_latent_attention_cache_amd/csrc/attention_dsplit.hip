@@ -531,8 +531,13 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         output_one(m < 8 ? vf0 : vf1, m < 8 ? pfr0 : pfr1, (m & 7) >> 1, m & 1);
         if (LP1 < LOADS && m % 4 == 1 && have_c) copy_load(cs, LP1 + m / 4, bn);
         // (after the first key step's MFMAs: its probability reads are not
-        // queued behind these writes)
-        if (m == 7 && have_b) write_partials();
+        // queued behind these writes; unconditional in the plain instance, so
+        // the compiler can count them: a branch around them turned the wait
+        // for the second key step's probabilities into lgkmcnt(0), behind all
+        // eight writes.  After the last tile they write a discarded repeat
+        // nobody reads.  With QK normalisation the register allocation of the
+        // unconditional form spills inside the loop.)
+        if (m == 7 && (!QKN || have_b)) write_partials();
         __builtin_amdgcn_sched_barrier(0);
       }
       if (!have_b) break;
