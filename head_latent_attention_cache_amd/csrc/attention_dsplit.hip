@@ -536,8 +536,9 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         // for the second key step's probabilities into lgkmcnt(0), behind all
         // eight writes.  After the last tile they write a discarded repeat
         // nobody reads.  With QK normalisation the register allocation of the
-        // unconditional form spills inside the loop.)
-        if (m == 7 && (!QKN || have_b)) write_partials();
+        // unconditional form spills inside the loop, so there they follow the
+        // last MFMA, where no read waits behind them.)
+        if (QKN ? m == 15 && have_b : m == 7) write_partials();
         __builtin_amdgcn_sched_barrier(0);
       }
       if (!have_b) break;
