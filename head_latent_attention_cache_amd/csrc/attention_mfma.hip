@@ -596,22 +596,6 @@ void attn_mfma_kernel(MfmaArgs ma) {
       // one barrier per tile: this tile is in LDS, the previous tile's
       // probabilities are published, and the buffer two tiles back is free
       lds_barrier();
-      // L2 prefetch of the tile 8 steps ahead where a sequence has several
-      // row blocks (their work-groups walk the same key tiles together):
-      // wave 0 loads one dword of each of 64 of the tile's 128-byte lines,
-      // slice (work-group / 8) of them, into the row-sum area (used only
-      // after the key loop, which waits for these loads first); the wait at
-      // the top of the next step covers it.  (Chunk workloads 2 % faster;
-      // decode, one row block per sequence, streams its own keys and was
-      // slower with it.)
-      if (ma.n_rb > 1 && wave == 0) {
-        constexpr int LPK = DQK / 64, TL = MF_BN * LPK, NSL = (TL + 63) / 64;   // lines per key, per tile
-        const int kp0 = (t_begin + min(cur + 8, ntl - 1)) * MF_BN;
-        const int ln = min(64 * (int)((blockIdx.x >> 3) % NSL) + lane, TL - 1);
-        const int kk = min(ln / LPK, cap - 1 - kp0);
-        dma4((const uint8_t*)(cache_b + (size_t)(kp0 + kk) * DQK) + (ln % LPK) * 128,
-             (uint32_t)(uintptr_t)(LDS_AS float*)lrow);
-      }
       // buffer of the next tile: the one holding neither this tile nor the previous one
       const int bnext = bprev < 0 ? (bcur + 1) % MF_NBUF : 3 - bcur - bprev;
       const DmaPlan dp = dma_plan(nxt < ntl ? nxt : cur, bnext);
@@ -645,8 +629,6 @@ void attn_mfma_kernel(MfmaArgs ma) {
       lds_barrier();
       output_product(bprev, pb ^ 1);
     }
-    // the last L2 prefetch has landed before the row sums take its area
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
     // tile sequence number `it` uses bf16 buffer it & 1 and staging it & 1;
     // the copy of tile it + 2 is issued at the top of step it, tile it + 1 is
