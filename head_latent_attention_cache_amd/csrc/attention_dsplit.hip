@@ -19,7 +19,8 @@
 // registers the score MFMAs take (no LDS bytes for it), one tile ahead.  The
 // content is copied into its LDS buffer one step ahead as well, by
 // global-to-LDS loads.  Three content buffers (96 KB), the partial scores
-// (32 KB) and the probabilities (4 KB) take 132 KB of LDS.  Step s of the
+// (32 KB), the probabilities (4 KB), the L2 prefetch's landing area (1 KB)
+// and the key-scale slots (512 B) take 133.5 KB of LDS.  Step s of the
 // key loop, with tiles t_s (attended now), t_s+1 (scored now) and t_s+2
 // (loaded now):
 //  * top: every load of the previous step has landed; barrier A (the partial
@@ -257,26 +258,14 @@ void attn_dsplit_kernel(MfmaArgs ma) {
           (LDS_AS i16x4_t*)(gbase + 8 * 128 + ((((d & 1) * 4 + cpart) ^ vsw1) << 4)));
     }
   };
-  // one of its MFMAs: output-dim block d, row block r
+  // O^T[wave's dims][both row blocks] += V^T . P^T, one MFMA: output-dim
+  // block d, row block r of one key step
   auto output_one = [&](const VFrag& f, const bf16x8_t* pfr, int d, int r) {
     const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[d]);
     bf16x8_t vf;
     vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
     vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
     o[d * 2 + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[r], o[d * 2 + r], 0, 0, 0);
-  };
-  // O^T[wave's dims][both row blocks] += V^T . P^T for key step j
-  auto output_mfma = [&](const VFrag& f, const bf16x8_t* pfr) {
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const bf16x4_t h0 = __builtin_bit_cast(bf16x4_t, f.v0[d]), h1 = __builtin_bit_cast(bf16x4_t, f.v1[d]);
-      bf16x8_t vf;
-      vf[0] = h0[0]; vf[1] = h0[1]; vf[2] = h0[2]; vf[3] = h0[3];
-      vf[4] = h1[0]; vf[5] = h1[1]; vf[6] = h1[2]; vf[7] = h1[3];
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        o[d * 2 + r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfr[r], o[d * 2 + r], 0, 0, 0);
-    }
   };
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   // the softmax lane's eight key positions in the tile (score elements 8 sj + i)
