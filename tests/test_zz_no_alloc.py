@@ -44,6 +44,8 @@ def test_noalloc_matches_workspace_call_twice_second_smaller(gpu_lib):
     _noalloc_matches(SMALL_CONFIGS[3], seed=33)
     _case("INT4 video chunk small: the packed cache dequantised into the scratch too")
     _noalloc_matches(SMALL_CONFIGS[5], seed=34)
+    _case("long video small (d_r 512, wide-row kernel, split partials in the scratch)")
+    _noalloc_matches(SMALL_CONFIGS[4], seed=35)
 
 
 def test_noalloc_rejects_a_call_beyond_the_scratch(gpu_lib):
