@@ -29,6 +29,26 @@ from __future__ import annotations
 import numpy as np
 
 
+def group_scale(amax, bits: int = 4):
+    """fp16 scale of a group whose largest magnitude is ``amax`` (float32):
+    fp16_round_to_nearest_even(amax / qmax)."""
+    qmax = (1 << (bits - 1)) - 1
+    return (np.asarray(amax, np.float32) / np.float32(qmax)).astype(np.float16)
+
+
+def codes_for(x, scale16, bits: int = 4):
+    """Codes of float32 values ``x`` under fp16 scales ``scale16`` (broadcast):
+    clamp(round_half_even(x / s)), and 0 where the scale is 0."""
+    qmax = (1 << (bits - 1)) - 1
+    qmin = -(1 << (bits - 1))
+    s = np.asarray(scale16).astype(np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(x / s)
+    q = np.where(s == 0, np.float32(0), q)
+    return np.clip(q, qmin, qmax).astype(np.int8)
+
+
 def quantize_groups(x, group: int, bits: int = 4):
     """Quantise the last axis in groups of ``group`` elements to ``bits``-bit
     symmetric codes.
@@ -37,20 +57,41 @@ def quantize_groups(x, group: int, bits: int = 4):
     (the bf16-rounded cache values).  Returns (codes int8 [..., n], scales
     float16 [..., n // group]).
     """
-    qmax = (1 << (bits - 1)) - 1
-    qmin = -(1 << (bits - 1))
     x = np.asarray(x, dtype=np.float32)
     n = x.shape[-1]
     assert n % group == 0
     g = x.reshape(x.shape[:-1] + (n // group, group))
-    amax = np.max(np.abs(g), axis=-1)
-    scale16 = (amax / np.float32(qmax)).astype(np.float16)
-    s = scale16.astype(np.float32)[..., None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.rint(g / s)
-    q = np.where(s == 0, np.float32(0), q)
-    q = np.clip(q, qmin, qmax).astype(np.int8)
+    scale16 = group_scale(np.max(np.abs(g), axis=-1), bits)
+    q = codes_for(g, scale16[..., None], bits)
     return q.reshape(x.shape), scale16
+
+
+def admissible_groups(lo, hi, group: int, bits: int = 4):
+    """Bounds on the codes and scales of ``quantize_groups`` when each input
+    element may be any value in [lo, hi] (float32-exact arrays, lo <= hi).
+
+    The scale is non-decreasing in the group maximum and the code of a fixed
+    value is monotone in the value and in the scale, so the extremes are
+    reached at the interval ends.  Returns (code_min, code_max int8 [..., n],
+    scale_min, scale_max float16 [..., n // group])."""
+    lo = np.asarray(lo, np.float32)
+    hi = np.asarray(hi, np.float32)
+    n = lo.shape[-1]
+    shp = lo.shape[:-1] + (n // group, group)
+    glo, ghi = lo.reshape(shp), hi.reshape(shp)
+    small = np.where((glo <= 0) & (ghi >= 0), np.float32(0), np.minimum(np.abs(glo), np.abs(ghi)))
+    big = np.maximum(np.abs(glo), np.abs(ghi))
+    s_min = group_scale(np.max(small, axis=-1), bits)
+    s_max = group_scale(np.max(big, axis=-1), bits)
+    cands = [codes_for(x, s[..., None], bits) for x in (glo, ghi) for s in (s_min, s_max)]
+    c_min = np.minimum.reduce(cands)
+    c_max = np.maximum.reduce(cands)
+    # a group that may be all zero may also take the smallest non-zero scales,
+    # under which any non-zero value clamps: no bound but the code range
+    wide = ((s_min == 0) & (s_max != 0))[..., None]
+    c_min = np.where(wide & (glo < 0), np.int8(-(1 << (bits - 1))), c_min)
+    c_max = np.where(wide & (ghi > 0), np.int8((1 << (bits - 1)) - 1), c_max)
+    return c_min.reshape(lo.shape), c_max.reshape(lo.shape), s_min, s_max
 
 
 def dequantize_groups(codes, scales, group: int):

@@ -51,6 +51,17 @@ def round_bf16(a) -> np.ndarray:
     return np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, a), r)
 
 
+def bf16_bracket(a):
+    """The two bfloat16 values next to each float64 value: (largest bf16 <= a,
+    smallest bf16 >= a), equal where ``a`` is a bf16 value.  A computation that
+    reaches ``a`` up to an error below half a bf16 step and then rounds to
+    nearest lands on one of them."""
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))
+    return np.floor(a / step) * step, np.ceil(a / step) * step
+
+
 def round_to_storage(a, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return round_bf16(a)
@@ -148,7 +159,9 @@ def content_bits(cfg) -> int:
 
 def new_cache(cfg) -> dict:
     B, cap = cfg.batch, cfg.capacity
-    st = {"values": np.zeros((B, cap, cfg.d_qk)), "newest": -1}
+    # "pre": each slot's row before storage rounding (float64), kept so that
+    # tests can bound the low-bit codes a correct computation may store
+    st = {"values": np.zeros((B, cap, cfg.d_qk)), "pre": np.zeros((B, cap, cfg.d_qk)), "newest": -1}
     if cfg.cache_fmt in ("int4", "int2"):
         st["codes"] = np.zeros((B, cap, cfg.d_c * content_bits(cfg) // 8 + cfg.d_r // 2), np.uint8)
         st["cscale"] = np.zeros((B, cap, cfg.d_c // INT4_GROUP), np.float16)
@@ -158,6 +171,7 @@ def new_cache(cfg) -> dict:
 
 def store_rows(st, cfg, slots, rows):
     """Round rows to the cache format and write them at ``slots``."""
+    st["pre"][:, slots] = rows
     stored = round_to_storage(rows, cfg.dtype)
     if cfg.cache_fmt in ("int4", "int2"):
         q = int4.quantize_cache_rows(stored, cfg.d_c, INT4_GROUP, content_bits(cfg))
@@ -221,6 +235,8 @@ def rope_shift(st, cfg, delta, slot_begin: int, n_slots: int):
         if not np.any(d):
             continue
         k = rope_rotate(st["values"][b, sl, cfg.d_c:], d, cfg)
+        if "pre" in st:
+            st["pre"][b, sl, cfg.d_c:] = k
         k = round_to_storage(k, cfg.dtype)
         if cfg.cache_fmt in ("int4", "int2"):
             codes, scale = int4.quantize_groups(k, cfg.d_r)

@@ -115,3 +115,62 @@ def compare(name, got, ref, dtype, report=None):
                                f"{TOL_BF16_REL}|ref| (max |d| {max_abs:.3g})")
         assert rel_l2 <= TOL_BF16_L2, f"{name}: relative L2 error {rel_l2:.3g} > {TOL_BF16_L2}"
     return max_abs, rel_l2
+
+
+def check_lowbit_codes(cfg, codes, cscale, rscale, st, slots):
+    """Every stored low-bit code and scale of ``slots`` (bool mask over ring
+    slots) is one a correct computation can store: the oracle's row before
+    storage rounding (``st["pre"]``), reached up to a float32 computation
+    error, rounded to bf16 and quantised.  The error allowed is 2^-16 of the
+    largest magnitude in the element's quantisation group (a code step is
+    1/7 of it for INT4, all of it for INT2), far above float32 rounding of the
+    projection and rotation and far below a code step, so every stored code
+    and scale is held to its rounding boundaries.
+
+    Returns the fraction of code bytes equal to the oracle's own."""
+    import oracle.int4 as oi
+    import oracle.mla as om
+    assert cfg.dtype == "bf16"
+    bits = om.content_bits(cfg)
+    d_c = cfg.d_c
+    ncb = d_c * bits // 8
+    pre = st["pre"][:, slots]
+    gmax_c = np.abs(pre[..., :d_c]).reshape(pre.shape[:-1] + (d_c // 32, 32)).max(axis=-1)
+    gmax_r = np.abs(pre[..., d_c:]).max(axis=-1, keepdims=True)
+    err = np.concatenate([np.repeat(gmax_c, 32, axis=-1), np.broadcast_to(gmax_r, pre[..., d_c:].shape)],
+                         axis=-1) * 2.0 ** -16
+    lo, _ = om.bf16_bracket(pre - err)
+    _, hi = om.bf16_bracket(pre + err)
+    got = np.asarray(codes)[:, slots]
+    unpack = oi.unpack_nibbles if bits == 4 else oi.unpack_crumbs
+    gc = unpack(got[..., :ncb])
+    gr = oi.unpack_nibbles(got[..., ncb:])
+    cmin, cmax, csmin, csmax = oi.admissible_groups(lo[..., :d_c], hi[..., :d_c], 32, bits)
+    rmin, rmax, rsmin, rsmax = oi.admissible_groups(lo[..., d_c:], hi[..., d_c:], cfg.d_r, 4)
+    gcs = np.asarray(cscale)[:, slots].astype(np.float64)
+    grs = np.asarray(rscale)[:, slots].astype(np.float64)[..., None]
+    for name, g, a, b in (("content codes", gc, cmin, cmax), ("rotary codes", gr, rmin, rmax),
+                          ("content scales", gcs, csmin.astype(np.float64), csmax.astype(np.float64)),
+                          ("rotary scales", grs, rsmin.astype(np.float64), rsmax.astype(np.float64))):
+        out = (g < a) | (g > b)
+        assert not out.any(), f"{name}: {int(out.sum())} of {out.size} outside the admissible bounds"
+    return float(np.mean(got == st["codes"][:, slots]))
+
+
+def upload_oracle_cache(cfg, st):
+    """Device (dims, geom, cache, aux) holding exactly the oracle's stored cache
+    ``st`` (dense values, or low-bit codes and fp16 scales)."""
+    import torch
+
+    from head_latent_attention_cache_amd import api
+    from mla_inputs import bf16_bits_from_f32
+    dims, geom = api.dims_from_config(cfg), api.geom_from_config(cfg)
+    cache, aux = api.new_cache(dims, geom)
+    if cfg.cache_fmt in ("int4", "int2"):
+        cache.copy_(torch.from_numpy(st["codes"]))
+        aux.copy_(torch.from_numpy(np.concatenate([st["cscale"].reshape(-1), st["rscale"].reshape(-1)])))
+    elif cfg.dtype == "bf16":
+        cache.copy_(to_device(bf16_bits_from_f32(st["values"].astype(np.float32))))
+    else:
+        cache.copy_(torch.from_numpy(st["values"].astype(np.float32)))
+    return {"dims": dims, "geom": geom, "cache": cache, "aux": aux}

@@ -711,6 +711,56 @@ def check_qk_norm():
     return float(max(errs))
 
 
+# ---------------------------------------------------------------------------
+# admissible low-bit codes: the bounds the GPU tests hold stored codes to
+# ---------------------------------------------------------------------------
+def check_admissible_codes():
+    bad = 0
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((300, 64)) * np.exp(rng.uniform(-6, 6, (300, 1)))
+    lo, hi = om.bf16_bracket(v)
+    # the bracket: bf16 values around v, one step apart, round_bf16 picks one
+    bad += int(np.any(om.round_bf16(lo) != lo) or np.any(om.round_bf16(hi) != hi))
+    bad += int(np.any(lo > v) or np.any(hi < v))
+    r = om.round_bf16(v)
+    bad += int(np.any((r != lo) & (r != hi)))
+    _, e = np.frexp(v)
+    bad += int(np.any((hi - lo != 0) & (hi - lo != np.ldexp(1.0, e - 8))))
+    ex = om.round_bf16(v)
+    elo, ehi = om.bf16_bracket(ex)
+    bad += int(np.any(elo != ex) or np.any(ehi != ex))
+    for bits, group in ((4, 32), (2, 32), (4, 64)):
+        # exact inputs: the bounds collapse to the quantiser's own result
+        q, s = oi.quantize_groups(ex, group, bits)
+        cmin, cmax, smin, smax = oi.admissible_groups(ex, ex, group, bits)
+        bad += int(np.any(cmin != q) or np.any(cmax != q))
+        bad += int(np.any(smin.view(np.uint16) != s.view(np.uint16)) or np.any(smax.view(np.uint16) != s.view(np.uint16)))
+        # brute force: every choice of bracket ends gives codes and scales
+        # inside the bounds, and the bounds are reached
+        cmin, cmax, smin, smax = oi.admissible_groups(lo, hi, group, bits)
+        seen_lo = np.zeros(cmin.shape, bool)
+        seen_hi = np.zeros(cmin.shape, bool)
+        for _ in range(64):
+            pick = rng.random(v.shape) < 0.5
+            x = np.where(pick, lo, hi)
+            qx, sx = oi.quantize_groups(x, group, bits)
+            bad += int(np.any(qx < cmin) or np.any(qx > cmax))
+            bad += int(np.any(sx.astype(np.float64) < smin.astype(np.float64))
+                       or np.any(sx.astype(np.float64) > smax.astype(np.float64)))
+            seen_lo |= qx == cmin
+            seen_hi |= qx == cmax
+        # intervals are at most one bf16 step wide: no code range wider than 2
+        bad += int(np.any(cmax.astype(int) - cmin.astype(int) > 2))
+        bad += int(np.mean(seen_lo & seen_hi) < 0.999)
+    # a code two away from the quantiser's is outside the bounds
+    q, _ = oi.quantize_groups(ex, 32)
+    cmin, cmax, _, _ = oi.admissible_groups(lo, hi, 32)
+    moved = np.clip(q.astype(int) + 2, -8, 7)
+    inside = (moved >= cmin) & (moved <= cmax) & (moved != q)
+    bad += int(np.any(inside & (np.abs(moved - q) == 2)))
+    return float(bad)
+
+
 CHECKS = {
     "bruteforce": (check_bruteforce, 1e-12),
     "absorption": (check_absorption, 1e-12),
@@ -723,6 +773,7 @@ CHECKS = {
     "bf16_rounding": (check_bf16_rounding, 0.0),
     "int4": (check_int4, 0.0),
     "int2": (check_int2, 0.0),
+    "admissible_codes": (check_admissible_codes, 0.0),
     "rope_shift": (check_rope_shift, 0.5),
     "query_fold": (check_query_fold, 1e-12),
     "qk_norm": (check_qk_norm, 1e-9),

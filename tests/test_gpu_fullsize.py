@@ -47,8 +47,9 @@ def test_fullsize_video_chunk(gpu_lib, key):
     got = gp.run_gpu(cfg, inp)
     st = om.build_cache(cfg, inp)
     if cfg.cache_fmt in ("int4", "int2"):
-        same = np.mean(got["codes"] == st["codes"])
-        assert same > 0.99, f"only {same:.4f} of low-bit code bytes agree"
+        written = om.slot_frames(cfg, st["newest"]) >= 0
+        same = gp.check_lowbit_codes(cfg, got["codes"], got["cscale"], got["rscale"], st, written)
+        print(f"low-bit code bytes equal to the oracle's: {same:.5f}", flush=True)
     else:
         gp.compare("cache", got["cache"], st["values"], cfg.dtype)
     toks = [(0, t) for t in (0, 51, 777, 1200, cfg.n_q - 1)]

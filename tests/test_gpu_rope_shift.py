@@ -1,6 +1,6 @@
 """Re-rotation of cached rotary keys (mla_cache_rope_shift) against the
-oracle's definition, applied to the path's own stored cache so that only the
-shift's arithmetic is compared; untouched columns and slots bit for bit; a zero
+oracle's definition, applied to the oracle's own stored cache (uploaded) so
+that only the shift's arithmetic is compared; untouched columns and slots bit for bit; a zero
 shift leaves every byte; attention is unchanged when the keys and the query
 move by the same time shift.  Every call goes through the C-ABI."""
 import numpy as np
@@ -16,20 +16,6 @@ pytestmark = pytest.mark.gpu
 
 def _case(msg):
     print(f"[case] {msg}", flush=True)
-
-
-def _state_from_gpu(cfg, got):
-    """Oracle cache state holding exactly the path's stored cache."""
-    st = {"newest": cfg.newest}
-    if cfg.cache_fmt in ("int4", "int2"):
-        st["codes"] = got["codes"].copy()
-        st["cscale"] = got["cscale"].copy()
-        st["rscale"] = got["rscale"].copy()
-        st["values"] = oi.dequantize_cache_rows(st["codes"], st["cscale"], st["rscale"], cfg.d_c, 32,
-                                                om.content_bits(cfg))
-    else:
-        st["values"] = got["cache"].copy()
-    return st
 
 
 def _snapshot(cfg, dev):
@@ -54,10 +40,9 @@ def test_shift_matches_oracle(gpu_lib, key, begin, count, delta):
     delta = np.array(delta, np.int64)[:cfg.batch]
     _case(f"rope shift {cfg.name} slots [{begin}, {begin + count}) delta {delta.tolist()}")
     inp = make_workload(cfg, seed=21)
-    got = gp.run_gpu(cfg, inp, fill=0xFF if cfg.cache_given else None, keep_device=True)
-    dev = got["_dev"]
+    st = om.build_cache(cfg, inp)
+    dev = gp.upload_oracle_cache(cfg, st)
     before, aux_before = _snapshot(cfg, dev)
-    st = _state_from_gpu(cfg, got)
     written = om.slot_frames(cfg, cfg.newest) >= 0
     api.cache_rope_shift(dev["dims"], dev["geom"], gp.int_tensor(delta.reshape(-1)), begin, count,
                          dev["cache"], dev["aux"])
@@ -78,18 +63,33 @@ def test_shift_matches_oracle(gpu_lib, key, begin, count, delta):
         nb = cfg.d_c * om.content_bits(cfg) // 8
         assert torch.equal(after[..., :nb], before[..., :nb]), "content codes changed"
         codes = after.cpu().numpy()
-        same = np.mean(codes[:, sel, nb:] == st["codes"][:, sel, nb:])
-        assert same > 0.99, f"only {same:.4f} of rotary code bytes agree"
+        ng = cfg.d_c // 32
+        aux = dev["aux"].cpu().numpy()
+        cscale = aux[:cfg.batch * cfg.capacity * ng].reshape(cfg.batch, cfg.capacity, ng)
+        rscale = aux[cfg.batch * cfg.capacity * ng:].reshape(cfg.batch, cfg.capacity)
+        same = gp.check_lowbit_codes(cfg, codes, cscale, rscale, st, sel)
+        print(f"rotary code bytes equal to the oracle's: {same:.5f}", flush=True)
         out = torch.empty((cfg.batch, cfg.capacity, cfg.d_qk), dtype=torch.float32, device="cuda")
         api.cache_dequant(dev["dims"], dev["geom"], dev["cache"], dev["aux"], out)
         torch.cuda.synchronize()
         vals = out.cpu().numpy().astype(np.float64)
-        ng = cfg.d_c // 32
         assert torch.equal(dev["aux"][:cfg.batch * cfg.capacity * ng], aux_before[:cfg.batch * cfg.capacity * ng])
     else:
         vals = gp.to_host(dev["cache"])
         elem = 2 if cfg.dtype == "bf16" else 4
         assert torch.equal(after[..., :cfg.d_c * elem], before[..., :cfg.d_c * elem]), "content changed"
+        if cfg.dtype == "bf16":
+            # every rotated key is one of the two bf16 values next to the
+            # oracle's unrounded rotation (float32 sin / cos of an fp64-reduced
+            # angle err by far less than half a bf16 step of the pair's norm)
+            pre = st["pre"][:, sel, cfg.d_c:]
+            pair = np.sqrt(pre[..., 0::2] ** 2 + pre[..., 1::2] ** 2)
+            err = np.repeat(pair, 2, axis=-1) * 2.0 ** -20
+            lo, _ = om.bf16_bracket(pre - err)
+            _, hi = om.bf16_bracket(pre + err)
+            v = vals[:, sel, cfg.d_c:]
+            outside = (v < lo) | (v > hi)
+            assert not outside.any(), f"{int(outside.sum())} rotated keys outside their bf16 bracket"
     gp.compare("rotary keys", vals[:, sel, cfg.d_c:], st["values"][:, sel, cfg.d_c:], cfg.dtype)
 
 

@@ -28,8 +28,8 @@ def _check_all(cfg, got, ref, report=None):
         out = torch.empty((cfg.batch, cfg.capacity, cfg.d_qk), dtype=torch.float32, device="cuda")
         api.cache_dequant(dev["dims"], dev["geom"], dev["cache"], dev["aux"], out)
         gp.compare("cache", gp.to_host(out)[:, written], st["values"][:, written], cfg.dtype, report)
-        same = np.mean(got["codes"][:, written] == st["codes"][:, written])
-        assert same > 0.99, f"only {same:.4f} of low-bit code bytes agree"
+        same = gp.check_lowbit_codes(cfg, got["codes"], got["cscale"], got["rscale"], st, written)
+        print(f"low-bit code bytes equal to the oracle's: {same:.5f}", flush=True)
     else:
         gp.compare("cache", got["cache"][:, written], st["values"][:, written], cfg.dtype, report)
     B, n_q, H = cfg.batch, cfg.n_q, cfg.n_heads
@@ -136,7 +136,8 @@ def test_lowbit_quantiser_bitexact(gpu_lib, key):
     slot0 = int(om.slot_index(cfg, 0, 0))
     assert np.array_equal(got["codes"][:, slot0, ncb:], st["codes"][:, slot0, ncb:])
     assert np.array_equal(got["rscale"][:, slot0].view(np.uint16), st["rscale"][:, slot0].view(np.uint16))
-    assert np.mean(got["codes"][..., ncb:] == st["codes"][..., ncb:]) > 0.99
+    written = om.slot_frames(cfg, st["newest"]) >= 0
+    gp.check_lowbit_codes(cfg, got["codes"], got["cscale"], got["rscale"], st, written)
 
 
 @pytest.mark.parametrize("key", [5, 6])
