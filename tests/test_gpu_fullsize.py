@@ -67,8 +67,8 @@ def test_fullsize_long_video(gpu_lib):
     rows: sampled cache rows, every absorbed query, and attention for sampled
     (token, head) pairs of all three query frames against the oracle's own
     cache (frames 45 and 46 see a frame-causal part of the window: the masked
-    key tiles of the benchmark's split plan), plus the un-absorb of sampled
-    tokens."""
+    key tiles of the benchmark's split plan), and two tokens end to end over
+    every head."""
     cfg = CONFIGS[4]
     _case(cfg.name)
     inp = make_workload(cfg, seed=0)
@@ -94,8 +94,15 @@ def test_fullsize_long_video(gpu_lib):
         _case(f"long video b={b} t={t} frame={frame} visible keys={n_vis}")
         gp.compare("o_lat", got["o_lat"][b, t, heads], o_lat[i, heads], cfg.dtype)
         gp.compare("lse", got["lse"][b, t, heads], lse[i, heads], cfg.dtype)
-    # un-absorb of sampled tokens from the path's own latent output
-    for b, t in toks:
-        o_heads, y = om.unabsorb(got["o_lat"][b, t], om.as_f64(inp["w_uv"]), om.as_f64(inp["w_o"]))
+    # two tokens (frames 45 and 47) end to end over every head: attention,
+    # then the un-absorb of the oracle's own latent output
+    full = [(0, 5), (1, cfg.n_q - 1)]
+    _, o_lat, lse = om.attend(cfg, st, om.as_f64(inp["q_nope"]), q_ref[..., cfg.d_c:], w_uk,
+                              om.as_f64(inp["w_uv"]), cfg.q_first, tokens=full)
+    for i, (b, t) in enumerate(full):
+        _case(f"long video end to end b={b} t={t}")
+        gp.compare("o_lat", got["o_lat"][b, t], o_lat[i], cfg.dtype)
+        gp.compare("lse", got["lse"][b, t], lse[i], cfg.dtype)
+        o_heads, y = om.unabsorb(o_lat[i], om.as_f64(inp["w_uv"]), om.as_f64(inp["w_o"]))
         gp.compare("o_heads", got["o_heads"][b, t], o_heads, cfg.dtype)
         gp.compare("y", got["y"][b, t], y, cfg.dtype)
