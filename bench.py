@@ -428,10 +428,13 @@ def main():
                                    "read_bytes": rows * 1024 * 2, "write_bytes": rows * 1024 * 2}
         del src_t, big
 
-    # ---- the MFMA-bound half of the metric: video-chunk attention ----
+    # ---- the MFMA-bound half of the metric: video-chunk attention, and the
+    # long-horizon video (d_r 512, the wide-row kernel) ----
     if args.config == 2 and not args.no_chunk_block:
         print("[bench] video-chunk attention block", file=sys.stderr, flush=True)
         out["video_chunk"] = chunk_block(stream, peaks)
+        print("[bench] long-video attention block", file=sys.stderr, flush=True)
+        out["long_video"] = chunk_block(stream, peaks, key=4, n_calls=8, warmup=2)
 
     # ---- CPU oracle on a bounded sample ----
     if not args.no_cpu_baseline:
@@ -456,21 +459,24 @@ def attention_flops(cfg):
     return 2.0 * cfg.batch * cfg.n_heads * keys * (cfg.d_qk + cfg.d_c)
 
 
-def chunk_block(stream, peaks, n_calls=120, warmup=10):
-    """Video-chunk attention (1560 query tokens x 32 heads over an 18,720-key
-    window): the cache built by appending 12 frames, the absorbed queries of
-    the last frame, then back-to-back mla_attention calls timed with HIP
-    events on the library's stream; FLOP-based roofline."""
+def chunk_block(stream, peaks, key=3, n_calls=120, warmup=10):
+    """Attention over a video window, inputs resident in HBM: the cache built
+    by appending every frame of the workload, the absorbed queries of its
+    query frames, then back-to-back mla_attention calls timed with HIP events
+    on the library's stream; FLOP-based roofline.  key 3: the video chunk
+    (1560 query tokens x 32 heads over an 18,720-key window); key 4: the
+    long-horizon video (batch 2, 4680 query tokens x 32 heads over 74,880
+    keys of 1024-wide rows)."""
     import numpy as np
     import torch
     from head_latent_attention_cache_amd import api
     from mla_inputs import get_config, make_workload
 
-    cfg = get_config(3)
+    cfg = get_config(key)
     dev = "cuda"
     dims, geom = api.dims_from_config(cfg), api.geom_from_config(cfg)
     B, H, P = cfg.batch, cfg.n_heads, cfg.tokens_per_frame
-    inp = make_workload(cfg, seed=0)
+    inp = make_workload(cfg, seed=0, parts=["x", "w_dkr", "w_uk", "q_nope", "q_rope"])
 
     def dev_t(a):
         a = np.ascontiguousarray(a)
@@ -488,6 +494,7 @@ def chunk_block(stream, peaks, n_calls=120, warmup=10):
     newest = torch.full((B,), cfg.newest, dtype=torch.int32, device=dev)
     q_abs = torch.empty((B, cfg.n_q, H, cfg.d_qk), dtype=torch.bfloat16, device=dev)
     api.absorb_q(dims, geom, dev_t(inp["q_nope"]), dev_t(inp["q_rope"]), q_first, w_uk, q_abs)
+    del inp
     o_lat = torch.empty((B, cfg.n_q, H, cfg.d_c), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, cfg.n_q, H), dtype=torch.float32, device=dev)
     ws = torch.empty(max(16, api.attention_workspace_bytes(dims, geom, cfg.n_q)), dtype=torch.uint8, device=dev)
@@ -506,7 +513,7 @@ def chunk_block(stream, peaks, n_calls=120, warmup=10):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n_calls
     single = []
-    for _ in range(20):
+    for _ in range(min(20, n_calls)):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         call()
