@@ -261,6 +261,9 @@ mla_status mla_absorb_q(const mla_dims* dims, const mla_geom* geom, void* stream
   ga.B = w_uk; ga.ldb = d.d_nope; ga.sB = (long long)d.d_c * d.d_nope;
   ga.C = q_abs; ga.ldc = (long long)d.H * d.d_qk; ga.sC = d.d_qk;
   ga.out_f32 = 0;
+  if (absorb_rope_fusable(d, ga))
+    return hip_status(launch_absorb_rope(d, g, ga, B, q_rope, n_q, q_first, q_abs, st), st,
+                      "absorbed query");
   hipError_t e = launch_gemm_nt(d.dtype, ga, st);
   if (e != hipSuccess) return hip_status(e, st, "absorb projection");
   e = launch_q_rope(d, g, B, q_rope, n_q, q_first, q_nope, q_abs, st);

@@ -45,6 +45,11 @@ hipError_t launch_fold_query(const Dims& d, int d_cq, const void* w_uq, const vo
                              hipStream_t st);
 hipError_t launch_append_store(const Dims& d, const Geo& g, int batch, const float* y, int n_tokens,
                                const int* frame, void* cache, void* aux, int nsplit, hipStream_t st);
+// q_abs in one launch (content product and rotary half side by side) where
+// absorb_rope_fusable(d, ga) holds; ga as for the content product
+bool absorb_rope_fusable(const Dims& d, const GemmArgs& ga);
+hipError_t launch_absorb_rope(const Dims& d, const Geo& g, const GemmArgs& ga, int batch, const void* q_rope, int n_q,
+                              const int* q_first, void* q_abs, hipStream_t st);
 hipError_t launch_q_rope(const Dims& d, const Geo& g, int batch, const void* q_rope, int n_q,
                          const int* q_first, const void* q_nope, void* q_abs, hipStream_t st);
 hipError_t launch_dequant(const Dims& d, const Geo& g, int batch, const void* cache, const void* aux,

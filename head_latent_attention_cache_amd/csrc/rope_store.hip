@@ -12,7 +12,7 @@
 // with the content latent in INT2 and the rotary key in INT4).  For b bits:
 // scale = fp16(amax / (2^(b-1) - 1)), code = round-half-even(x / scale)
 // clamped to [-2^(b-1), 2^(b-1) - 1] in IEEE fp32, the lowest bits first.
-#include "launch.hpp"
+#include "skinny_gemm.hpp"
 
 namespace mla {
 
@@ -144,14 +144,15 @@ __global__ void append_store_kernel(Dims d, Geo g, const float* __restrict__ y, 
 // mean over every head of the token (each work-group of the token computes
 // the same sum in the same order).
 // ---------------------------------------------------------------------------
+// work-group (t, b, hz): query token t of sequence b, heads 16 hz .. 16 hz + 15
 template <typename T>
-__global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n_q,
-                              const int* __restrict__ q_first, const T* __restrict__ q_nope, T* __restrict__ q_abs) {
+__device__ __forceinline__ void q_rope_body(const Dims& d, const Geo& g, const T* __restrict__ q_rope, int n_q,
+                                            const int* __restrict__ q_first, const T* __restrict__ q_nope,
+                                            T* __restrict__ q_abs, int t, int b, int hz) {
   extern __shared__ float smem[];
   float* cosv = smem;
   float* sinv = smem + d.d_r / 2;
   __shared__ float red[4];
-  const int t = blockIdx.x, b = blockIdx.y;
   const int f = q_first[b] + t / g.P, tok = t % g.P;
   double coord[3];
   token_coords(d.rope_dims, g.P, g.grid_w, f, tok, coord);
@@ -159,7 +160,7 @@ __global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n
   __syncthreads();
   const int npair = d.d_r / 2;
   const size_t tok_index = (size_t)b * n_q + t;
-  const int h0 = blockIdx.z * 16, h1 = min(d.H, h0 + 16);
+  const int h0 = hz * 16, h1 = min(d.H, h0 + 16);
   for (int e = threadIdx.x; e < (h1 - h0) * npair; e += blockDim.x) {
     const int h = h0 + e / npair, p = e % npair;
     const T* src = q_rope + (tok_index * d.H + h) * d.d_r;
@@ -217,6 +218,52 @@ __global__ void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n
       }
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void q_rope_kernel(Dims d, Geo g, const T* __restrict__ q_rope, int n_q,
+                                                     const int* __restrict__ q_first, const T* __restrict__ q_nope,
+                                                     T* __restrict__ q_abs) {
+  q_rope_body<T>(d, g, q_rope, n_q, q_first, q_nope, q_abs, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// ---------------------------------------------------------------------------
+// the decode-time absorbed query in one launch (bf16, no QK normalisation,
+// at most 32 query rows, d_nope <= 128): work-groups [0, n_gemm) form the
+// content half, the skinny product q_nope[:, h] . w_uk[h]^T (column block,
+// head), the others the rotary half (query token, sequence, group of 16
+// heads), the work of q_rope_kernel.  The halves are disjoint columns of
+// q_abs, so they run side by side instead of one launch after the other,
+// each with the same code and results as its own kernel.
+// ---------------------------------------------------------------------------
+constexpr int ABSORB_BN = 128, ABSORB_SEG = 128;
+__global__ __launch_bounds__(256) void absorb_rope_kernel(GemmArgs ga, int gemm_bx, Dims d, Geo g, int batch,
+                                                          const bf16_t* __restrict__ q_rope, int n_q,
+                                                          const int* __restrict__ q_first, bf16_t* __restrict__ q_abs) {
+  const int id = blockIdx.x, n_gemm = gemm_bx * ga.batch;
+  if (id < n_gemm) {
+    skinny_gemm_body<1, ABSORB_BN, ABSORB_SEG>(ga, id % gemm_bx, 0, id / gemm_bx);
+    return;
+  }
+  const int r = id - n_gemm;
+  q_rope_body<bf16_t>(d, g, q_rope, n_q, q_first, nullptr, q_abs, r % n_q, (r / n_q) % batch, r / (n_q * batch));
+}
+
+bool absorb_rope_fusable(const Dims& d, const GemmArgs& ga) {
+  return d.dtype == MLA_BF16 && !d.qk_norm && ga.M <= 32 && ga.K <= ABSORB_SEG && ga.ksplit == 1;
+}
+
+hipError_t launch_absorb_rope(const Dims& d, const Geo& g, const GemmArgs& ga, int batch, const void* q_rope, int n_q,
+                              const int* q_first, void* q_abs, hipStream_t st) {
+  if (!absorb_rope_fusable(d, ga)) return hipErrorInvalidValue;
+  const int gemm_bx = (ga.N + ABSORB_BN - 1) / ABSORB_BN;
+  const long long blocks = (long long)gemm_bx * ga.batch + (long long)n_q * batch * ((d.H + 15) / 16);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const size_t shm = (size_t)d.d_r * sizeof(float);   // the rotary work-groups' cosine and sine table
+  absorb_rope_kernel<<<(unsigned)blocks, 256, shm, st>>>(ga, gemm_bx, d, g, batch, (const bf16_t*)q_rope, n_q, q_first,
+                                                          (bf16_t*)q_abs);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
