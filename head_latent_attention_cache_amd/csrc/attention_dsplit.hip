@@ -45,6 +45,12 @@
 //    ds_read_b64_tr_b16 from t_s's content buffer during phase 1), with the
 //    other half of t_s+2's content copy between its MFMAs and the partial
 //    scores of t_s+1 written to LDS between its two key steps.
+// QK normalisation ("Multi-Head Latent Attention" topic page, QK-Norm
+// abstract; the key's inverse RMS scales the content part of its score):
+// the contraction is split by kind instead of by quarter, waves 0 and 1 on
+// the content dims, waves 2 and 3 on the rotary dims, so that the softmax
+// scales the content partials of each key and the chain keeps one
+// accumulator per row block.
 // What bounds it: the vector-memory side.  64 KB of cache rows per 64 rows
 // and 32 keys is 2.5 times the bytes per MFMA of the narrow kernel (128
 // rows per 1152-byte row); a step with every load removed runs in 60 % of
@@ -64,7 +70,7 @@ constexpr size_t attn_dsplit_lds_bytes() {
          + 2 * 4 * 64 * 64                       // partial scores [block][quarter][chunk][lane] (16 B)
          + 2 * 2 * 64 * 16                       // probabilities [block][key step][lane] (16 B)
          + 1024                                  // landing area of the L2 prefetch (never read)
-         + 2 * 256;                              // key scales of QK normalisation, two tiles
+         + 3 * 256;                              // key scales of QK normalisation, three tiles
 }
 
 template <int DC, int DR, bool QKN = false>
@@ -76,6 +82,13 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   constexpr int NKC = DC / 64;              // 16-dim content score steps of one wave (d_c / 4 dims)
   constexpr int NKR = DR / 64;              // rotary score steps of one wave (d_r / 4 dims)
   constexpr int NKS = NKC + NKR;
+  // QK normalisation with d_r = d_c: the score contraction split by kind
+  // instead of by quarter: waves 0 and 1 take content dims [256 w, 256 w +
+  // 256), waves 2 and 3 rotary dims [256 (w - 2), ...), so that a wave's
+  // partial score is all content or all rotary and the softmax applies each
+  // key's inverse RMS to the content partials alone (no second accumulator)
+  constexpr bool RS = QKN && DR == DC;
+  constexpr int NKR_W = RS ? NKS : NKR;     // rotary key fragments a wave holds
   constexpr int WDIMS = DC / 4;             // output dims owned by one wave
   constexpr int NDB = WDIMS / 32;           // its 32-dim output blocks
   static_assert(DC == 512 && DR % 64 == 0 && CT_BYTES % 4096 == 0, "widths");
@@ -153,7 +166,9 @@ void attn_dsplit_kernel(MfmaArgs ma) {
 
   // queries of both row blocks, this wave's content and rotary quarters:
   // steps 0 .. NKC - 1 content dims wave * d_c / 4 + 16 ks, then rotary dims
-  // d_c + wave * d_r / 4 + 16 (ks - NKC)
+  // d_c + wave * d_r / 4 + 16 (ks - NKC); split by kind, step ks of content
+  // wave w (0, 1) is dim 256 w + 16 ks, of rotary wave w (2, 3) dim
+  // d_c + 256 (w - 2) + 16 ks
   bf16x8_t qf[2][NKS];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -162,7 +177,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     const bf16_t* qrow = (const bf16_t*)a.q_abs + ((size_t)b * n_rows + (ok ? row : 0)) * DQK + g * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const int dim = ks < NKC ? wave * (DC / 4) + ks * 16 : DC + wave * (DR / 4) + (ks - NKC) * 16;
+      const int dim = RS ? (wave < 2 ? wave * (DC / 2) + ks * 16 : DC + (wave - 2) * (DR / 2) + ks * 16)
+                         : ks < NKC ? wave * (DC / 4) + ks * 16 : DC + wave * (DR / 4) + (ks - NKC) * 16;
       bf16x8_t v = *(const bf16x8_t*)(qrow + dim);
       if (!ok) {
 #pragma unroll
@@ -233,10 +249,10 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   // this wave's rotary key fragments of tile t (key lane & 31, 16 dims per
   // score step), straight from the cache into registers; past-the-end keys
   // read the last slot (their scores are masked)
-  bf16x8_t kr[NKR];
+  bf16x8_t kr[NKR_W];
   auto rope_src = [&](int t) -> const bf16_t* {
     const int key = min((t_begin + t) * MF_BN + (lane & 31), cap - 1);
-    return cache_b + (size_t)key * DQK + DC + wave * (DR / 4) + g * 8;
+    return cache_b + (size_t)key * DQK + DC + (RS ? (wave & 1) * (DR / 2) : wave * (DR / 4)) + g * 8;
   };
   // value fragments of the tile in `vbuf` for this wave's output dims; the
   // probabilities' key order is the score accumulators' (a fixed
@@ -272,14 +288,12 @@ void attn_dsplit_kernel(MfmaArgs ma) {
   auto skey = [&](int i) -> int { return 16 * sj + 8 * (i >> 2) + 4 * sg + (i & 3); };
 
   // QK normalisation: the content part of a score is scaled by its key's
-  // inverse RMS.  The chain then keeps content and rotary accumulators and
-  // combines them at its end, s = c * scale + r (the scales of the lane's
-  // sixteen keys 8k + 4g + i in the MFMA layout).  A tile's 32 scales reach
-  // LDS a step ahead, one 4-byte global-to-LDS load per lane of wave 1
-  // (lanes 32 .. 63 repeat lanes 0 .. 31), into one of two slots; the chain
-  // reads them from there just before the combination (a global load in the
-  // step would make the chain wait for it, and registers are short).
-  float ksc[QKN ? 16 : 1];
+  // inverse RMS.  The contraction is split by kind (RS): the content
+  // partials of waves 0 and 1 are scaled in the softmax, which reads the
+  // scales of its eight keys of the tile.  A tile's 32 scales reach LDS two
+  // steps before that softmax, one 4-byte global-to-LDS load per lane of
+  // wave 1 (lanes 32 .. 63 repeat lanes 0 .. 31), into one of three slots
+  // (the tiles being softmaxed, scored and loaded).
   auto ksc_copy = [&](int t, int slot) {
     if (QKN && wave == 1) {
       const int kt = (t_begin + t) * MF_BN;
@@ -287,43 +301,64 @@ void attn_dsplit_kernel(MfmaArgs ma) {
            (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(ksl + slot * 256));
     }
   };
-  auto ksc_read = [&](int slot) {
-    if constexpr (QKN) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4_t v = *(const LDS_AS f32x4_t*)(ksl + slot * 256 + (8 * k + 4 * g) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ksc[4 * k + i] = v[i];
-      }
-    }
-  };
-
-  // Partial scores of both row blocks over this wave's quarters for the tile
+  // Partial scores of both row blocks over this wave's dims for the tile
   // whose content sits in buffer kbuf and whose rotary fragments are in kr;
-  // kr is reloaded from `rnext` as it is consumed.  Rotary and content steps
-  // alternate (the register loads spread over the chain).
+  // kr is reloaded from `rnext` as it is consumed.  Quarters: rotary and
+  // content steps alternate (the register loads spread over the chain);
+  // split by kind: all of a wave's steps are of its kind (measured on the
+  // long video: the split by kind costs the plain kernel 9 %, and saves the
+  // QK-normalised one the second pair of accumulators, +11.5 % -> +5.3 %
+  // over the plain kernel).
   // stage(i) runs after score step i (copy pieces, softmax work).
   f32x16_t s0, s1;
   constexpr int NALT = NKR < NKC ? NKR : NKC;   // alternating pairs
-  auto score_chain = [&](int kbuf, int kslot, const bf16_t* rnext, auto&& stage) {
+  static_assert(!QKN || RS, "QK normalisation: the split by kind (d_r = d_c)");
+  auto score_chain = [&](int kbuf, const bf16_t* rnext, auto&& stage) {
     const int key = lane & 31;
     const int sw = key_swizzle(key) ^ g;
     const LDS_AS uint8_t* krow = (const LDS_AS uint8_t*)(smem + kbuf * CT_BYTES + key * 128);
     auto kaddr = [&](int ks) -> const LDS_AS bf16x8_t* {
-      const int gks = wave * NKC + ks;
+      const int gks = (RS ? (wave & 1) * NKS : wave * NKC) + ks;
       return (const LDS_AS bf16x8_t*)(krow + (gks >> 2) * MF_BN * 128 + ((((gks & 3) << 1) ^ sw) << 4));
     };
     constexpr int KPF = 4;
     bf16x8_t kb[KPF];
+    if constexpr (RS) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
+      if (wave >= 2) {
+        // rotary waves: every step from the registers, each reloaded with the
+        // next tile right after its MFMAs
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+          const bf16x8_t k = kr[i];
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][i], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][i], s1, 0, 0, 0);
+          kr[i] = *(const bf16x8_t*)(rnext + i * 16);
+          stage(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // content waves: every step from LDS, read KPF steps ahead
+#pragma unroll
+        for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+          const bf16x8_t k = kb[i % KPF];
+          if (i + KPF < NKS) kb[i % KPF] = *kaddr(i + KPF);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][i], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][i], s1, 0, 0, 0);
+          stage(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KPF; ++i) kb[i] = *kaddr(i);
-    f32x16_t c0, c1;   // content parts (QK normalisation)
 #pragma unroll
     for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
-    if constexpr (QKN) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NKS; ++i) {
@@ -338,24 +373,11 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         const int ks = i < 2 * NALT ? i / 2 : i - NALT;
         const bf16x8_t k = kb[ks % KPF];
         if (ks + KPF < NKC) kb[ks % KPF] = *kaddr(ks + KPF);
-        if constexpr (QKN) {
-          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], c1, 0, 0, 0);
-        } else {
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], s1, 0, 0, 0);
-        }
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], s1, 0, 0, 0);
       }
-      if (QKN && i == NKS - 2) ksc_read(kslot);
       stage(i);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (QKN) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s0[e] = fmaf(c0[e], ksc[e], s0[e]);
-        s1[e] = fmaf(c1[e], ksc[e], s1[e]);
-      }
     }
   };
   auto write_partials = [&]() {
@@ -381,14 +403,16 @@ void attn_dsplit_kernel(MfmaArgs ma) {
     // the second tile's copy issued between its MFMAs ----
     int tb = next_tile(ta + 1);
     int ba = 0, bb = 1, bn = 2;   // content buffers of t_s, t_s+1 and t_s+2
-    int kslot = 1;                // key-scale slot of t_s+1
+    int ksa = 0, ksb = 1;         // key-scale slots of t_s and t_s+1 (of three)
     {
       const uint8_t* cs = content_src(ta);
 #pragma unroll
       for (int q = 0; q < LOADS; ++q) copy_load(cs, q, ba);
       const bf16_t* rs = rope_src(ta);
+      if (!RS || wave >= 2) {
 #pragma unroll
-      for (int i = 0; i < NKR; ++i) kr[i] = *(const bf16x8_t*)(rs + i * 16);
+        for (int i = 0; i < NKR_W; ++i) kr[i] = *(const bf16x8_t*)(rs + i * 16);
+      }
       ksc_copy(ta, 0);
     }
     // vmcnt(0) lgkmcnt(0), as the builtin: the compiler counts it as done
@@ -402,7 +426,7 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       const bool have_b = tb < ntl;
       ksc_copy(have_b ? tb : ta, 1);
       const uint8_t* cs = content_src(have_b ? tb : ta);
-      score_chain(ba, 0, rope_src(have_b ? tb : ta), [&](int i) {
+      score_chain(ba, rope_src(have_b ? tb : ta), [&](int i) {
         if (copy_step(i)) copy_load(cs, copy_piece(i), bb);
       });
       write_partials();
@@ -421,7 +445,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       lds_barrier();
       const int tc = have_b ? next_tile(tb + 1) : ntl;
       const bool have_c = tc < ntl;
-      ksc_copy(have_c ? tc : ta, kslot ^ 1);
+      const int ksn = 3 - ksa - ksb;   // the third slot: t_s+2's
+      ksc_copy(have_c ? tc : ta, ksn);
       // L2 prefetch of the tile DS_PF_AHEAD steps ahead: wave 0 loads one
       // 16-byte piece of each of 64 of its 128-byte lines (a global-to-LDS
       // load into a landing area nothing reads), slice (work-group / 8) of
@@ -445,11 +470,12 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       // ---- phase 1: scores of t_s+1 (a discarded repeat of t_s's content
       // when there is none), the softmax of t_s between them ----
       f32x4_t pr[8];
+      f32x4_t kin[QKN ? 2 : 1];   // inverse RMS of the lane's eight keys of t_s
       float sv[8];
       float mloc = 0.f, neg_m = 0.f;
       bf16x8_t pf;
       VFrag vf0, vf1;
-      score_chain(have_b ? bb : ba, kslot, rope_src(have_c ? tc : ta), [&](int i) {
+      score_chain(have_b ? bb : ba, rope_src(have_c ? tc : ta), [&](int i) {
         if (loop_copy_step(i) && have_c) copy_load(cs, loop_copy_piece(i), bn);
         if (i == 0) {
 #pragma unroll
@@ -457,11 +483,26 @@ void attn_dsplit_kernel(MfmaArgs ma) {
             pr[2 * q] = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj);
             pr[2 * q + 1] = *(const LDS_AS f32x4_t*)sx_chunk(sb, q, sl, 2 * sj + 1);
           }
-        } else if (i == 2) {
+          if constexpr (QKN) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[e] = ((pr[0][e] + pr[2][e]) + pr[4][e]) + pr[6][e];
-            sv[4 + e] = ((pr[1][e] + pr[3][e]) + pr[5][e]) + pr[7][e];
+            for (int h = 0; h < 2; ++h)
+              kin[h] = *(const LDS_AS f32x4_t*)(LDS_AS float*)(ksl + ksa * 256 + (16 * sj + 8 * h + 4 * sg) * 4);
+          }
+        } else if (i == 2) {
+          if constexpr (QKN) {
+            // content quarters (waves 0, 1) scaled by the key's inverse RMS,
+            // then the rotary quarters (waves 2, 3), in a fixed order
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sv[e] = (fmaf(pr[0][e] + pr[2][e], kin[0][e], pr[4][e])) + pr[6][e];
+              sv[4 + e] = (fmaf(pr[1][e] + pr[3][e], kin[1][e], pr[5][e])) + pr[7][e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sv[e] = ((pr[0][e] + pr[2][e]) + pr[4][e]) + pr[6][e];
+              sv[4 + e] = ((pr[1][e] + pr[3][e]) + pr[5][e]) + pr[7][e];
+            }
           }
           if (cla != TILE_FULL) {
 #pragma unroll
@@ -524,9 +565,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
         // the compiler can count them: a branch around them turned the wait
         // for the second key step's probabilities into lgkmcnt(0), behind all
         // eight writes.  After the last tile they write a discarded repeat
-        // nobody reads.  With QK normalisation the register allocation of the
-        // unconditional form spills inside the loop, so there they follow the
-        // last MFMA, where no read waits behind them.)
+        // nobody reads.  With QK normalisation they follow the last MFMA,
+        // where no read waits behind them: measured 2 % faster there.)
         if (QKN ? m == 15 && have_b : m == 7) write_partials();
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -538,7 +578,8 @@ void attn_dsplit_kernel(MfmaArgs ma) {
       ba = bb;
       bb = bn;
       bn = bt;
-      kslot ^= 1;
+      ksa = ksb;
+      ksb = ksn;
     }
   }
   if (!block_any(overflow)) break;
