@@ -75,6 +75,11 @@ QKN_CASES["4x5"] = SMALL_CONFIGS[4].replace(name="long_video_small_4x5", grid_h=
 # the long video with 4 of 6 ring frames written, the other slots (and their
 # key statistics) NaN bit patterns: masked tiles of the wide-row kernel
 QKN_CASES["4_partial"] = SMALL_CONFIGS[4].replace(name="long_video_small_partial", n_frames=4, q_first=1)
+# a longer key loop for the wide-row kernel: 30 key tiles per row block (the
+# key-scale slots rotate through many steps), 48-token frames, a wrapped
+# 20-frame ring, frame-causal 3-frame chunk
+QKN_CASES["4_medium"] = SMALL_CONFIGS[4].replace(name="long_video_medium", grid_h=6, grid_w=8, window=20, n_frames=23,
+                                                 q_first=20)
 
 
 @pytest.mark.parametrize("key", list(QKN_CASES))
