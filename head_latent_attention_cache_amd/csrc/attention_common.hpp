@@ -296,7 +296,8 @@ float softmax_rerun_slack();
 // launch plan (key-split fields of MfmaArgs) for row blocks of `rows_per_wg`
 // and MF_BN-key tiles; returns the number of work-groups (the grid must be
 // exactly that: wg_piece derives each work-group's piece from it)
-int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma);
+// max_piece > 0: at most that many key tiles per piece (more splits)
+int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma, int max_piece = 0);
 // workspace bytes of a plan
 size_t attn_plan_workspace(const MfmaArgs& ma);
 // point the plan's partial buffers into the workspace

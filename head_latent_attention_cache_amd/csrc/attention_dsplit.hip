@@ -63,6 +63,12 @@ namespace mla {
 constexpr int DS_ROWS = 64;   // rows per work-group (2 blocks of 32)
 
 constexpr int DS_PF_AHEAD = 8;  // L2 prefetch distance (tiles)
+// at most this many key tiles per work-group piece: the long video (2340
+// tiles per row block) measured 69.3 ms with 6 or 8 splits against 72.1 ms
+// with the 2 the plan's cost model picks (4: 70.9, 10: 70.4, 16: 71.4; one
+// box); the model counts the partials' traffic but not what shorter pieces
+// gain, whose concurrently running work-groups attend a narrower key range
+constexpr int DS_MAX_PIECE_TILES = 400;
 
 template <int DC, int DR>
 constexpr size_t attn_dsplit_lds_bytes() {
@@ -675,7 +681,7 @@ size_t attn_dsplit_workspace(const Dims& d, const Geo& g, int batch, int n_rows)
   ma.a.d = d;
   ma.a.batch = batch;
   ma.a.n_rows = n_rows;
-  attn_plan(d, g, batch, n_rows, DS_ROWS, &ma);
+  attn_plan(d, g, batch, n_rows, DS_ROWS, &ma, DS_MAX_PIECE_TILES);
   return attn_plan_workspace(ma);
 }
 
@@ -692,7 +698,7 @@ static hipError_t launch_dsplit_shape(const MfmaArgs& ma, int blocks, hipStream_
 hipError_t launch_attn_dsplit(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   MfmaArgs ma;
   ma.a = a;
-  const int blocks = attn_plan(a.d, a.g, a.batch, a.n_rows, DS_ROWS, &ma);
+  const int blocks = attn_plan(a.d, a.g, a.batch, a.n_rows, DS_ROWS, &ma, DS_MAX_PIECE_TILES);
   if (ws_bytes < attn_plan_workspace(ma)) return hipErrorInvalidValue;
   attn_plan_bind(&ma, ws);
   hipError_t e = a.d.d_r != 512 ? launch_dsplit_shape<512, 64, false>(ma, blocks, st)

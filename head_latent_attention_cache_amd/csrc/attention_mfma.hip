@@ -889,10 +889,12 @@ static int forced_splits() {
 // the plan of a shape: the best uniform split count, then two-group plans
 // with 1 or 2 more splits for the last row blocks of every sequence; chosen
 // once per shape (the search runs a small dispatch simulation) and cached
-struct PlanKey { int B, n_rb, rows_wg, n_rows, tiles, d_c; };
+struct PlanKey { int B, n_rb, rows_wg, n_rows, tiles, d_c, max_piece; };
 struct PlanVal { int n_a, ns_a, ns_b; };
 static PlanVal search_plan(const PlanKey& k) {
-  const int min_ns = (k.tiles + MF_MAX_TPS - 1) / MF_MAX_TPS;   // a class table holds MF_MAX_TPS tiles
+  // a class table holds MF_MAX_TPS tiles; max_piece > 0 caps a piece's tiles
+  const int min_ns = std::max((k.tiles + MF_MAX_TPS - 1) / MF_MAX_TPS,
+                              k.max_piece > 0 ? (k.tiles + k.max_piece - 1) / k.max_piece : 1);
   auto cost = [&](int n_a, int ns_a, int ns_b) {
     return plan_cost(k.B, k.n_rb, k.rows_wg, k.n_rows, k.tiles, k.d_c, n_a, ns_a, ns_b);
   };
@@ -952,7 +954,7 @@ float softmax_rerun_slack() {
   return v;
 }
 
-int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma) {
+int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_wg, MfmaArgs* ma, int max_piece) {
   ma->rerun_log2 = softmax_rerun_slack();
   ma->n_rb = (n_rows + rows_per_wg - 1) / rows_per_wg;
   ma->rows_wg = rows_per_wg;
@@ -972,6 +974,7 @@ int attn_plan(const Dims& d, const Geo& g, int batch, int n_rows, int rows_per_w
     PlanKey k;
     memset(&k, 0, sizeof(k));
     k.B = batch; k.n_rb = ma->n_rb; k.rows_wg = rows_per_wg; k.n_rows = n_rows; k.tiles = ma->tiles; k.d_c = d.d_c;
+    k.max_piece = max_piece;
     v = cached_plan(k);
   }
   ma->n_a = v.n_a;
