@@ -752,6 +752,23 @@ def check_admissible_codes():
         # intervals are at most one bf16 step wide: no code range wider than 2
         bad += int(np.any(cmax.astype(int) - cmin.astype(int) > 2))
         bad += int(np.mean(seen_lo & seen_hi) < 0.999)
+    # groups whose intervals may all hold zero: the scale may be zero or any
+    # tiny value, under which a small element can take the largest code
+    # (brute force over interval ends and zero)
+    for bits in (4, 2):
+        h = np.ldexp(1.0, rng.integers(-30, -8, (200, 1))) * rng.uniform(0.05, 1.0, (200, 32))
+        zlo = -h * (rng.random((200, 32)) < 0.7)
+        zhi = h * (rng.random((200, 32)) < 0.7)
+        cmin, cmax, smin, smax = oi.admissible_groups(zlo, zhi, 32, bits)
+        bad += int(np.any(smin != 0))
+        for _ in range(64):
+            pick = rng.integers(0, 3, (200, 32))
+            x = np.where(pick == 0, zlo, np.where(pick == 1, zhi, 0.0))
+            # most elements zero, so that a small one can be the group maximum
+            x = np.where(rng.random((200, 32)) < 0.9, 0.0, x)
+            qx, sx = oi.quantize_groups(x, 32, bits)
+            bad += int(np.any(qx < cmin) or np.any(qx > cmax))
+            bad += int(np.any(sx.astype(np.float64) > smax.astype(np.float64)))
     # a code two away from the quantiser's is outside the bounds
     q, _ = oi.quantize_groups(ex, 32)
     cmin, cmax, _, _ = oi.admissible_groups(lo, hi, 32)

@@ -20,6 +20,7 @@ _orig = {
     "unpack_nibbles": oi.unpack_nibbles, "pack_crumbs": oi.pack_crumbs, "unpack_crumbs": oi.unpack_crumbs,
     "rope_shift": om.rope_shift, "fold_query_weights": om.fold_query_weights, "query_up": om.query_up,
     "rms_normalise": om.rms_normalise, "attend_qk_norm": om.attend_qk_norm,
+    "admissible_groups": oi.admissible_groups, "bf16_bracket": om.bf16_bracket,
 }
 
 
@@ -214,6 +215,32 @@ def _unpack_swapped(packed):
     return out.reshape(out.shape[:-1] + (-1, 2))[..., ::-1].reshape(out.shape)
 
 
+def _admissible_no_zero_groups(lo, hi, group, bits=4):
+    # forgets that a group which may be all zero may take a tiny scale
+    lo32, hi32 = np.asarray(lo, np.float32), np.asarray(hi, np.float32)
+    shp = lo32.shape[:-1] + (lo32.shape[-1] // group, group)
+    glo, ghi = lo32.reshape(shp), hi32.reshape(shp)
+    small = np.where((glo <= 0) & (ghi >= 0), np.float32(0), np.minimum(np.abs(glo), np.abs(ghi)))
+    big = np.maximum(np.abs(glo), np.abs(ghi))
+    s_min = oi.group_scale(np.max(small, axis=-1), bits)
+    s_max = oi.group_scale(np.max(big, axis=-1), bits)
+    cands = [oi.codes_for(x, s[..., None], bits) for x in (glo, ghi) for s in (s_min, s_max)]
+    return (np.minimum.reduce(cands).reshape(lo32.shape), np.maximum.reduce(cands).reshape(lo32.shape),
+            s_min, s_max)
+
+
+def _admissible_scale_fixed(lo, hi, group, bits=4):
+    # takes the scale of the lower interval ends as the only one
+    cmin, cmax, s_min, _ = _orig["admissible_groups"](lo, hi, group, bits)
+    q, s = oi.quantize_groups(lo, group, bits)
+    return np.minimum(cmin, q), np.maximum(cmin, q), s_min, s
+
+
+def _bracket_nearest_only(a):
+    r = om.round_bf16(a)
+    return r, r
+
+
 MUTANTS = {
     "rope_rotates_backwards": [(om, "rope_rotate", _rope_sign)],
     "rope_frequency_exponent": [(om, "rope_frequencies", _rope_freq)],
@@ -248,6 +275,9 @@ MUTANTS = {
     "qk_norm_per_head_rms": [(om, "rms_normalise", _rms_per_head)],
     "qk_norm_eps_outside_root": [(om, "rms_normalise", _rms_eps_outside)],
     "qk_norm_key_weight_dropped": [(om, "attend_qk_norm", _qkn_key_weight_dropped)],
+    "admissible_codes_no_zero_groups": [(oi, "admissible_groups", _admissible_no_zero_groups)],
+    "admissible_scale_of_low_ends": [(oi, "admissible_groups", _admissible_scale_fixed)],
+    "bf16_bracket_nearest_only": [(om, "bf16_bracket", _bracket_nearest_only)],
 }
 
 
