@@ -54,12 +54,33 @@ def parse():
     return ap.parse_args()
 
 
+def _code_lines(text):
+    """The lines of a C++ source with line comments and blank lines removed
+    (a "//" inside a string literal is kept), so that a comment edit leaves
+    the hash of the compiled code unchanged."""
+    for line in text.splitlines():
+        in_str, cut = False, len(line)
+        for i, ch in enumerate(line):
+            if ch == '"' and (i == 0 or line[i - 1] != "\\"):
+                in_str = not in_str
+            elif not in_str and line.startswith("//", i):
+                cut = i
+                break
+        code = line[:cut].rstrip()
+        if code:
+            yield code
+
+
 def source_hash():
+    """Hash of the attention kernels' code (comments excluded): ties the
+    stored HBM-traffic counters to the kernels they were taken from."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "head_latent_attention_cache_amd", "csrc")
     for n in sorted(os.listdir(d)):
         if n.startswith("attention") or n in ("common.hpp", "launch.hpp"):
-            h.update(open(os.path.join(d, n), "rb").read())
+            h.update(n.encode() + b"\n")
+            for line in _code_lines(open(os.path.join(d, n), encoding="utf-8").read()):
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

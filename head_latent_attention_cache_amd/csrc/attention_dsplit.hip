@@ -20,7 +20,7 @@
 // content is copied into its LDS buffer one step ahead as well, by
 // global-to-LDS loads.  Three content buffers (96 KB), the partial scores
 // (32 KB), the probabilities (4 KB), the L2 prefetch's landing area (1 KB)
-// and the key-scale slots (512 B) take 133.5 KB of LDS.  Step s of the
+// and the key-scale slots of three tiles (768 B) take 133.75 KB of LDS.  Step s of the
 // key loop, with tiles t_s (attended now), t_s+1 (scored now) and t_s+2
 // (loaded now):
 //  * top: every load of the previous step has landed; barrier A (the partial
