@@ -26,12 +26,14 @@ _orig = {
 
 def _rms_per_head(v, g, eps):
     v = np.asarray(v, np.float64)
-    return np.asarray(g, np.float64) * v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    with np.errstate(invalid="ignore", divide="ignore"):   # 0 / 0 where a pin passes eps = 0 with zero rows
+        return np.asarray(g, np.float64) * v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
 
 
 def _rms_eps_outside(v, g, eps):
     v = np.asarray(v, np.float64)
-    return np.asarray(g, np.float64) * v / (np.sqrt(np.mean(v * v, axis=(-2, -1), keepdims=True)) + eps)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return np.asarray(g, np.float64) * v / (np.sqrt(np.mean(v * v, axis=(-2, -1), keepdims=True)) + eps)
 
 
 def _qkn_key_weight_dropped(cfg, st, q_nope, q_rope_rot, w_uk, w_uv, g_q, g_k, eps, q_first, tokens=None):
